@@ -1,0 +1,58 @@
+"""Diagnostic model of the fp8 attention forward — TEST INFRASTRUCTURE ONLY.
+
+[FA3-wiki] innovation 3: Q and K are rotated by a random orthogonal matrix,
+then quantised to fp8; attention is computed on the quantised operands.
+The page fixes neither the scaling granularity nor which other operands are
+fp8. Readings used here: Q' = Q·R and K' = K·R (``oracle.hadamard.rotate``),
+V is not rotated; each of Q', K', V is quantised with one scale per (batch,
+head), scale = amax/448 (scale 1 when the head is all zeros), code =
+E4M3FN(x/scale) with round-to-nearest-even and saturation.
+
+The error of the fp8 path is always measured against the float64 attention
+on the *unrotated, unquantised* inputs (the rotation does not change the exact
+answer). This model only separates the error of quantising the operands from
+the error of the kernel, and gives the exact codes the quantisation step must
+produce.
+"""
+import numpy as np
+
+from .attention import attention_forward
+from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode
+from .hadamard import rotate as _rotate
+
+
+def quantize_per_head(x):
+    """Per-(b,h) amax scaling and E4M3FN encoding of x [B, H, N, d].
+
+    Returns (codes uint8 [B,H,N,d], scales float64 [B,H]); x ≈ decode(codes)·scale.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.max(np.abs(x), axis=(2, 3))
+    scales = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    codes = e4m3_encode(x / scales[:, :, None, None])
+    return codes, scales
+
+
+def dequantize(codes, scales):
+    """decode(codes) · scale per (b, h)."""
+    return e4m3_decode(codes) * np.asarray(scales)[:, :, None, None]
+
+
+def fp8_attention_model(q, k, v, causal, scale, rotate, seed):
+    """Rotate (optionally), quantise Q', K', V per head, dequantise, attend.
+
+    Returns a dict with the float64 output O and LSE of the model and the
+    intermediate codes / scales for comparison with the quantisation step.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    qr = _rotate(q, seed) if rotate else q
+    kr = _rotate(k, seed) if rotate else k
+    q8, sq = quantize_per_head(qr)
+    k8, sk = quantize_per_head(kr)
+    v8, sv = quantize_per_head(v)
+    o, lse = attention_forward(dequantize(q8, sq), dequantize(k8, sk),
+                               dequantize(v8, sv), causal, scale)
+    return {"o": o, "lse": lse, "q8": q8, "k8": k8, "v8": v8,
+            "sq": sq, "sk": sk, "sv": sv, "q_rot": qr, "k_rot": kr}

@@ -1,0 +1,109 @@
+"""Pins for the OCP E4M3FN model and the fp8 quantisation model (CPU only).
+
+torch's float8_e4m3fn dtype is an independent library implementation of the
+same OCP format: its decode of every code, and its round-to-nearest-even
+cast for in-range values, must agree with ``oracle.e4m3``.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle.attention import attention_forward
+from oracle.e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_values
+from oracle.fp8_model import dequantize, fp8_attention_model, quantize_per_head
+
+
+def test_decode_known_codes():
+    assert e4m3_decode(0x00) == 0.0
+    assert e4m3_decode(0x01) == 2.0 ** -9
+    assert e4m3_decode(0x07) == 7 * 2.0 ** -9
+    assert e4m3_decode(0x08) == 2.0 ** -6
+    assert e4m3_decode(0x38) == 1.0
+    assert e4m3_decode(0x7E) == 448.0
+    assert e4m3_decode(0xFE) == -448.0
+    assert np.isnan(e4m3_decode(0x7F)) and np.isnan(e4m3_decode(0xFF))
+    assert E4M3_MAX == 448.0
+
+
+def test_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e4m3_decode(codes)
+    theirs = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(theirs))
+    ok = ~np.isnan(ours)
+    np.testing.assert_array_equal(ours[ok], theirs[ok])
+
+
+def test_encode_roundtrip_all_finite_codes():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F])
+    back = e4m3_encode(e4m3_decode(codes))
+    expect = np.where(codes == 0x80, 0, codes)       # −0 encodes as +0
+    np.testing.assert_array_equal(back, expect)
+
+
+def test_encode_ties_to_even_and_saturation():
+    vals = e4m3_values()
+    mids = (vals[:-1] + vals[1:]) / 2
+    codes = e4m3_encode(mids)
+    lo = np.arange(len(mids))
+    expect = np.where(lo % 2 == 0, lo, lo + 1)
+    np.testing.assert_array_equal(codes, expect)
+    assert e4m3_encode(1e9) == 0x7E and e4m3_encode(-1e9) == 0xFE
+    assert e4m3_encode(460.0) == 0x7E
+    assert e4m3_encode(2.0 ** -11) == 0x00          # below half the smallest step
+    assert e4m3_encode(3 * 2.0 ** -11) == 0x01      # 0.75 step rounds up
+
+
+def test_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(20000) * 50,
+                        rng.standard_normal(20000) * 1e-2,
+                        rng.uniform(-448, 448, 20000)])
+    ours = e4m3_encode(x)
+    theirs = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    # torch keeps the sign of a zero result; our encoder returns +0.
+    theirs = np.where(theirs == 0x80, 0, theirs)
+    np.testing.assert_array_equal(ours, theirs)
+
+
+def test_quantize_per_head_amax_maps_to_max_code():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 3, 16, 8))
+    x[1, 2] = 0.0                                      # an all-zero head
+    codes, scales = quantize_per_head(x)
+    assert scales[1, 2] == 1.0 and np.all(codes[1, 2] == 0)
+    for b in range(2):
+        for h in range(3):
+            if b == 1 and h == 2:
+                continue
+            j = np.argmax(np.abs(x[b, h]))
+            assert codes[b, h].flat[j] in (0x7E, 0xFE)
+    # relative error of the round trip stays within half a step (2^-4 relative)
+    xr = dequantize(codes, scales)
+    big = np.abs(x) > scales[:, :, None, None] * 2.0 ** -6
+    rel = np.abs(xr - x)[big] / np.abs(x)[big]
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+
+
+def test_fp8_model_without_rotation_is_attention_on_dequantised():
+    rng = np.random.default_rng(2)
+    q, k, v = (rng.standard_normal((1, 2, 24, 16)) for _ in range(3))
+    m = fp8_attention_model(q, k, v, False, 0.25, rotate=False, seed=0)
+    o, _ = attention_forward(dequantize(m["q8"], m["sq"]), dequantize(m["k8"], m["sk"]),
+                             dequantize(m["v8"], m["sv"]), False, 0.25)
+    np.testing.assert_array_equal(m["o"], o)
+    np.testing.assert_array_equal(m["q_rot"], q)
+    exact, _ = attention_forward(q, k, v, False, 0.25)
+    rel = np.linalg.norm(m["o"] - exact) / np.linalg.norm(exact)
+    assert 1e-4 < rel < 6e-2
+
+
+def test_fp8_model_with_rotation_quantises_rotated_operands():
+    rng = np.random.default_rng(3)
+    q, k, v = (rng.standard_normal((1, 1, 8, 16)) for _ in range(3))
+    m = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=9)
+    from oracle.hadamard import rotate
+    np.testing.assert_allclose(m["q_rot"], rotate(q, 9), atol=0)
+    codes, scales = quantize_per_head(rotate(k, 9))
+    np.testing.assert_array_equal(m["k8"], codes)
+    np.testing.assert_array_equal(m["sk"], scales)

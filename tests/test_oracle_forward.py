@@ -1,0 +1,161 @@
+"""Pins for the float64 attention forward of the oracle (CPU only).
+
+Each test fixes a property that the plain definition S = scale·Q·Kᵀ,
+P = row-softmax(S), O = P·V must have, so that a dropped term, a wrong sign,
+a wrong causal direction, a missing scale or a transposed operand in
+``oracle.attention`` fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle.attention import (attention_forward, attention_forward_rows,
+                              softmax_rows)
+from oracle.brute import brute_forward
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _closed(expr):
+    return eval(expr, {"__builtins__": {}}, {"e": math.e, "log": math.log})
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def test_golden_two_tokens():
+    g = json.load(open(os.path.join(GOLDEN, "two_token_forward.json")))
+    q = np.array(g["q"])[None, None]
+    k = np.array(g["k"])[None, None]
+    v = np.array(g["v"])[None, None]
+    for key, causal in (("non_causal", False), ("causal", True)):
+        o, lse = attention_forward(q, k, v, causal, g["scale"])
+        exp_o = [_closed(x) for x in g[key]["o"]]
+        exp_l = [_closed(x) for x in g[key]["lse"]]
+        np.testing.assert_allclose(o[0, 0, :, 0], exp_o, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(lse[0, 0], exp_l, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", [(1, 1), (2, 3), (5, 4), (7, 8), (16, 3)])
+def test_matches_brute_force(n, d, causal):
+    q, k, v = (_rand((1, 1, n, d), s) for s in (1, 2, 3))
+    scale = 0.7
+    o, lse = attention_forward(q, k, v, causal, scale)
+    bo, bl = brute_forward(q[0, 0].tolist(), k[0, 0].tolist(),
+                           v[0, 0].tolist(), causal, scale)
+    np.testing.assert_allclose(o[0, 0], np.array(bo), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], np.array(bl), rtol=0, atol=1e-13)
+
+
+def test_softmax_rows_sum_to_one_and_masked_rows():
+    s = _rand((9, 13), 4, 5.0)
+    s[2, 5:] = -np.inf
+    s[7, :] = -np.inf                      # a row with nothing visible
+    p, lse = softmax_rows(s)
+    sums = p.sum(axis=1)
+    np.testing.assert_allclose(np.delete(sums, 7), 1.0, rtol=0, atol=1e-12)
+    assert np.all(p[2, 5:] == 0)
+    assert np.all(p[7] == 0) and lse[7] == -np.inf
+    # LSE definition on a plain row
+    np.testing.assert_allclose(lse[0], math.log(np.sum(np.exp(s[0]))), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_closed_form(causal):
+    n, d, scale = 12, 6, 0.4
+    q = _rand((1, 1, n, d), 5)
+    krow = _rand((d,), 6)
+    k = np.broadcast_to(krow, (1, 1, n, d)).copy()
+    v = _rand((1, 1, n, d), 7)
+    o, lse = attention_forward(q, k, v, causal, scale)
+    for i in range(n):
+        visible = i + 1 if causal else n
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, :visible].mean(axis=0),
+                                   rtol=0, atol=1e-13)
+        np.testing.assert_allclose(
+            lse[0, 0, i], scale * q[0, 0, i] @ krow + math.log(visible),
+            rtol=0, atol=1e-12)
+
+
+def test_causal_row_zero_and_n_equals_one():
+    q, k, v = (_rand((2, 3, 9, 5), s) for s in (8, 9, 10))
+    scale = 0.3
+    o, lse = attention_forward(q, k, v, True, scale)
+    np.testing.assert_array_equal(o[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0],
+                               scale * np.sum(q[:, :, 0] * k[:, :, 0], -1),
+                               rtol=0, atol=1e-14)
+    for causal in (False, True):
+        o1, l1 = attention_forward(q[:, :, :1], k[:, :, :1], v[:, :, :1],
+                                   causal, scale)
+        np.testing.assert_array_equal(o1, v[:, :, :1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    n, d, scale = 10, 4, 0.5
+    q, k, v = (_rand((1, 2, n, d), s) for s in (11, 12, 13))
+    u = _rand((d,), 14)
+    o, lse = attention_forward(q, k, v, causal, scale)
+    o2, lse2 = attention_forward(q, k + u, v, causal, scale)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse + scale * (q @ u), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_affine_in_v(causal):
+    n, d, scale = 11, 5, 0.9
+    q, k, v = (_rand((1, 1, n, d), s) for s in (15, 16, 17))
+    c = _rand((d,), 18)
+    w = _rand((d, 3), 19)
+    o, _ = attention_forward(q, k, v, causal, scale)
+    o_shift, _ = attention_forward(q, k, v + c, causal, scale)
+    np.testing.assert_allclose(o_shift, o + c, rtol=0, atol=1e-13)
+    o_lin, _ = attention_forward(q, k, v @ w, causal, scale)
+    np.testing.assert_allclose(o_lin, o @ w, rtol=0, atol=1e-12)
+
+
+def test_permutation_equivariance():
+    n, d, scale = 13, 4, 0.6
+    q, k, v = (_rand((1, 1, n, d), s) for s in (20, 21, 22))
+    o, lse = attention_forward(q, k, v, False, scale)
+    perm = np.random.default_rng(23).permutation(n)
+    o_kv, lse_kv = attention_forward(q, k[:, :, perm], v[:, :, perm], False, scale)
+    np.testing.assert_allclose(o_kv, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_kv, lse, rtol=0, atol=1e-13)
+    o_q, lse_q = attention_forward(q[:, :, perm], k, v, False, scale)
+    np.testing.assert_allclose(o_q, o[:, :, perm], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_q, lse[:, :, perm], rtol=0, atol=1e-13)
+
+
+def test_hard_attention_limit():
+    # With a huge scale the softmax becomes an argmax: O_i = V[argmax_j S_ij].
+    n, d = 8, 3
+    q, k, v = (_rand((1, 1, n, d), s) for s in (24, 25, 26))
+    o, _ = attention_forward(q, k, v, False, 1e4)
+    arg = np.argmax(q[0, 0] @ k[0, 0].T, axis=1)
+    np.testing.assert_allclose(o[0, 0], v[0, 0, arg], rtol=0, atol=1e-9)
+
+
+def test_scale_only_multiplies_scores():
+    # scale·(Q·Kᵀ) == (scale·Q)·Kᵀ: moving the scale into Q gives the same result.
+    q, k, v = (_rand((1, 1, 7, 4), s) for s in (27, 28, 29))
+    o, lse = attention_forward(q, k, v, True, 0.25)
+    o2, lse2 = attention_forward(q * 0.25, k, v, True, 1.0)
+    np.testing.assert_allclose(o, o2, atol=1e-14)
+    np.testing.assert_allclose(lse, lse2, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_variant_matches_full(causal):
+    q, k, v = (_rand((2, 2, 33, 8), s) for s in (30, 31, 32))
+    o, lse = attention_forward(q, k, v, causal, 0.35)
+    rows = np.array([0, 5, 17, 32])
+    o_r, lse_r = attention_forward_rows(q, k, v, causal, 0.35, 1, 0, rows)
+    np.testing.assert_allclose(o_r, o[1, 0, rows], atol=1e-14)
+    np.testing.assert_allclose(lse_r, lse[1, 0, rows], atol=1e-14)
