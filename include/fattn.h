@@ -1,0 +1,139 @@
+/*
+ * libfattn — fused exact attention for AMD Instinct MI355X (gfx950).
+ *
+ * Computes O = softmax(scale · Q·Kᵀ [causal mask]) · V tile by tile with an
+ * online softmax, keeps the N×N score matrix on chip, saves the per-row
+ * log-sum-exp, and forms dQ, dK, dV in the backward pass by recomputing P
+ * from that log-sum-exp. An fp8 forward rotates Q and K with a random-sign
+ * Hadamard matrix before e4m3 quantisation ("incoherent processing").
+ *
+ * Sources (web pages describing the method):
+ *  - "FlashAttention-4: cómo Together AI aceleró la atención en GPU
+ *    Blackwell" (news.hamidun.com) — section "Por qué el enfoque estándar ya
+ *    no funciona": the problem is the two products S = Q·Kᵀ and O = P·V with
+ *    a softmax between them.
+ *  - "FlashAttention-3 (ES)" (systems-analysis.ru) — "FlashAttention y
+ *    FlashAttention-2": tiling into on-chip memory and fusion, so no
+ *    intermediate reaches global memory; innovation 3: fp8 with incoherent
+ *    processing by a random orthogonal (Hadamard) matrix.
+ *  - "FlashAttention-4: Algorithm and Kernel Pipelining Co-Design for
+ *    Asymmetric Hardware Scaling" (gist.science) — technical summary 2.B
+ *    (software exp2 on FMA units, conditional rescaling past a threshold),
+ *    2.C (backward: dS, dQ and global atomic reductions).
+ *
+ * Conventions for every entry point
+ *  - Tensors are device pointers to contiguous [B, H, N, d] arrays (d fastest)
+ *    of bfloat16 (2-byte storage) unless stated otherwise; LSE and the
+ *    backward statistics are float32 [B, H, N]. Every pointer must be 16-byte
+ *    aligned. The caller owns all memory; the library never allocates device
+ *    memory and never synchronises.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; the return value is the enqueue status only. Device
+ *    faults surface at the caller's next synchronisation.
+ *  - Supported: B, H, N ≥ 1 with B·H·N·d < 2^31 elements per tensor,
+ *    d ∈ {64, 128}, any N (ragged tails are masked), causal ∈ {0, 1} with the
+ *    reading that key j is visible to query i iff j ≤ i, finite scale > 0.
+ *  - All argument checks run on the host before any HIP call, so a rejected
+ *    call has no effect on the device.
+ *  - Calls are re-entrant; concurrent calls that share output or workspace
+ *    buffers race.
+ */
+#ifndef FATTN_H
+#define FATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FATTN_OK = 0,
+  FATTN_EINVAL = 1,      /* null/misaligned pointer, B/H/N < 1, bad scale, bad flag */
+  FATTN_ENOTSUP = 2,     /* d not in {64, 128}; tensor too large for 32-bit indexing */
+  FATTN_EWORKSPACE = 3,  /* workspace pointer null or smaller than required */
+  FATTN_EHIP = 4,        /* a HIP runtime call failed; see fattn_last_error() */
+  FATTN_EDEVICE = 5      /* the current device is not gfx950 */
+} fattn_status;
+
+/* Which exp2 the softmax uses (forward kernels). */
+typedef enum {
+  FATTN_EXP_AUTO = 0,    /* the variant measured fastest on gfx950 (hardware) */
+  FATTN_EXP_HW = 1,      /* v_exp_f32 on the transcendental unit */
+  FATTN_EXP_POLY = 2     /* Cody–Waite split + degree-3 polynomial on FMA units */
+} fattn_exp_mode;
+
+/*
+ * Forward, bfloat16 in and out.
+ *   q, k, v  [B,H,N,d] bf16 inputs.
+ *   o        [B,H,N,d] bf16 output, O = softmax(scale·Q·Kᵀ [mask])·V,
+ *            rounded to nearest even.
+ *   lse      [B,H,N] fp32 output, natural-log log-sum-exp of the masked,
+ *            scaled scores of each row (required: the backward consumes it).
+ *   exp_mode one of fattn_exp_mode.
+ * The softmax keeps a running row max and sum and rescales the partial
+ * output only when the row max has grown by more than 2^8 in the exp2
+ * domain (FlashAttention-4 gist, technical summary 2.B), which is exact.
+ */
+fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o,
+                       float* lse, int B, int H, int N, int d, int causal,
+                       float scale, int exp_mode, void* stream);
+
+/*
+ * Backward, bfloat16 in and out, from the forward's saved O and LSE.
+ *   dout        [B,H,N,d] bf16 upstream gradient dO.
+ *   dq, dk, dv  [B,H,N,d] bf16 outputs.
+ *   workspace   device memory of at least fattn_bwd_workspace_bytes(B,H,N,d)
+ *               bytes, 256-byte aligned; contents on entry are ignored.
+ *               Layout: fp32 dQ accumulator [B,H,N,d] at offset 0, then fp32
+ *               D = rowsum(dO∘O) [B,H,N].
+ * dK and dV are accumulated without atomics (each key block is owned by one
+ * workgroup); dQ is reduced with fp32 global atomics, so dq is reproducible
+ * only up to the order of floating-point additions.
+ */
+size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d);
+fattn_status fattn_bwd(const void* q, const void* k, const void* v,
+                       const void* o, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                       int causal, float scale, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Forward with fp8 (OCP e4m3fn) operands and bf16 in/out
+ * (FlashAttention-3 page, innovation 3).
+ *   q, k, v     [B,H,N,d] bf16 inputs; o [B,H,N,d] bf16 output.
+ *   lse         optional [B,H,N] fp32 output (NULL to skip).
+ *   rotate      1: Q' = Q·R, K' = K·R with R = diag(s)·H_d/√d, H_d the
+ *               Sylvester Hadamard matrix, s_i = ±1 from the top bit of the
+ *               i-th SplitMix64 output for state `seed`; 0: no rotation.
+ *   workspace   at least fattn_fwd_fp8_workspace_bytes(B,H,N,d) bytes,
+ *               256-byte aligned. Layout (see fattn_fwd_fp8_workspace_layout):
+ *               e4m3 Q8 [B,H,N,d], e4m3 K8 [B,H,N,d], e4m3 V8 stored
+ *               transposed per head as [B,H,d,Npad] (Npad = N rounded up to
+ *               64, zero padded), then fp32 scales [3][B·H]
+ *               (Q', K', V per head: amax/448, or 1 for an all-zero head).
+ * Each operand is quantised per (b,h) with round-to-nearest-even and
+ * saturation; P is quantised to e4m3 after multiplication by 2^8.
+ */
+size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d);
+fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d,
+                                            size_t* off_q8, size_t* off_k8,
+                                            size_t* off_v8t, size_t* off_scales);
+fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
+                           float* lse, int B, int H, int N, int d, int causal,
+                           float scale, int rotate, uint64_t seed,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* fattn_strerror(int status);
+/* Detail of the last error on the calling thread (argument or HIP message). */
+const char* fattn_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int fattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FATTN_H */

@@ -1,0 +1,103 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/fattn.h, and rejects bad arguments on the host before any
+HIP call (fake, aligned, non-null device addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_attention_fattn_amd as fa
+from tiled_attention_fattn_amd._lib import PROTOTYPES
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "fattn.h")
+
+OK, EINVAL, ENOTSUP, EWORKSPACE = 0, 1, 2, 3
+P = ctypes.c_void_p(0x10000)           # aligned fake device address
+MIS = ctypes.c_void_p(0x10008)         # 8-byte aligned only
+NUL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.lib()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), f"{n} missing from libfattn.so"
+        assert n in PROTOTYPES, f"{n} has no ctypes prototype"
+    assert lib.fattn_version() >= 100
+
+
+def test_strerror_covers_codes():
+    lib = fa.lib()
+    for s in range(6):
+        assert lib.fattn_strerror(s)
+    assert b"unknown" in lib.fattn_strerror(99)
+
+
+def fwd(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=128, causal=0, scale=0.1, exp=0)
+    a.update(kw)
+    return fa.lib().fattn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                              a["d"], a["causal"], ctypes.c_float(a["scale"]), a["exp"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NUL), EINVAL), (dict(k=NUL), EINVAL), (dict(v=NUL), EINVAL), (dict(o=NUL), EINVAL),
+    (dict(lse=NUL), EINVAL), (dict(q=MIS), EINVAL), (dict(B=0), EINVAL), (dict(H=-1), EINVAL),
+    (dict(N=0), EINVAL), (dict(d=96), ENOTSUP), (dict(d=256), ENOTSUP), (dict(causal=2), EINVAL),
+    (dict(scale=0.0), EINVAL), (dict(scale=-1.0), EINVAL), (dict(scale=float("inf")), EINVAL),
+    (dict(scale=float("nan")), EINVAL), (dict(exp=3), EINVAL),
+    (dict(B=4096, H=64, N=8192, d=128), ENOTSUP),
+])
+def test_fwd_rejects_bad_arguments(kw, code):
+    assert fwd(**kw) == code
+    assert fa.lib().fattn_last_error()
+
+
+def test_bwd_workspace_checks():
+    lib = fa.lib()
+    need = lib.fattn_bwd_workspace_bytes(2, 3, 100, 64)
+    assert need >= 4 * 2 * 3 * 100 * 64 + 4 * 2 * 3 * 100
+    assert need % 256 == 0
+    assert lib.fattn_bwd_workspace_bytes(0, 1, 1, 64) == 0
+
+    def call(ws, nbytes, **kw):
+        a = dict(B=2, H=3, N=100, d=64, causal=1, scale=0.125)
+        a.update(kw)
+        return lib.fattn_bwd(P, P, P, P, P, P, P, P, P, a["B"], a["H"], a["N"], a["d"],
+                             a["causal"], ctypes.c_float(a["scale"]), ws, nbytes, NUL)
+    assert call(NUL, need) == EWORKSPACE
+    assert call(ctypes.c_void_p(0x10010), need) == EWORKSPACE      # not 256-aligned
+    assert call(P, need - 1) == EWORKSPACE
+    assert call(P, need, d=32) == ENOTSUP
+    assert call(P, need, N=0) == EINVAL
+
+
+def test_fp8_workspace_layout_and_checks():
+    lib = fa.lib()
+    B, H, N, d = 2, 3, 100, 128
+    need = lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
+    offs = [ctypes.c_size_t() for _ in range(4)]
+    assert lib.fattn_fwd_fp8_workspace_layout(B, H, N, d, *[ctypes.byref(x) for x in offs]) == OK
+    oq, ok, ov, osc = (x.value for x in offs)
+    npad = 128
+    assert oq == 0 and ok >= B * H * N * d and ov >= ok + B * H * N * d
+    assert osc >= ov + B * H * d * npad and need >= osc + 12 * B * H
+    assert all(x % 256 == 0 for x in (oq, ok, ov, osc))
+
+    def call(ws, nbytes, **kw):
+        a = dict(rotate=1, lse=P, d=d)
+        a.update(kw)
+        return lib.fattn_fwd_fp8(P, P, P, P, a["lse"], B, H, N, a["d"], 0, ctypes.c_float(0.1),
+                                 a["rotate"], ctypes.c_uint64(7), ws, nbytes, NUL)
+    assert call(P, need - 1) == EWORKSPACE
+    assert call(NUL, need) == EWORKSPACE
+    assert call(P, need, rotate=2) == EINVAL
+    assert call(P, need, lse=MIS) == EINVAL
+    assert call(P, need, d=80) == ENOTSUP

@@ -1,0 +1,152 @@
+"""Python binding of libfattn (fused exact attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfattn.so``; PyTorch supplies device memory and the current
+stream. There is no fallback: if the library is not built, or a call fails,
+an exception is raised.
+
+    o, lse = fwd(q, k, v, causal=False, scale=None, exp_mode="auto")
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
+    o, lse = fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0)
+
+Tensors are contiguous CUDA (HIP) bfloat16 [B, H, N, d], d ∈ {64, 128};
+``scale`` defaults to 1/√d.
+"""
+import ctypes
+import os
+
+from ._lib import FattnError, lib, lib_path  # noqa: F401
+
+__all__ = ["fwd", "bwd", "fwd_fp8", "fp8_workspace_views", "bwd_workspace_bytes",
+           "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
+           "EXP_AUTO", "EXP_HW", "EXP_POLY"]
+
+EXP_AUTO, EXP_HW, EXP_POLY = 0, 1, 2
+_EXP = {"auto": EXP_AUTO, "hw": EXP_HW, "poly": EXP_POLY,
+        EXP_AUTO: EXP_AUTO, EXP_HW: EXP_HW, EXP_POLY: EXP_POLY}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _call(status):
+    if status != 0:
+        raise FattnError(status)
+
+
+def fwd(q, k, v, causal=False, scale=None, exp_mode="auto", out=None, lse=None):
+    """Forward. Returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N])."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16)
+    B, H, N, d = _shape(q)
+    if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    scale = float(d ** -0.5 if scale is None else scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(o, "out", torch.bfloat16)
+    _check(lse_t, "lse", torch.float32)
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                              int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
+                              _stream(q)))
+    return o, lse_t
+
+
+def bwd_workspace_bytes(B, H, N, d):
+    return int(lib().fattn_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, out=None):
+    """Backward from the forward's O and LSE. Returns (dQ, dK, dV) bf16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, torch.bfloat16)
+    _check(lse, "lse", torch.float32)
+    B, H, N, d = _shape(q)
+    scale = float(d ** -0.5 if scale is None else scale)
+    if out is None:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    else:
+        dq, dk, dv = out
+    need = bwd_workspace_bytes(B, H, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                              _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
+                              ctypes.c_float(scale), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                              _stream(q)))
+    return dq, dk, dv
+
+
+def fp8_workspace_bytes(B, H, N, d):
+    return int(lib().fattn_fwd_fp8_workspace_bytes(B, H, N, d))
+
+
+def fp8_workspace_views(ws, B, H, N, d):
+    """Views (q8, k8, v8t, scales) into an fp8 workspace (uint8 tensor).
+
+    q8, k8: uint8 [B,H,N,d] e4m3 codes; v8t: uint8 [B,H,d,Npad] (V transposed,
+    zero padded to Npad = N rounded up to 64); scales: fp32 [3, B, H].
+    """
+    torch = _torch()
+    offs = [ctypes.c_size_t() for _ in range(4)]
+    _call(lib().fattn_fwd_fp8_workspace_layout(B, H, N, d, *[ctypes.byref(x) for x in offs]))
+    oq, ok, ov, osc = (x.value for x in offs)
+    npad = (N + 63) // 64 * 64
+    n = B * H * N * d
+    q8 = ws[oq:oq + n].view(B, H, N, d)
+    k8 = ws[ok:ok + n].view(B, H, N, d)
+    v8t = ws[ov:ov + B * H * d * npad].view(B, H, d, npad)
+    sc = ws[osc:osc + 12 * B * H].view(torch.float32).view(3, B, H)
+    return q8, k8, v8t, sc
+
+
+def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=True,
+            workspace=None, out=None):
+    """fp8 (e4m3) forward with optional Hadamard rotation. Returns (O, LSE or None)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16)
+    B, H, N, d = _shape(q)
+    scale = float(d ** -0.5 if scale is None else scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if want_lse else None
+    need = fp8_workspace_bytes(B, H, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
+                                  int(bool(causal)), ctypes.c_float(scale), int(bool(rotate)),
+                                  ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
+                                  ctypes.c_size_t(ws.numel()), _stream(q)))
+    return o, lse_t

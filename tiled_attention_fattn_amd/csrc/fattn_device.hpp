@@ -1,0 +1,124 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types,
+// MFMA wrappers with their lane layouts, the LDS swizzle, the LDS transpose
+// read, cross-half reductions and the two exp2 variants.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "exp2_poly_coeffs.h"
+
+namespace fattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+#define FATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32x16 bf16 (gfx950).  With h = lane/32 and c = lane%32:
+//   A (32×16): lane holds A[c][8h + e], e = 0..7
+//   B (16×32): lane holds B[8h + e][c]
+//   C (32×32): lane holds C[8(r/4) + 4h + r%4][c], r = 0..15
+// Any simultaneous relabelling of the k index in A and B leaves the product
+// unchanged; the kernels use that freedom to keep P in registers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp8 (e4m3fn for both operands) 32x32x64: A lane holds 32 k values of row c,
+// B lane holds 32 k values of column c; the k split between the lane halves
+// is the same for A and B, C as for mfma32.
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // format 0 = e4m3 for A (cbsz) and B (blgp); block scales 127 = 2^0.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Row index of accumulator register r in lane-half h (column = lane%32).
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// ---------------------------------------------------------------------------
+// LDS tile layout for [rows][D] bf16 tiles: 16-byte chunks are XOR-swizzled
+// per row so that the 32-row × 16-byte MFMA operand reads and the 8-row
+// transpose reads spread over all banks.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row, int chunk) {
+  if constexpr (D == 128) {
+    return chunk ^ ((row & 7) << 1);
+  } else {
+    return chunk ^ (((row >> 1) & 3) << 1);
+  }
+}
+// Byte offset of (row, 16-byte chunk) in a [rows][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * (D * 2) + swz_chunk<D>(row, chunk) * 16;
+}
+
+// ds_read_b64_tr_b16 on gfx950: within each 16-lane group g, output lane i
+// receives, for e = 0..3, element i%4 of the 8-byte row addressed by lane
+// 16g + 4e + i/4.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 FATTN_LDS*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Value of lane l combined with lane l^32 (both halves get the result).
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---------------------------------------------------------------------------
+// exp2 variants (FlashAttention-4 gist, technical summary 2.B: 2^x computed
+// either by the special-function unit or by a polynomial on FMA units).
+// ---------------------------------------------------------------------------
+enum { EXP_HW = 1, EXP_POLY = 2 };
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 2^x = 2^n · 2^f with n = floor(x), f = x − n ∈ [0, 1); 2^f by a degree-3
+// polynomial (own minimax fit, coefficients in exp2_poly_coeffs.h), 2^n
+// applied with ldexp. x is clamped at −200 so that −∞ gives exactly 0.
+__device__ __forceinline__ float exp2_poly(float x) {
+  x = fmaxf(x, -200.0f);
+  float n = __builtin_floorf(x);
+  float f = x - n;
+  float p = fmaf(fmaf(fmaf(kExp2PolyC3, f, kExp2PolyC2), f, kExp2PolyC1), f, kExp2PolyC0);
+  return __builtin_amdgcn_ldexpf(p, (int)n);
+}
+
+template <int MODE>
+__device__ __forceinline__ float exp2_sel(float x) {
+  if constexpr (MODE == EXP_POLY) return exp2_poly(x);
+  else return exp2_hw(x);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (bf16)a;
+  v[1] = (bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+}  // namespace fattn

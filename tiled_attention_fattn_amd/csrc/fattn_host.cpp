@@ -1,0 +1,212 @@
+// C-ABI entry points of libfattn: argument validation (host only, before any
+// HIP call), the gfx950 device check, workspace carving and kernel launch on
+// the caller's stream. Allocates nothing, never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/fattn.h"
+#include "fattn_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fattn_status fail(fattn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shape checks shared by every entry point.
+fattn_status check_shape(int B, int H, int N, int d, int causal, float scale) {
+  if (B < 1 || H < 1 || N < 1)
+    return fail(FATTN_EINVAL, "B, H and N must be >= 1 (got B=%d H=%d N=%d)", B, H, N);
+  if (d != 64 && d != 128) return fail(FATTN_ENOTSUP, "head dimension d=%d not supported (64 or 128)", d);
+  if (causal != 0 && causal != 1) return fail(FATTN_EINVAL, "causal must be 0 or 1 (got %d)", causal);
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(FATTN_EINVAL, "scale must be finite and > 0 (got %g)", (double)scale);
+  const unsigned long long elems = (unsigned long long)B * H * N * d;
+  if (elems >= (1ull << 31))
+    return fail(FATTN_ENOTSUP, "tensor of %llu elements exceeds 2^31-1", elems);
+  return FATTN_OK;
+}
+
+fattn_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(FATTN_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(FATTN_EINVAL, "%s is not 16-byte aligned", name);
+  return FATTN_OK;
+}
+
+// gfx950 check, cached per device id.
+std::mutex g_dev_mu;
+int g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
+
+fattn_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FATTN_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(FATTN_EDEVICE, "device id %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(FATTN_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_dev_ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    if (g_dev_ok[dev] == 2) return fail(FATTN_EDEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (g_dev_ok[dev] != 1) return fail(FATTN_EDEVICE, "device %d is not gfx950", dev);
+  return FATTN_OK;
+}
+
+fattn_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return FATTN_OK;
+}
+
+#define FATTN_TRY(x)                    \
+  do {                                  \
+    fattn_status s_ = (x);              \
+    if (s_ != FATTN_OK) return s_;      \
+  } while (0)
+
+struct Fp8Layout {
+  size_t q8, k8, v8t, scales, total;
+};
+
+Fp8Layout fp8_layout(int B, int H, int N, int d) {
+  const size_t bh = (size_t)B * H;
+  const size_t npad = round_up((size_t)N, fattn::kFp8Npad);
+  Fp8Layout L;
+  L.q8 = 0;
+  L.k8 = round_up(L.q8 + bh * N * d, 256);
+  L.v8t = round_up(L.k8 + bh * N * d, 256);
+  L.scales = round_up(L.v8t + bh * d * npad, 256);
+  L.total = round_up(L.scales + 3 * bh * sizeof(float), 256);
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int N, int d, int causal, float scale, int exp_mode, void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  FATTN_TRY(check_ptr(lse, "lse"));
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  if (exp_mode < FATTN_EXP_AUTO || exp_mode > FATTN_EXP_POLY)
+    return fail(FATTN_EINVAL, "exp_mode must be 0, 1 or 2 (got %d)", exp_mode);
+  FATTN_TRY(check_device());
+  const int mode = exp_mode == FATTN_EXP_POLY ? 2 : 1;
+  return hip_status(fattn::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, mode,
+                                           (hipStream_t)stream),
+                    "fattn_fwd launch");
+}
+
+size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  const size_t n = (size_t)B * H * N;
+  return round_up(n * d * sizeof(float), 256) + round_up(n * sizeof(float), 256);
+}
+
+fattn_status fattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                       int causal, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  FATTN_TRY(check_ptr(lse, "lse"));
+  FATTN_TRY(check_ptr(dout, "dout"));
+  FATTN_TRY(check_ptr(dq, "dq"));
+  FATTN_TRY(check_ptr(dk, "dk"));
+  FATTN_TRY(check_ptr(dv, "dv"));
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
+  if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
+  const size_t need = fattn_bwd_workspace_bytes(B, H, N, d);
+  if (workspace_bytes < need)
+    return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, need);
+  FATTN_TRY(check_device());
+  const size_t n = (size_t)B * H * N;
+  float* dq_acc = (float*)workspace;
+  float* dvec = (float*)((char*)workspace + round_up(n * d * sizeof(float), 256));
+  return hip_status(fattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, B, H,
+                                           N, d, causal != 0, scale, (hipStream_t)stream),
+                    "fattn_bwd launch");
+}
+
+size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  return fp8_layout(B, H, N, d).total;
+}
+
+fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d, size_t* off_q8,
+                                            size_t* off_k8, size_t* off_v8t, size_t* off_scales) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FATTN_EINVAL, "B, H, N and d must be >= 1");
+  const Fp8Layout L = fp8_layout(B, H, N, d);
+  if (off_q8) *off_q8 = L.q8;
+  if (off_k8) *off_k8 = L.k8;
+  if (off_v8t) *off_v8t = L.v8t;
+  if (off_scales) *off_scales = L.scales;
+  return FATTN_OK;
+}
+
+fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int N, int d, int causal, float scale, int rotate, uint64_t seed,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  if (lse != nullptr && !aligned16(lse)) return fail(FATTN_EINVAL, "lse is not 16-byte aligned");
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  if (rotate != 0 && rotate != 1) return fail(FATTN_EINVAL, "rotate must be 0 or 1 (got %d)", rotate);
+  if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
+  if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
+  const Fp8Layout L = fp8_layout(B, H, N, d);
+  if (workspace_bytes < L.total)
+    return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, L.total);
+  FATTN_TRY(check_device());
+  char* ws = (char*)workspace;
+  return hip_status(fattn::launch_fwd_fp8(q, k, v, o, lse, (uint8_t*)(ws + L.q8),
+                                          (uint8_t*)(ws + L.k8), (uint8_t*)(ws + L.v8t),
+                                          (float*)(ws + L.scales), B, H, N, d, causal != 0, scale,
+                                          rotate != 0, seed, (hipStream_t)stream),
+                    "fattn_fwd_fp8 launch");
+}
+
+const char* fattn_strerror(int status) {
+  switch (status) {
+    case FATTN_OK: return "success";
+    case FATTN_EINVAL: return "invalid argument";
+    case FATTN_ENOTSUP: return "unsupported shape or option";
+    case FATTN_EWORKSPACE: return "workspace missing or too small";
+    case FATTN_EHIP: return "HIP runtime error";
+    case FATTN_EDEVICE: return "device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+const char* fattn_last_error(void) { return g_last_error; }
+
+int fattn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Internal launcher interface between the C-ABI host code (fattn_host.cpp)
+// and the kernel translation units. Arguments are already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fattn {
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, bool causal, float scale, int exp_mode,
+                           hipStream_t stream);
+
+// Backward: `dq_acc` fp32 [B,H,N,d] and `dvec` fp32 [B,H,N] live in the caller's workspace.
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* dq_acc, float* dvec, int B, int H, int N, int d, bool causal,
+                           float scale, hipStream_t stream);
+
+// fp8 forward: q8/k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32 [3][B*H].
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                          uint8_t* q8, uint8_t* k8, uint8_t* v8t, float* scales, int B, int H,
+                          int N, int d, bool causal, float scale, bool rotate, uint64_t seed,
+                          hipStream_t stream);
+
+constexpr int kFp8Npad = 64;
+
+}  // namespace fattn
