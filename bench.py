@@ -1,0 +1,228 @@
+"""Throughput of the libfattn hot path on one MI355X.
+
+One step = one pass of the whole hot path over resident synthetic inputs:
+  * bf16 forward, non-causal, B=2 H=16 N=8192 d=128   (fattn_fwd)
+  * bf16 backward, causal,   B=4 H=16 N=4096 d=128   (fattn_bwd)
+  * fp8 forward with Hadamard rotation, non-causal, B=4 H=16 N=4096 d=128
+    (fattn_fwd_fp8)
+value = algorithmic FLOP of the step / time of the step, in TFLOP/s
+(forward 4·B·H·N²·d, backward 2.5× that, halved under causal).
+
+Prints ONE JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PEAK_BF16 = 2500.0      # TFLOP/s, MI355X dense bf16 MFMA
+PEAK_FP8 = 5000.0       # TFLOP/s, MI355X dense fp8 MFMA
+
+PARTS = ["fwd", "bwd", "fp8"]
+PART_WORKLOAD = {"fwd": 3, "bwd": 4, "fp8": 5}
+KERNEL_SOURCES = {
+    "fwd": ["fwd_bf16.hip", "fattn_device.hpp"],
+    "bwd": ["bwd_bf16.hip", "fattn_device.hpp"],
+    "fp8": ["fwd_fp8.hip", "fattn_device.hpp"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--parts", default=",".join(PARTS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1)
+    return ap.parse_args()
+
+
+def source_hash(part):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[part]:
+        with open(os.path.join(HERE, "tiled_attention_fattn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(part):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the
+    kernel source has not changed since the counters were taken."""
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(part)
+    if not rec or rec.get("source_hash") != source_hash(part):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def part_flops(part):
+    from tiled_attention_fattn_amd.inputs import WORKLOADS, flops_bwd, flops_fwd
+    w = WORKLOADS[PART_WORKLOAD[part]]
+    args = (w["B"], w["H"], w["N"], w["d"], w["causal"])
+    return flops_bwd(*args) if part == "bwd" else flops_fwd(*args)
+
+
+def setup_part(part, torch, fa):
+    """Resident inputs/outputs for one part; returns a zero-arg launch closure."""
+    from tiled_attention_fattn_amd.inputs import WORKLOADS, gen_workload, to_device_bf16
+    k = PART_WORKLOAD[part]
+    w = WORKLOADS[k]
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    names = ("q", "k", "v", "do") if part == "bwd" else ("q", "k", "v")
+    inp = gen_workload(k, names=names)
+    t = {n: to_device_bf16(inp[n][1]) for n in names}
+    del inp
+    scale = d ** -0.5
+    if part == "fwd":
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        return lambda mode="auto": fa.fwd(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
+                                          exp_mode=mode, out=o, lse=lse)
+    if part == "bwd":
+        o, lse = fa.fwd(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale)
+        grads = tuple(torch.empty_like(t["q"]) for _ in range(3))
+        ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+        return lambda: fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w["causal"],
+                              scale=scale, workspace=ws, out=grads)
+    o = torch.empty_like(t["q"])
+    ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    return lambda: fa.fwd_fp8(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
+                              rotate=w["rotate"], seed=k, want_lse=False, workspace=ws, out=o)
+
+
+def cpu_baseline(parts, heads):
+    """The float64 oracle on a bounded sample (`heads` heads of each part's workload)."""
+    from oracle.attention import attention_backward, attention_forward
+    from oracle.fp8_model import fp8_attention_model
+    from tiled_attention_fattn_amd.inputs import WORKLOADS, flops_bwd, flops_fwd, gen_workload
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    flop = 0.0
+    secs = 0.0
+    for part in parts:
+        k = PART_WORKLOAD[part]
+        w = WORKLOADS[k]
+        shape = (1, heads, w["N"], w["d"])
+        names = ("q", "k", "v", "do") if part == "bwd" else ("q", "k", "v")
+        x = gen_workload(k, names=names, shape=shape)
+        scale = w["d"] ** -0.5
+        t0 = time.perf_counter()
+        if part == "fwd":
+            attention_forward(x["q"][0], x["k"][0], x["v"][0], w["causal"], scale)
+        elif part == "bwd":
+            attention_backward(x["q"][0], x["k"][0], x["v"][0], x["do"][0], w["causal"], scale)
+        else:
+            fp8_attention_model(x["q"][0], x["k"][0], x["v"][0], w["causal"], scale,
+                                rotate=True, seed=k)
+        secs += time.perf_counter() - t0
+        f = (flops_bwd if part == "bwd" else flops_fwd)(1, heads, w["N"], w["d"], w["causal"])
+        flop += f
+    return {"value": flop / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} head(s) of each part's workload ({', '.join(parts)}), "
+                      f"float64 numpy, {secs:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention path has no multi-GPU mode).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tiled_attention_fattn_amd as fa
+
+    parts = [p for p in args.parts.split(",") if p]
+    torch.cuda.set_device(0)
+    launch = {p: setup_part(p, torch, fa) for p in parts}
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for p in parts:
+            launch[p]()
+    torch.cuda.synchronize()
+
+    ev = {p: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for p in parts}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        for p in parts:
+            ev[p][i][0].record()
+            launch[p]()
+            ev[p][i][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    part_ms = {p: float(np.mean([a.elapsed_time(b) for a, b in ev[p]])) for p in parts}
+    flops = {p: part_flops(p) for p in parts}
+    step_flop = sum(flops.values())
+    value = step_flop / (ms_per_step * 1e-3) / 1e12
+
+    info = {}
+    for p in parts:
+        tf = flops[p] / (part_ms[p] * 1e-3) / 1e12
+        peak = PEAK_FP8 if p == "fp8" else PEAK_BF16
+        info[p] = {"workload": fa_workload_name(p), "ms": round(part_ms[p], 4),
+                   "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
+
+    # The C3 forward is also reported with each exp2 variant.
+    if "fwd" in parts:
+        variants = {}
+        for mode in ("hw", "poly"):
+            for _ in range(3):
+                launch["fwd"](mode)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(10):
+                launch["fwd"](mode)
+            b.record()
+            torch.cuda.synchronize()
+            variants[mode] = round(flops["fwd"] / (a.elapsed_time(b) / 10 * 1e-3) / 1e12, 1)
+        info["fwd"]["tflops_by_exp2"] = variants
+
+    dom = max(parts, key=lambda p: part_ms[p])
+    dom_peak = PEAK_FP8 if dom == "fp8" else PEAK_BF16
+    achieved = flops[dom] / (part_ms[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": dom_peak, "unit": "TFLOP/s", "frac": round(achieved / dom_peak, 4),
+                "traffic": committed_traffic(dom)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(parts, args.cpu_heads)
+
+    dtype = "bf16" if "fp8" not in parts else ("fp8" if parts == ["fp8"] else "bf16+fp8")
+    line = {
+        "metric": "attention TFLOP/s (bf16 fwd, bwd; fp8 fwd) and % of MI355X MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic: seeded N(0,1) rounded to bf16 (fp8 part: 0.1% x20 outliers in Q, K)",
+        "config": {"workload": "+".join(fa_workload_name(p) for p in parts),
+                   "step_tflop": round(step_flop / 1e12, 4), "parallelism": "single GPU"},
+        "parts": info, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def fa_workload_name(p):
+    from tiled_attention_fattn_amd.inputs import WORKLOADS
+    return WORKLOADS[PART_WORKLOAD[p]]["name"]
+
+
+if __name__ == "__main__":
+    main()
