@@ -89,8 +89,10 @@ def test_fp8_model_without_rotation_is_attention_on_dequantised():
     rng = np.random.default_rng(2)
     q, k, v = (rng.standard_normal((1, 2, 24, 16)) for _ in range(3))
     m = fp8_attention_model(q, k, v, False, 0.25, rotate=False, seed=0)
-    o, _ = attention_forward(dequantize(m["q8"], m["sq"]), dequantize(m["k8"], m["sk"]),
-                             dequantize(m["v8"], m["sv"]), False, 0.25)
+    from oracle.fp8_model import dequantize_split
+    o, _ = attention_forward(dequantize_split(m["q8"], m["q8lo"], m["sq"]),
+                             dequantize(m["k8"], m["sk"]), dequantize(m["v8"], m["sv"]),
+                             False, 0.25)
     np.testing.assert_array_equal(m["o"], o)
     np.testing.assert_array_equal(m["q_rot"], q)
     exact, _ = attention_forward(q, k, v, False, 0.25)
@@ -107,3 +109,36 @@ def test_fp8_model_with_rotation_quantises_rotated_operands():
     codes, scales = quantize_per_head(rotate(k, 9))
     np.testing.assert_array_equal(m["k8"], codes)
     np.testing.assert_array_equal(m["sk"], scales)
+
+
+def test_quantisation_uses_the_exact_ratio_at_ties():
+    # bf16 inputs make exact e4m3 midpoints common: with amax = 3.0625,
+    # x = 1.4765625 gives x·448/amax = 216 exactly, the midpoint of 208 (odd
+    # code 0x75) and 224 (even code 0x76): round-to-nearest-even picks 0x76.
+    x = np.zeros((1, 1, 2, 1))
+    x[0, 0, 0, 0] = 3.0625
+    x[0, 0, 1, 0] = 1.4765625
+    codes, scales = quantize_per_head(x)
+    assert codes[0, 0, 0, 0] == 0x7E and codes[0, 0, 1, 0] == 0x76
+    assert scales[0, 0] == 3.0625 / 448
+
+
+def test_split_quantisation_residual():
+    from oracle.fp8_model import dequantize_split, quantize_per_head_split
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((2, 2, 64, 32))
+    x[0, 1, 3, 5] = 40.0
+    hi, lo, scales = quantize_per_head_split(x)
+    hi1, sc1 = quantize_per_head(x)
+    np.testing.assert_array_equal(hi, hi1)
+    np.testing.assert_array_equal(scales, sc1)
+    # the residual never saturates: |16·r| ≤ 16·(half the largest step, 16) = 256
+    assert np.max(np.abs(e4m3_decode(lo))) <= 256
+    xr = dequantize_split(hi, lo, scales)
+    t = x / scales[:, :, None, None]
+    big = np.abs(t) >= 1.0
+    rel = np.abs(xr - x)[big] / np.abs(x)[big]
+    assert rel.max() <= 2.0 ** -7
+    # the two-term value is closer than the one-term value
+    one = dequantize(hi, scales)
+    assert np.linalg.norm(xr - x) < np.linalg.norm(one - x) / 8
