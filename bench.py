@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--parts", default=",".join(PARTS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1)
+    ap.add_argument("--cpu-heads", type=int, default=8)
     return ap.parse_args()
 
 

@@ -109,17 +109,27 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v,
  *               i-th SplitMix64 output for state `seed`; 0: no rotation.
  *   workspace   at least fattn_fwd_fp8_workspace_bytes(B,H,N,d) bytes,
  *               256-byte aligned. Layout (see fattn_fwd_fp8_workspace_layout):
- *               e4m3 Q8 [B,H,N,d], e4m3 K8 [B,H,N,d], e4m3 V8 stored
+ *               e4m3 Q8 [B,H,N,d], e4m3 Q8lo [B,H,N,d] (residual of Q',
+ *               see below), e4m3 K8 [B,H,N,d], e4m3 V8 stored
  *               transposed per head as [B,H,d,Npad] (Npad = N rounded up to
- *               64, zero padded), then fp32 scales [3][B·H]
- *               (Q', K', V per head: amax/448, or 1 for an all-zero head).
- * Each operand is quantised per (b,h) with round-to-nearest-even and
- * saturation; P is quantised to e4m3 after multiplication by 2^8.
+ *               64, zero padded; inside each block of 64 keys, position
+ *               p = 32a + s holds key 32(s/16) + 8((s%16)/4) + 4a + s%4,
+ *               the order in which the kernel's P operand holds keys),
+ *               then fp32 scales [3][B·H]
+ *               (Q', K', V per head: amax/448, or 1 for an all-zero head),
+ *               then a uint32 [3][B·H] scratch for the running amax.
+ * Each operand is quantised per (b,h): code = e4m3(x·448/amax), the exact
+ * ratio rounded to nearest even. Q' keeps a second e4m3 term for its
+ * quantisation residual, Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that
+ * Q' ≈ scale_q·(Q8 + Q8lo/16); the scores use both terms (two fp8 MFMAs).
+ * P is quantised to e4m3 after multiplication by 2^8.
+ * Additionally requires B·H ≤ 65535 (ENOTSUP otherwise).
  */
 size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d);
 fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d,
-                                            size_t* off_q8, size_t* off_k8,
-                                            size_t* off_v8t, size_t* off_scales);
+                                            size_t* off_q8, size_t* off_q8lo,
+                                            size_t* off_k8, size_t* off_v8t,
+                                            size_t* off_scales);
 fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                            float* lse, int B, int H, int N, int d, int causal,
                            float scale, int rotate, uint64_t seed,

@@ -83,13 +83,14 @@ def test_fp8_workspace_layout_and_checks():
     lib = fa.lib()
     B, H, N, d = 2, 3, 100, 128
     need = lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
-    offs = [ctypes.c_size_t() for _ in range(4)]
+    offs = [ctypes.c_size_t() for _ in range(5)]
     assert lib.fattn_fwd_fp8_workspace_layout(B, H, N, d, *[ctypes.byref(x) for x in offs]) == OK
-    oq, ok, ov, osc = (x.value for x in offs)
+    oq, oql, ok, ov, osc = (x.value for x in offs)
     npad = 128
-    assert oq == 0 and ok >= B * H * N * d and ov >= ok + B * H * N * d
-    assert osc >= ov + B * H * d * npad and need >= osc + 12 * B * H
-    assert all(x % 256 == 0 for x in (oq, ok, ov, osc))
+    n = B * H * N * d
+    assert oq == 0 and oql >= n and ok >= oql + n and ov >= ok + n
+    assert osc >= ov + B * H * d * npad and need >= osc + 2 * 12 * B * H
+    assert all(x % 256 == 0 for x in (oq, oql, ok, ov, osc))
 
     def call(ws, nbytes, **kw):
         a = dict(rotate=1, lse=P, d=d)

@@ -114,22 +114,24 @@ def fp8_workspace_bytes(B, H, N, d):
 
 
 def fp8_workspace_views(ws, B, H, N, d):
-    """Views (q8, k8, v8t, scales) into an fp8 workspace (uint8 tensor).
+    """Views (q8, q8lo, k8, v8t, scales) into an fp8 workspace (uint8 tensor).
 
-    q8, k8: uint8 [B,H,N,d] e4m3 codes; v8t: uint8 [B,H,d,Npad] (V transposed,
-    zero padded to Npad = N rounded up to 64); scales: fp32 [3, B, H].
+    q8, q8lo, k8: uint8 [B,H,N,d] e4m3 codes (q8lo: residual of Q'); v8t: uint8
+    [B,H,d,Npad] (V transposed, zero padded to Npad = N rounded up to 64, keys
+    permuted inside each 64-key block); scales: fp32 [3, B, H].
     """
     torch = _torch()
-    offs = [ctypes.c_size_t() for _ in range(4)]
+    offs = [ctypes.c_size_t() for _ in range(5)]
     _call(lib().fattn_fwd_fp8_workspace_layout(B, H, N, d, *[ctypes.byref(x) for x in offs]))
-    oq, ok, ov, osc = (x.value for x in offs)
+    oq, oql, ok, ov, osc = (x.value for x in offs)
     npad = (N + 63) // 64 * 64
     n = B * H * N * d
     q8 = ws[oq:oq + n].view(B, H, N, d)
+    q8lo = ws[oql:oql + n].view(B, H, N, d)
     k8 = ws[ok:ok + n].view(B, H, N, d)
     v8t = ws[ov:ov + B * H * d * npad].view(B, H, d, npad)
     sc = ws[osc:osc + 12 * B * H].view(torch.float32).view(3, B, H)
-    return q8, k8, v8t, sc
+    return q8, q8lo, k8, v8t, sc
 
 
 def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=True,

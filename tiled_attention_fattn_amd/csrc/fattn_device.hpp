@@ -45,6 +45,11 @@ __device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// Same product with the B operand scaled by 2^-4 (E8M0 block scale 123).
+__device__ __forceinline__ f32x16 mfma32_fp8_bscale(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 123);
+}
+
 // Row index of accumulator register r in lane-half h (column = lane%32).
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
@@ -53,18 +58,28 @@ __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >
 // per row so that the 32-row × 16-byte MFMA operand reads and the 8-row
 // transpose reads spread over all banks.
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int swz_chunk(int row, int chunk) {
-  if constexpr (D == 128) {
+// Rows of RB bytes (RB = 64, 128 or 256): the chunk index is XORed with a
+// function of the row that sends the rows sharing a 256-byte bank window to
+// different chunk positions.
+template <int RB>
+__device__ __forceinline__ int swz_chunk_rb(int row, int chunk) {
+  if constexpr (RB == 256) {
     return chunk ^ ((row & 7) << 1);
-  } else {
+  } else if constexpr (RB == 128) {
     return chunk ^ (((row >> 1) & 3) << 1);
+  } else {
+    return chunk ^ ((row >> 2) & 3);
   }
+}
+// Byte offset of (row, 16-byte chunk) in a tile with RB-byte rows.
+template <int RB>
+__device__ __forceinline__ int tile_off_rb(int row, int chunk) {
+  return row * RB + swz_chunk_rb<RB>(row, chunk) * 16;
 }
 // Byte offset of (row, 16-byte chunk) in a [rows][D] bf16 tile.
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * (D * 2) + swz_chunk<D>(row, chunk) * 16;
+  return tile_off_rb<D * 2>(row, chunk);
 }
 
 // ds_read_b64_tr_b16 on gfx950: within each 16-lane group g, output lane i

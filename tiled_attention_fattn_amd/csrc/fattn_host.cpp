@@ -83,7 +83,7 @@ fattn_status hip_status(hipError_t e, const char* what) {
   } while (0)
 
 struct Fp8Layout {
-  size_t q8, k8, v8t, scales, total;
+  size_t q8, q8lo, k8, v8t, scales, amax, total;
 };
 
 Fp8Layout fp8_layout(int B, int H, int N, int d) {
@@ -91,10 +91,12 @@ Fp8Layout fp8_layout(int B, int H, int N, int d) {
   const size_t npad = round_up((size_t)N, fattn::kFp8Npad);
   Fp8Layout L;
   L.q8 = 0;
-  L.k8 = round_up(L.q8 + bh * N * d, 256);
+  L.q8lo = round_up(L.q8 + bh * N * d, 256);
+  L.k8 = round_up(L.q8lo + bh * N * d, 256);
   L.v8t = round_up(L.k8 + bh * N * d, 256);
   L.scales = round_up(L.v8t + bh * d * npad, 256);
-  L.total = round_up(L.scales + 3 * bh * sizeof(float), 256);
+  L.amax = round_up(L.scales + 3 * bh * sizeof(float), 256);
+  L.total = round_up(L.amax + 3 * bh * sizeof(uint32_t), 256);
   return L;
 }
 
@@ -159,10 +161,12 @@ size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
 }
 
 fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d, size_t* off_q8,
-                                            size_t* off_k8, size_t* off_v8t, size_t* off_scales) {
+                                            size_t* off_q8lo, size_t* off_k8, size_t* off_v8t,
+                                            size_t* off_scales) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FATTN_EINVAL, "B, H, N and d must be >= 1");
   const Fp8Layout L = fp8_layout(B, H, N, d);
   if (off_q8) *off_q8 = L.q8;
+  if (off_q8lo) *off_q8lo = L.q8lo;
   if (off_k8) *off_k8 = L.k8;
   if (off_v8t) *off_v8t = L.v8t;
   if (off_scales) *off_scales = L.scales;
@@ -179,6 +183,8 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   if (lse != nullptr && !aligned16(lse)) return fail(FATTN_EINVAL, "lse is not 16-byte aligned");
   FATTN_TRY(check_shape(B, H, N, d, causal, scale));
   if (rotate != 0 && rotate != 1) return fail(FATTN_EINVAL, "rotate must be 0 or 1 (got %d)", rotate);
+  if ((long long)B * H > 65535)
+    return fail(FATTN_ENOTSUP, "fp8 forward supports B*H <= 65535 (got %lld)", (long long)B * H);
   if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
   if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
   const Fp8Layout L = fp8_layout(B, H, N, d);
@@ -187,8 +193,9 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   FATTN_TRY(check_device());
   char* ws = (char*)workspace;
   return hip_status(fattn::launch_fwd_fp8(q, k, v, o, lse, (uint8_t*)(ws + L.q8),
-                                          (uint8_t*)(ws + L.k8), (uint8_t*)(ws + L.v8t),
-                                          (float*)(ws + L.scales), B, H, N, d, causal != 0, scale,
+                                          (uint8_t*)(ws + L.q8lo), (uint8_t*)(ws + L.k8), (uint8_t*)(ws + L.v8t),
+                                          (float*)(ws + L.scales), (uint32_t*)(ws + L.amax), B,
+                                          H, N, d, causal != 0, scale,
                                           rotate != 0, seed, (hipStream_t)stream),
                     "fattn_fwd_fp8 launch");
 }

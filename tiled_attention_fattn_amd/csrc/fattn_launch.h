@@ -17,11 +17,13 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
                            float* dq_acc, float* dvec, int B, int H, int N, int d, bool causal,
                            float scale, hipStream_t stream);
 
-// fp8 forward: q8/k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32 [3][B*H].
+// fp8 forward: q8/q8lo/k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32
+// [3][B*H]; amax uint32 [3][B*H] scratch.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
-                          uint8_t* q8, uint8_t* k8, uint8_t* v8t, float* scales, int B, int H,
-                          int N, int d, bool causal, float scale, bool rotate, uint64_t seed,
-                          hipStream_t stream);
+                          uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
+                          uint32_t* amax,
+                          int B, int H, int N, int d, bool causal, float scale, bool rotate,
+                          uint64_t seed, hipStream_t stream);
 
 constexpr int kFp8Npad = 64;
 

@@ -1,8 +1,478 @@
+// fp8 (OCP e4m3fn) attention forward with incoherent processing, for gfx950.
+//
+// FlashAttention-3 page, innovation 3: Q and K are multiplied by a random
+// orthogonal (Hadamard) matrix before fp8 quantisation, which spreads outlier
+// coordinates and cannot change Q·Kᵀ. Here R = diag(s)·H_d/√d with s from
+// SplitMix64 (Steele, Lea & Flood 2014) and H_d the Sylvester Hadamard matrix,
+// applied row by row with a fast Walsh–Hadamard transform in registers.
+//
+// Launches (one stream):
+//   1. fp8_init   — clear the per-head amax scratch.
+//   2. fp8_amax   — per (b,h) amax of |Q·R|, |K·R| and |V| (atomic max on the
+//                   float bits, all values non-negative).
+//   3. fp8_quant_qk — recompute Q·R, K·R; code = e4m3(t), t = x·448/amax
+//                   (one correctly rounded division), round to nearest even;
+//                   for Q' also the residual code e4m3(16·(t − decode(code)));
+//                   write Q8, Q8lo, K8 and the scales.
+//   4. fp8_quant_v  — V codes written transposed ([d][keys]) in the key order
+//                   the attention kernel's P operand uses.
+//   5. fwd_fp8    — attention: Sᵀ = K8·(Q8 + Q8lo/16)ᵀ (two MFMAs, the second
+//                   with the block scale 2^-4) and Oᵀ += V8ᵀ·P8ᵀ on the
+//                   32x32x64 f8f6f4 MFMA; P̃ = 2^(s·c − m + 8) quantised to
+//                   e4m3 (P̃ ≤ 1 because the running max is updated whenever
+//                   it grows, so P̃·2^8 ≤ 256 < 448); O = Oᵀ·s_v/l.
+#include "fattn_device.hpp"
 #include "fattn_launch.h"
+
 namespace fattn {
-hipError_t launch_fwd_fp8(const void*, const void*, const void*, void*, float*, uint8_t*, uint8_t*,
-                          uint8_t*, float*, int, int, int, int, bool, float, bool, uint64_t,
-                          hipStream_t) {
-  return hipErrorNotSupported;
+
+constexpr float kE4m3Max = 448.0f;
+
+// SplitMix64: state advanced by the golden-ratio increment, then mixed.
+__device__ __forceinline__ float rotation_sign(uint64_t seed, int i) {
+  uint64_t z = seed + (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z = z ^ (z >> 31);
+  return (z >> 63) ? -1.0f : 1.0f;
 }
+
+// Unnormalised Walsh–Hadamard transform of one row held by LPR lanes with 8
+// consecutive elements each (element index = lane_in_row·8 + e).
+template <int LPR>
+__device__ __forceinline__ void fwht_row(float (&x)[8], int lane_in_row) {
+#pragma unroll
+  for (int w = 1; w < 8; w <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!(e & w)) {
+        const float a = x[e], b = x[e + w];
+        x[e] = a + b;
+        x[e + w] = a - b;
+      }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) {
+    const bool upper = lane_in_row & m;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = __shfl_xor(x[e], m, LPR);
+      x[e] = upper ? (y - x[e]) : (x[e] + y);
+    }
+  }
+}
+
+// Loads the 8 values of (row, part), rotated when `rot`; false if row >= N.
+template <int D>
+__device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, int part, bool rot,
+                                              const float* sgn, float (&x)[8]) {
+  constexpr int LPR = D / 8;
+  const bool ok = row < N;
+  bf16x8 v = {};
+  if (ok) v = *(const bf16x8*)(src + (size_t)row * D + part * 8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  if (rot) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= sgn[part * 8 + e];
+    fwht_row<LPR>(x, part);
+    const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= inv_sqrt_d;
+  }
+  return ok;
+}
+
+__global__ void fp8_init_kernel(uint32_t* amax, int n) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) amax[t] = 0u;
+}
+
+// grid (row blocks, BH, 3 tensors); 256 threads = (256/LPR) rows × LPR lanes.
+template <int D>
+__global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ Q,
+                                                      const bf16* __restrict__ K,
+                                                      const bf16* __restrict__ V,
+                                                      uint32_t* __restrict__ amax, int N, int BH,
+                                                      int rotate, uint64_t seed) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  __shared__ float sgn[D];
+  const int t = blockIdx.z, bh = blockIdx.y;
+  const bool rot = rotate && t < 2;
+  if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
+  __syncthreads();
+  const bf16* src = (t == 0 ? Q : t == 1 ? K : V) + (size_t)bh * N * D;
+  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float x[8];
+  load_row_part<D>(src, row, N, part, rot, sgn, x);
+  float m = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax + t * BH + bh, __float_as_uint(m));
+}
+
+__device__ __forceinline__ float scale_from_amax(uint32_t bits) {
+  const float a = __uint_as_float(bits);
+  return a > 0.0f ? a / kE4m3Max : 1.0f;
+}
+
+// Four e4m3 codes (round to nearest even), a in the lowest byte.
+__device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+// Two e4m3 codes in the low 16 bits.
+__device__ __forceinline__ int cvt_fp8x2(float a, float b) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+}
+
+__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -kE4m3Max), kE4m3Max); }
+
+// Decode the four e4m3 codes of a packed word (lowest byte first).
+__device__ __forceinline__ void dec_fp8x4(int w, float* out) {
+  out[0] = __builtin_amdgcn_cvt_f32_fp8(w, 0);
+  out[1] = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+  out[2] = __builtin_amdgcn_cvt_f32_fp8(w, 2);
+  out[3] = __builtin_amdgcn_cvt_f32_fp8(w, 3);
+}
+
+// x·448/amax with one correctly rounded division (x·448 is exact for bf16 x),
+// so exact e4m3 midpoints stay exact.
+__device__ __forceinline__ float ratio448(float x, float am) { return __fdiv_rn(x * kE4m3Max, am); }
+
+// grid (row blocks, BH, 2 tensors)
+template <int D>
+__global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restrict__ Q,
+                                                          const bf16* __restrict__ K,
+                                                          uint8_t* __restrict__ q8,
+                                                          uint8_t* __restrict__ q8lo,
+                                                          uint8_t* __restrict__ k8,
+                                                          const uint32_t* __restrict__ amax,
+                                                          float* __restrict__ scales, int N, int BH,
+                                                          int rotate, uint64_t seed) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  __shared__ float sgn[D];
+  const int t = blockIdx.z, bh = blockIdx.y;
+  if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
+  __syncthreads();
+  const size_t head = (size_t)bh * N * D;
+  const bf16* src = (t == 0 ? Q : K) + head;
+  uint8_t* dst = (t == 0 ? q8 : k8) + head;
+  const uint32_t abits = amax[t * BH + bh];
+  const float am = __uint_as_float(abits);
+  if (blockIdx.x == 0 && threadIdx.x == 0) scales[t * BH + bh] = scale_from_amax(abits);
+  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float x[8];
+  if (!load_row_part<D>(src, row, N, part, rotate != 0, sgn, x)) return;
+  float tt[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) tt[e] = am > 0.0f ? clamp448(ratio448(x[e], am)) : x[e];
+  i32x2 w;
+  w[0] = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
+  w[1] = cvt_fp8x4(tt[4], tt[5], tt[6], tt[7]);
+  *(i32x2*)(dst + (size_t)row * D + part * 8) = w;
+  if (t == 0) {
+    // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
+    float dec[8];
+    dec_fp8x4(w[0], dec);
+    dec_fp8x4(w[1], dec + 4);
+    float r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = 16.0f * (tt[e] - dec[e]);
+    i32x2 wl;
+    wl[0] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
+    wl[1] = cvt_fp8x4(r[4], r[5], r[6], r[7]);
+    *(i32x2*)(q8lo + head + (size_t)row * D + part * 8) = wl;
+  }
+}
+
+// Position of key r (0..63) inside its 64-key block of V8ᵀ.
+__device__ __forceinline__ int v8_pos(int r) {
+  const int s = 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3);
+  return 32 * ((r >> 2) & 1) + s;
+}
+
+// grid (Npad/64, BH): one 64-key block of one head, transposed through LDS.
+template <int D>
+__global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict__ V,
+                                                         uint8_t* __restrict__ v8t,
+                                                         const uint32_t* __restrict__ amax,
+                                                         float* __restrict__ scales, int N,
+                                                         int Npad, int BH) {
+  constexpr int CHUNKS = D / 8;
+  constexpr int CPT = 64 * CHUNKS / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * 64];
+  const int bh = blockIdx.y, kb = blockIdx.x;
+  const uint32_t abits = amax[2 * BH + bh];
+  const float am = __uint_as_float(abits);
+  if (kb == 0 && threadIdx.x == 0) scales[2 * BH + bh] = scale_from_amax(abits);
+  const bf16* src = V + (size_t)bh * N * D;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int ch = threadIdx.x + i * 256;
+    const int r = ch / CHUNKS, cc = ch % CHUNKS;
+    const int key = kb * 64 + r;
+    bf16x8 v = {};
+    if (key < N) v = *(const bf16x8*)(src + (size_t)key * D + cc * 8);
+    const int p = v8_pos(r);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float a = (float)v[e], b = (float)v[e + 1];
+      const int w = am > 0.0f ? cvt_fp8x2(clamp448(ratio448(a, am)), clamp448(ratio448(b, am)))
+                              : cvt_fp8x2(a, b);
+      tile[(cc * 8 + e) * 64 + p] = (uint8_t)(w & 0xff);
+      tile[(cc * 8 + e + 1) * 64 + p] = (uint8_t)((w >> 8) & 0xff);
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = v8t + (size_t)bh * D * Npad + (size_t)kb * 64;
+  for (int ch = threadIdx.x; ch < D * 4; ch += 256) {
+    const int d = ch >> 2, part = ch & 3;
+    *(i32x4*)(dst + (size_t)d * Npad + part * 16) = *(const i32x4*)(tile + d * 64 + part * 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 attention kernel: 4 waves × 32 queries, 64-key tiles.
+// ---------------------------------------------------------------------------
+constexpr int kF8Waves = 4;
+constexpr int kF8BM = 32 * kF8Waves;
+constexpr int kF8BN = 64;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ q8lo,
+                    const uint8_t* __restrict__ k8,
+                    const uint8_t* __restrict__ v8t, const float* __restrict__ scales,
+                    bf16* __restrict__ O, float* __restrict__ LSE, int N, int Npad, int BH,
+                    int n_qtiles, float scale_log2) {
+  constexpr int KD = D / 64;           // fp8 MFMA k-steps over d
+  constexpr int KB = kF8BN * D;        // bytes of the K8 tile ([64][D])
+  constexpr int VB = D * kF8BN;        // bytes of the V8ᵀ tile ([D][64])
+  constexpr int KCH = D / 16;          // 16-byte chunks per K8 row
+  constexpr int KCPT = kF8BN * KCH / 256;
+  constexpr int VCPT = D * 4 / 256;
+  constexpr int DT = D / 32;
+  __shared__ __attribute__((aligned(16))) char lds[2 * (KB + VB)];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, c = lane & 31;
+
+  const int total = n_qtiles * BH;
+  int logical = blockIdx.x;
+  if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int bh = logical / n_qtiles;
+  int qt = logical - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+
+  const float sq = scales[bh], sk = scales[BH + bh], sv = scales[2 * BH + bh];
+  const float c_log2 = sq * sk * scale_log2;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint8_t* Qh = q8 + head;
+  const uint8_t* Ql = q8lo + head;
+  const uint8_t* Kh = k8 + head;
+  const uint8_t* Vt = v8t + (size_t)bh * D * Npad;
+  const int q_start = qt * kF8BM;
+  const int q0 = q_start + wave * 32;
+  const int qi = q0 + c;
+
+  i32x8 qreg[KD], qlo[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) {
+    if (qi < N) {
+      const size_t off = (size_t)qi * D + kk * 64 + 32 * h;
+      const i32x4 a = *(const i32x4*)(Qh + off);
+      const i32x4 b = *(const i32x4*)(Qh + off + 16);
+      qreg[kk] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+      const i32x4 al = *(const i32x4*)(Ql + off);
+      const i32x4 bl = *(const i32x4*)(Ql + off + 16);
+      qlo[kk] = __builtin_shufflevector(al, bl, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      qreg[kk] = i32x8{};
+      qlo[kk] = i32x8{};
+    }
+  }
+
+  const int kv_end = CAUSAL ? min(N, q_start + kF8BM) : N;
+  const int n_kv = (kv_end + kF8BN - 1) / kF8BN;
+
+  i32x4 pk[KCPT], pv[VCPT];
+  auto gload = [&](int j) {
+    const int key0 = j * kF8BN;
+#pragma unroll
+    for (int i = 0; i < KCPT; ++i) {
+      const int ch = tid + i * 256;
+      const int r = ch / KCH, cc = ch % KCH;
+      pk[i] = (key0 + r < N) ? *(const i32x4*)(Kh + (size_t)(key0 + r) * D + cc * 16) : i32x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < VCPT; ++i) {
+      const int ch = tid + i * 256;
+      const int d = ch >> 2, part = ch & 3;
+      pv[i] = *(const i32x4*)(Vt + (size_t)d * Npad + key0 + part * 16);
+    }
+  };
+  auto lstore = [&](int stage) {
+    char* kb = lds + stage * (KB + VB);
+    char* vb = kb + KB;
+#pragma unroll
+    for (int i = 0; i < KCPT; ++i) {
+      const int ch = tid + i * 256;
+      const int r = ch / KCH, cc = ch % KCH;
+      *(i32x4*)(kb + tile_off_rb<D>(r, cc)) = pk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCPT; ++i) {
+      const int ch = tid + i * 256;
+      const int d = ch >> 2, part = ch & 3;
+      *(i32x4*)(vb + tile_off_rb<64>(d, part)) = pv[i];
+    }
+  };
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  float m_c = -INFINITY;
+  float l_part = 0.0f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_kv; ++j) {
+    const int stage = j & 1;
+    if (j + 1 < n_kv) gload(j + 1);
+    const char* kb = lds + stage * (KB + VB);
+    const char* vb = kb + KB;
+    const int key0 = j * kF8BN;
+    const bool active = !CAUSAL || key0 <= q0 + 31;
+    if (active) {
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{};
+        const int row = 32 * t + c;
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          const i32x4 a0 = *(const i32x4*)(kb + tile_off_rb<D>(row, 4 * kk + 2 * h));
+          const i32x4 a1 = *(const i32x4*)(kb + tile_off_rb<D>(row, 4 * kk + 2 * h + 1));
+          const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+          s[t] = mfma32_fp8(a, qreg[kk], s[t]);
+          s[t] = mfma32_fp8_bscale(a, qlo[kk], s[t]);
+        }
+      }
+      const bool need_mask = (key0 + kF8BN > N) || (CAUSAL && key0 + kF8BN - 1 > q0);
+      if (need_mask) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * t + acc_row(r, h);
+            if (key >= N || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      mx = half_max(mx);
+      const float mx_c = mx * c_log2;
+      const bool resc = mx_c > m_c;
+      if (__ballot(resc)) {
+        const float m_new = resc ? mx_c : m_c;
+        const float alpha = resc ? exp2_hw(m_c - m_new) : 1.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        l_part *= alpha;
+        m_c = m_new;
+      }
+      // P̃·2^8 in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
+      const float off = 8.0f - m_c;
+      i32x8 p8;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          float pv4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pv4[e] = exp2_hw(fmaf(s[t][4 * wd + e], c_log2, off));
+            l_part += pv4[e];
+          }
+          p8[4 * t + wd] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
+        }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int row = 32 * dt + c;
+        const i32x4 a0 = *(const i32x4*)(vb + tile_off_rb<64>(row, 2 * h));
+        const i32x4 a1 = *(const i32x4*)(vb + tile_off_rb<64>(row, 2 * h + 1));
+        oacc[dt] = mfma32_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8, oacc[dt]);
+      }
+    }
+    if (j + 1 < n_kv) lstore(stage ^ 1);
+    __syncthreads();
+  }
+
+  const float l = half_sum(l_part);
+  const float inv = sv / l;
+  if (qi < N) {
+    bf16* Orow = O + head + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        i32x2 w;
+        w[0] = (int)pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
+        w[1] = (int)pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        *(i32x2*)(Orow + 32 * dt + 8 * g + 4 * h) = w;
+      }
+    if (LSE != nullptr && h == 0)
+      LSE[(size_t)bh * N + qi] = (m_c + __builtin_log2f(l) - 8.0f) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse,
+                               uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
+                               uint32_t* amax, int BH, int N, float scale, bool rotate,
+                               uint64_t seed, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 8);
+  const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
+  hipLaunchKernelGGL(fp8_init_kernel, dim3((3 * BH + 255) / 256), dim3(256), 0, stream, amax,
+                     3 * BH);
+  const unsigned rblocks = (unsigned)((N + RPB - 1) / RPB);
+  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(rblocks, BH, 3), dim3(256), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, amax, N, BH, (int)rotate, seed);
+  hipLaunchKernelGGL((fp8_quant_qk_kernel<D>), dim3(rblocks, BH, 2), dim3(256), 0, stream,
+                     (const bf16*)q, (const bf16*)k, q8, q8lo, k8, (const uint32_t*)amax, scales, N, BH,
+                     (int)rotate, seed);
+  hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(Npad / 64, BH), dim3(256), 0, stream,
+                     (const bf16*)v, v8t, (const uint32_t*)amax, scales, N, Npad, BH);
+  const int n_qtiles = (N + kF8BM - 1) / kF8BM;
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, stream,
+                     (const uint8_t*)q8, (const uint8_t*)q8lo, (const uint8_t*)k8, (const uint8_t*)v8t,
+                     (const float*)scales, (bf16*)o, lse, N, Npad, BH, n_qtiles, scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                          uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
+                          uint32_t* amax, int B, int H, int N, int d, bool causal, float scale,
+                          bool rotate, uint64_t seed, hipStream_t stream) {
+  const int BH = B * H;
+  if (d == 64) {
+    return causal ? launch_fp8_t<64, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream)
+                  : launch_fp8_t<64, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream);
+  }
+  return causal ? launch_fp8_t<128, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream)
+                : launch_fp8_t<128, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream);
+}
+
 }  // namespace fattn
