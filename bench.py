@@ -40,7 +40,24 @@ def parse():
     ap.add_argument("--parts", default=",".join(PARTS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--no-exp-variants", action="store_true",
+                    help="skip the separate hw/poly exp2 timing of the forward")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a device-to-device copy of this many bytes "
+                         "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes, reps):
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch_read": n * 4, "write": n * 4, "launches": reps}))
 
 
 def source_hash(part):
@@ -139,6 +156,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the attention path has no multi-GPU mode).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, max(1, args.steps))
+        return
     import torch
     import tiled_attention_fattn_amd as fa
 
@@ -180,7 +200,7 @@ def main():
                    "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
 
     # The C3 forward is also reported with each exp2 variant.
-    if "fwd" in parts:
+    if "fwd" in parts and not args.no_exp_variants:
         variants = {}
         for mode in ("hw", "poly"):
             for _ in range(3):

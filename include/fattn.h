@@ -86,8 +86,10 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o,
  *   dq, dk, dv  [B,H,N,d] bf16 outputs.
  *   workspace   device memory of at least fattn_bwd_workspace_bytes(B,H,N,d)
  *               bytes, 256-byte aligned; contents on entry are ignored.
- *               Layout: fp32 dQ accumulator [B,H,N,d] at offset 0, then fp32
- *               D = rowsum(dO∘O) [B,H,N].
+ *               Layout (Npad = N rounded up to 64): fp32 dQ accumulator
+ *               [B,H,Npad,d] at offset 0, then fp32 D = rowsum(dO∘O)
+ *               [B,H,Npad], then fp32 LSE·log2(e) [B,H,Npad] (padded rows:
+ *               D = 0, +∞), each piece 256-byte aligned.
  * dK and dV are accumulated without atomics (each key block is owned by one
  * workgroup); dQ is reduced with fp32 global atomics, so dq is reproducible
  * only up to the order of floating-point additions.
@@ -117,7 +119,7 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v,
  *               the order in which the kernel's P operand holds keys),
  *               then fp32 scales [3][B·H]
  *               (Q', K', V per head: amax/448, or 1 for an all-zero head),
- *               then a uint32 [3][B·H] scratch for the running amax.
+ *               then an fp32 [3][B·H][⌈N/256⌉] scratch of per-chunk amax.
  * Each operand is quantised per (b,h): code = e4m3(x·448/amax), the exact
  * ratio rounded to nearest even. Q' keeps a second e4m3 term for its
  * quantisation residual, Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that

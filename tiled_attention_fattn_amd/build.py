@@ -55,6 +55,13 @@ def build(verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    # Every kernel's host stub must be defined: a host-pass problem in a kernel
+    # body can drop a stub silently and leave an undefined symbol behind.
+    import ctypes
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB)
     return LIB
 

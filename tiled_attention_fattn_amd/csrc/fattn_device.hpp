@@ -58,15 +58,19 @@ __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >
 // per row so that the 32-row × 16-byte MFMA operand reads and the 8-row
 // transpose reads spread over all banks.
 // ---------------------------------------------------------------------------
-// Rows of RB bytes (RB = 64, 128 or 256): the chunk index is XORed with a
-// function of the row that sends the rows sharing a 256-byte bank window to
-// different chunk positions.
+// Rows of RB bytes (RB = 64, 128 or 256); the LDS has 64 four-byte banks, so a
+// 256-byte window holds one row of 256 B, two of 128 B or four of 64 B. The
+// 16-byte chunk index is XORed with a bijection of the row so that
+//  * 16 consecutive rows read at the same chunk (the 16 lanes of a 16-byte
+//    MFMA operand read) land on 16 different 16-byte bank groups, and
+//  * 4 consecutive rows read over 4 consecutive chunks (a 16-lane group of the
+//    8-byte transpose read) cover 4 disjoint bank groups.
 template <int RB>
 __device__ __forceinline__ int swz_chunk_rb(int row, int chunk) {
   if constexpr (RB == 256) {
-    return chunk ^ ((row & 7) << 1);
+    return chunk ^ (((row & 3) << 2) | ((row >> 2) & 3));
   } else if constexpr (RB == 128) {
-    return chunk ^ (((row >> 1) & 3) << 1);
+    return chunk ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
   } else {
     return chunk ^ ((row >> 2) & 3);
   }
@@ -89,6 +93,44 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
   i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 FATTN_LDS*)(p));
   return __builtin_bit_cast(bf16x4, v);
 }
+
+// Buffer resource over `bytes` bytes from `base` (raw buffer, 32-bit data
+// format so that the range check applies): loads at byte offsets ≥ bytes
+// return zero.
+// (The buffer-resource type exists only in the device compilation; the host
+// pass sees empty bodies for these helpers, which it never runs.)
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+#endif
+
+// Moves LOADS × 1 KB of a tile into LDS with buffer loads: wave load i takes
+// 16 bytes per lane from byte offset off[i] of the buffer [base, base + bytes)
+// (zero past the end) to LDS at dst + (first + i)·1 KB + lane·16.
+template <int LOADS>
+__device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, char* dst,
+                                              const int (&off)[LOADS], int first) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, bytes);
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FATTN_LDS void*)(dst + (first + i) * 1024), 16,
+                                             off[i], 0, 0, 0);
+#endif
+}
+
+// 64 floats from `src` into LDS at `dst` (one 4-byte element per lane).
+__device__ __forceinline__ void stats_to_lds(const float* src, char* dst, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, 256);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FATTN_LDS void*)dst, 4, lane * 4, 0, 0, 0);
+#endif
+}
+
+// Wait until this wave's outstanding global loads (including those that
+// write straight into LDS) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);

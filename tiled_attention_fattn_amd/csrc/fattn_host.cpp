@@ -83,7 +83,7 @@ fattn_status hip_status(hipError_t e, const char* what) {
   } while (0)
 
 struct Fp8Layout {
-  size_t q8, q8lo, k8, v8t, scales, amax, total;
+  size_t q8, q8lo, k8, v8t, scales, partial, total;
 };
 
 Fp8Layout fp8_layout(int B, int H, int N, int d) {
@@ -95,8 +95,9 @@ Fp8Layout fp8_layout(int B, int H, int N, int d) {
   L.k8 = round_up(L.q8lo + bh * N * d, 256);
   L.v8t = round_up(L.k8 + bh * N * d, 256);
   L.scales = round_up(L.v8t + bh * d * npad, 256);
-  L.amax = round_up(L.scales + 3 * bh * sizeof(float), 256);
-  L.total = round_up(L.amax + 3 * bh * sizeof(uint32_t), 256);
+  const size_t nchunks = (N + fattn::kFp8AmaxRows - 1) / fattn::kFp8AmaxRows;
+  L.partial = round_up(L.scales + 3 * bh * sizeof(float), 256);
+  L.total = round_up(L.partial + 3 * bh * nchunks * sizeof(float), 256);
   return L;
 }
 
@@ -123,8 +124,8 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o, flo
 
 size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
-  const size_t n = (size_t)B * H * N;
-  return round_up(n * d * sizeof(float), 256) + round_up(n * sizeof(float), 256);
+  const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
+  return round_up(n * d * sizeof(float), 256) + 2 * round_up(n * sizeof(float), 256);
 }
 
 fattn_status fattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -147,11 +148,12 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v, const void* 
   if (workspace_bytes < need)
     return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, need);
   FATTN_TRY(check_device());
-  const size_t n = (size_t)B * H * N;
+  const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
   float* dq_acc = (float*)workspace;
   float* dvec = (float*)((char*)workspace + round_up(n * d * sizeof(float), 256));
-  return hip_status(fattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, B, H,
-                                           N, d, causal != 0, scale, (hipStream_t)stream),
+  float* lse2 = (float*)((char*)dvec + round_up(n * sizeof(float), 256));
+  return hip_status(fattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, lse2, B,
+                                           H, N, d, causal != 0, scale, (hipStream_t)stream),
                     "fattn_bwd launch");
 }
 
@@ -194,7 +196,7 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   char* ws = (char*)workspace;
   return hip_status(fattn::launch_fwd_fp8(q, k, v, o, lse, (uint8_t*)(ws + L.q8),
                                           (uint8_t*)(ws + L.q8lo), (uint8_t*)(ws + L.k8), (uint8_t*)(ws + L.v8t),
-                                          (float*)(ws + L.scales), (uint32_t*)(ws + L.amax), B,
+                                          (float*)(ws + L.scales), (float*)(ws + L.partial), B,
                                           H, N, d, causal != 0, scale,
                                           rotate != 0, seed, (hipStream_t)stream),
                     "fattn_fwd_fp8 launch");

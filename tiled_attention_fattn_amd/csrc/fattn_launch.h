@@ -11,20 +11,24 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int N, int d, bool causal, float scale, int exp_mode,
                            hipStream_t stream);
 
-// Backward: `dq_acc` fp32 [B,H,N,d] and `dvec` fp32 [B,H,N] live in the caller's workspace.
+// Backward: `dq_acc` fp32 [B,H,Npad,d], `dvec` and `lse2` fp32 [B,H,Npad] live
+// in the caller's workspace (Npad = N rounded up to kBwdRowPad).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* dq_acc, float* dvec, int B, int H, int N, int d, bool causal,
-                           float scale, hipStream_t stream);
+                           float* dq_acc, float* dvec, float* lse2, int B, int H, int N, int d,
+                           bool causal, float scale, hipStream_t stream);
+
+constexpr int kBwdRowPad = 64;
 
 // fp8 forward: q8/q8lo/k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32
-// [3][B*H]; amax uint32 [3][B*H] scratch.
+// [3][B*H]; partial fp32 [3][B*H][ceil(N/kFp8AmaxRows)] scratch.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                           uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
-                          uint32_t* amax,
+                          float* partial,
                           int B, int H, int N, int d, bool causal, float scale, bool rotate,
                           uint64_t seed, hipStream_t stream);
 
 constexpr int kFp8Npad = 64;
+constexpr int kFp8AmaxRows = 256;  // rows per amax chunk
 
 }  // namespace fattn

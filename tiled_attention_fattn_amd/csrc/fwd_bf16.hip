@@ -2,37 +2,122 @@
 //
 // What is computed (FlashAttention-4 news page, "Por qué el enfoque estándar
 // ya no funciona"; FlashAttention-3 page, "FlashAttention y FlashAttention-2"):
-// O = softmax(scale·Q·Kᵀ [causal]) · V, one workgroup per 128 query rows of
+// O = softmax(scale·Q·Kᵀ [causal]) · V, one workgroup per 256 query rows of
 // one head; K and V stream through LDS in 64-key tiles; the scores and the
 // probabilities never leave the compute unit.
 //
-// Layout inside a workgroup (4 waves of 64 lanes, 32 queries per wave):
+// Layout inside a workgroup (4 waves of 64 lanes, one wave per SIMD, 64
+// queries per wave split in two 32-query sub-tiles A and B):
 //  * Sᵀ = K·Qᵀ on 32x32x16 bf16 MFMA: the accumulator column is the query,
 //    so each lane owns one query row and the row max / row sum are in-lane
-//    reductions plus one exchange between the two lane halves.
+//    reductions plus one exchange between the two lane halves. Each K operand
+//    read from LDS feeds the MFMAs of both sub-tiles.
 //  * Oᵀ += Vᵀ·Pᵀ on the same MFMA: Pᵀ is taken straight from the Sᵀ
 //    accumulator registers (the k order inside a 16-key step is free as long
 //    as the Vᵀ operand uses the same order); Vᵀ comes from the row-major V tile
-//    through the LDS transpose read.
+//    through the LDS transpose read, again shared by both sub-tiles.
+//  * The two sub-tiles are staggered so that the softmax (VALU and
+//    transcendental work) of one overlaps the MFMAs of the other:
+//      S_A | S_B ∥ softmax_A | PV_A ∥ softmax_B | PV_B
+//    (FlashAttention-4 news page, "Cómo Together AI resolvió el problema":
+//    overlap the tensor units, the exponential units and memory).
 //  * Online softmax in the exp2 domain with conditional rescaling
 //    (FlashAttention-4 gist, technical summary 2.B): the running max used for
 //    the exponent moves only when a new tile max exceeds it by more than
 //    kRescaleTau, so most tiles skip the rescale of Oᵀ and l. Exact, because
 //    the same max is used for O, l and LSE.
+//  * Row sums are taken on the bf16 values that enter the PV product
+//    (v_dot2_f32_bf16 against (1, 1)), so numerator and denominator see the
+//    same probabilities.
 //  * K/V tiles are double-buffered: the next tile's global loads are issued
 //    before the current tile's math and written to the other LDS stage after it
 //    (FlashAttention-3 page, innovation 2: loads hidden behind compute).
 //  * Causal: key tiles past the workgroup's last query are never loaded, and a
 //    wave skips tiles that lie wholly above its diagonal.
+#include <type_traits>
+
 #include "fattn_device.hpp"
 #include "fattn_launch.h"
 
 namespace fattn {
 
 constexpr int kFwdWaves = 4;
-constexpr int kFwdBM = 32 * kFwdWaves;  // query rows per workgroup
-constexpr int kFwdBN = 64;              // keys per K/V tile
-constexpr float kRescaleTau = 8.0f;     // log2 units: P̃ ≤ 2^8 between rescales
+constexpr int kFwdQW = 32;                  // queries per wave
+constexpr int kFwdBM = kFwdQW * kFwdWaves;  // query rows per workgroup
+constexpr int kFwdBN = 64;                  // keys per K/V tile
+constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between rescales
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100, SG_TRANS = 0x400 };
+
+// Running softmax state of one 32-query sub-tile (per lane: one query).
+template <int DT>
+struct SubTile {
+  f32x16 o[DT];
+  float m_c;     // exponent offset in use (log2 domain)
+  float l_part;  // this lane half's share of the row sum
+};
+
+// Masks the scores of a 64-key tile for ragged N and the causal diagonal.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int N, int qi, int h) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + t * 32 + acc_row(r, h);
+      if (key >= N || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
+    }
+}
+
+// Tile row max, conditional rescale of the sub-tile state (rare branch).
+template <int DT>
+__device__ __forceinline__ void softmax_update_max(SubTile<DT>& st, const f32x16 (&s)[2],
+                                                   float c_log2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+  mx = half_max(mx);
+  const float mx_c = mx * c_log2;
+  const bool resc = mx_c > st.m_c + kRescaleTau;
+  if (__ballot(resc)) {
+    const float m_new = resc ? mx_c : st.m_c;
+    const float alpha = resc ? exp2_hw(st.m_c - m_new) : 1.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[dt][r] *= alpha;
+    st.l_part *= alpha;
+    st.m_c = m_new;
+  }
+}
+
+// P̃ = 2^(s·c − m_c) packed to bf16 in the Pᵀ operand layout (slot e of step
+// ks: key 16ks + 8(e/4) + 4h + e%4), and the row-sum update.
+template <int EXPM, int DT>
+__device__ __forceinline__ void softmax_exp(SubTile<DT>& st, const f32x16 (&s)[2], float c_log2,
+                                            bf16x8 (&p)[4]) {
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  float l = st.l_part;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      i32x4 packed;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e], c_log2, -st.m_c));
+        const float p1 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e + 1], c_log2, -st.m_c));
+        const uint32_t w = pack_bf16x2(p0, p1);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l, false);
+        packed[e] = (int)w;
+      }
+      p[2 * t + half] = __builtin_bit_cast(bf16x8, packed);
+    }
+  st.l_part = l;
+}
 
 template <int D, bool CAUSAL, int EXPM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -40,15 +125,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
                      int N, int BH, int n_qtiles, float c_log2) {
   constexpr int KD = D / 16;          // MFMA k-steps over the head dimension
-  constexpr int CHUNKS = D / 8;       // 16-byte chunks per row
-  constexpr int TILE = kFwdBN * D * 2;
-  constexpr int CPT = kFwdBN * CHUNKS / 256;  // 16-byte chunks per thread per tensor
-  constexpr int NT = kFwdBN / 32;     // 32-key accumulator tiles
+  constexpr int RB = D * 2;           // bytes per K/V row
+  constexpr int TILE = kFwdBN * RB;
   constexpr int NS = kFwdBN / 16;     // 16-key PV steps
   constexpr int DT = D / 32;          // 32-wide output tiles over d
-  __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILE];
+  // LDS: K slots 0, 1 then V slots 0, 1.
+  __shared__ __attribute__((aligned(16))) char lds[4 * TILE];
+  char* const k_lds = lds;
+  char* const v_lds = lds + 2 * TILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int h = lane >> 5, c = lane & 31;
 
   // Workgroup → (head, query tile). Consecutive workgroup ids go to different
@@ -66,147 +153,172 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* Kh = K + head;
   const bf16* Vh = V + head;
   const int q_start = qt * kFwdBM;
-  const int q0 = q_start + wave * 32;
-  const int qi = q0 + c;
+  const int q0 = q_start + wave * kFwdQW;
+  const int qi = q0 + c;  // this lane's query
 
   // Qᵀ operand: lane holds Q[qi][16kk + 8h + 0..7].
-  bf16x8 qreg[KD];
+  bf16x8 qr[KD];
 #pragma unroll
-  for (int kk = 0; kk < KD; ++kk) {
-    if (qi < N) qreg[kk] = *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + 8 * h);
-    else qreg[kk] = bf16x8{};
-  }
+  for (int kk = 0; kk < KD; ++kk)
+    qr[kk] = qi < N ? *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
 
-  const int kv_end = CAUSAL ? min(N, q_start + kFwdBM) : N;
-  const int n_kv = (kv_end + kFwdBN - 1) / kFwdBN;
-
-  i32x4 pk[CPT], pv[CPT];
-  auto gload = [&](int j) {
-    const int key0 = j * kFwdBN;
+  // Per-lane LDS offsets, constant over the loop (the swizzle depends on the
+  // row only through bits that do not change between the 32-row tiles or the
+  // 16-row PV steps).
+  int koff[KD];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + i * 256;
-      const int r = ch / CHUNKS, cc = ch % CHUNKS;
-      const int key = key0 + r;
-      if (key < N) {
-        pk[i] = *(const i32x4*)(Kh + (size_t)key * D + cc * 8);
-        pv[i] = *(const i32x4*)(Vh + (size_t)key * D + cc * 8);
-      } else {
-        pk[i] = i32x4{};
-        pv[i] = i32x4{};
-      }
-    }
-  };
-  auto lstore = [&](int stage) {
-    char* kb = lds + stage * 2 * TILE;
-    char* vb = kb + TILE;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int ch = tid + i * 256;
-      const int r = ch / CHUNKS, cc = ch % CHUNKS;
-      const int off = tile_off<D>(r, cc);
-      *(i32x4*)(kb + off) = pk[i];
-      *(i32x4*)(vb + off) = pv[i];
-    }
-  };
-
-  f32x16 oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float m_c = -INFINITY;  // exponent offset in use (log2 domain)
-  float l_part = 0.0f;    // this lane half's share of the row sum
-
-  // Per-lane pieces of the transpose-read addresses (see lds_read_tr16).
+  for (int kk = 0; kk < KD; ++kk) koff[kk] = tile_off<D>(c, 2 * kk + h);
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   const int tr_sub = (lane & 1) * 8;
+  int voff[2][DT];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      voff[hf][dt] = tile_off<D>(tr_row + 8 * hf, 4 * dt + tr_chunk) + tr_sub;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  const int kv_end = CAUSAL ? min(N, q_start + kFwdBM) : N;
+  const int n_kv = (kv_end + kFwdBN - 1) / kFwdBN;
+  // First tile whose scores need the element mask (ragged end or diagonal).
+  const int first_masked = CAUSAL ? min(q_start / kFwdBN, N / kFwdBN) : N / kFwdBN;
 
-  for (int j = 0; j < n_kv; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < n_kv) gload(j + 1);
-    const char* kt = lds + stage * 2 * TILE;
-    const char* vt = kt + TILE;
+  // Global → LDS without staging registers: each wave moves 1 KB (64 lanes ×
+  // 16 B) per load straight into LDS at a wave-uniform base. The source is a
+  // buffer resource starting at the tile's first row and ending at row N, so
+  // rows past N read as zero (range check) and the per-lane byte offset is a
+  // loop constant; the swizzle is applied on the source side (the XOR
+  // swizzle is its own inverse).
+  constexpr int ROWS_PER_LOAD = 1024 / RB;          // rows per 1 KB wave load
+  constexpr int LOADS = TILE / 1024 / kFwdWaves;    // wave loads per tensor per tile
+  int ld_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = (wave * LOADS + i) * ROWS_PER_LOAD + lane / (RB / 16);
+    ld_off[i] = r * RB + swz_chunk_rb<RB>(r, lane % (RB / 16)) * 16;
+  }
+  auto gload = [&](const bf16* src, char* dst_tile, int j) __device__ {
     const int key0 = j * kFwdBN;
-    const bool active = !CAUSAL || key0 <= q0 + 31;
-    if (active) {
-      f32x16 s[NT];
+    buffer_to_lds<LOADS>(src + (size_t)key0 * D, (N - key0) * RB, dst_tile, ld_off, wave * LOADS);
+  };
+
+  SubTile<DT> st;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        s[t] = f32x16{};
-        const int row = t * 32 + c;
+  for (int dt = 0; dt < DT; ++dt) st.o[dt] = f32x16{};
+  st.l_part = 0.0f;
+
+  auto scores = [&](const char* kt, f32x16 (&s)[2]) {
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          const bf16x8 a = *(const bf16x8*)(kt + tile_off<D>(row, 2 * kk + h));
-          s[t] = mfma32(a, qreg[kk], s[t]);
-        }
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+        s[t] = mfma32(*(const bf16x8*)(kt + t * 32 * RB + koff[kk]), qr[kk], s[t]);
+    }
+  };
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    return half_max(mx) * c_log2;
+  };
+
+  // Prologue: K0, K1, V0 in flight; S(0); running max from tile 0.
+  gload(Kh, k_lds, 0);
+  if (n_kv > 1) gload(Kh, k_lds + TILE, 1);
+  gload(Vh, v_lds, 0);
+  wait_vmem();
+  __syncthreads();
+  f32x16 s[2];
+  scores(k_lds, s);
+  if (first_masked == 0) mask_tile<CAUSAL>(s, 0, N, qi, h);
+  st.m_c = tile_max(s);
+
+  // Iteration j: exp(S(j)) ∥ S(j+1) on the MFMA pipe, then max(S(j+1)) ∥
+  // PV(j), then the (rare) conditional rescale for tile j+1. The last
+  // iteration (no tile j+1) is peeled so that each of the two phases is one
+  // basic block the scheduler can interleave.
+  auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
+    constexpr int PAR = decltype(parity_tag)::value;  // j & 1, a compile-time slot index
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    // Loads for later iterations: K(j+2) into the K slot that held K(j)
+    // (consumed by S(j) one iteration ago), V(j+1) into the V slot that held
+    // V(j−1) (consumed by PV(j−1) one iteration ago).
+    if constexpr (HAS_NEXT) {
+      if (j + 2 < n_kv) gload(Kh, k_lds + PAR * TILE, j + 2);
+      gload(Vh, v_lds + (PAR ^ 1) * TILE, j + 1);
+    }
+    bf16x8 p[NS];
+    f32x16 ns[2];
+    softmax_exp<EXPM>(st, s, c_log2, p);
+    if constexpr (HAS_NEXT) {
+      scores(k_lds + (PAR ^ 1) * TILE, ns);
+#pragma unroll
+      for (int i = 0; i < 2 * KD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU | SG_TRANS, 6, 0);
       }
-      const bool need_mask = (key0 + kFwdBN > N) || (CAUSAL && key0 + kFwdBN - 1 > q0);
-      if (need_mask) {
+      // Keep the exponentials in this block (next to the S MFMAs) instead of
+      // letting them sink past the mask branch into the PV block.
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+      for (int ks = 0; ks < NS; ++ks) asm volatile("" ::"v"(p[ks]));
+      if (j + 1 >= first_masked) mask_tile<CAUSAL>(ns, (j + 1) * kFwdBN, N, qi, h);
+    }
+
+    // PV(j): Vᵀ operands by transpose reads.
+    const char* vt = v_lds + PAR * TILE;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + t * 32 + acc_row(r, h);
-            if (key >= N || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
-          }
+    for (int ks = 0; ks < NS; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x4 lo = lds_read_tr16(vt + 16 * ks * RB + voff[0][dt]);
+        const bf16x4 hi = lds_read_tr16(vt + 16 * ks * RB + voff[1][dt]);
+        st.o[dt] = mfma32(concat(lo, hi), p[ks], st.o[dt]);
       }
-      float mx = -INFINITY;
+    if constexpr (HAS_NEXT) {
+      const float mx = tile_max(ns);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = half_max(mx);
-      const float mx_c = mx * c_log2;
-      const bool resc = mx_c > m_c + kRescaleTau;
+      for (int i = 0; i < NS * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+      }
+      // Conditional rescale (FlashAttention-4 gist, technical summary 2.B).
+      const bool resc = mx > st.m_c + kRescaleTau;
       if (__ballot(resc)) {
-        const float m_new = resc ? mx_c : m_c;
-        const float alpha = resc ? exp2_hw(m_c - m_new) : 1.0f;
+        const float alpha = resc ? exp2_hw(st.m_c - mx) : 1.0f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        l_part *= alpha;
-        m_c = m_new;
+          for (int r = 0; r < 16; ++r) st.o[dt][r] *= alpha;
+        st.l_part *= alpha;
+        if (resc) st.m_c = mx;
       }
-      // P̃ = 2^(s·c − m_c) in bf16, kept in the Pᵀ operand layout.
-      bf16x8 p[NS];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          i32x4 packed;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e], c_log2, -m_c));
-            const float p1 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e + 1], c_log2, -m_c));
-            l_part += p0 + p1;
-            packed[e] = (int)pack_bf16x2(p0, p1);
-          }
-          p[2 * t + half] = __builtin_bit_cast(bf16x8, packed);
-        }
-      // Oᵀ += Vᵀ·Pᵀ. Slot e of step ks holds key 16ks + 8(e/4) + 4h + e%4.
-#pragma unroll
-      for (int ks = 0; ks < NS; ++ks) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int row = 16 * ks + tr_row;
-          const int chunk = 4 * dt + tr_chunk;
-          const bf16x4 lo = lds_read_tr16(vt + tile_off<D>(row, chunk) + tr_sub);
-          const bf16x4 hi = lds_read_tr16(vt + tile_off<D>(row + 8, chunk) + tr_sub);
-          oacc[dt] = mfma32(concat(lo, hi), p[ks], oacc[dt]);
-        }
-      }
+      s[0] = ns[0];
+      s[1] = ns[1];
+      wait_vmem();
+      __syncthreads();
     }
-    if (j + 1 < n_kv) lstore(stage ^ 1);
-    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int j = 0;
+  for (; j + 2 < n_kv; j += 2) {
+    iteration(j, I0{}, std::true_type{});
+    iteration(j + 1, I1{}, std::true_type{});
+  }
+  if (j + 1 < n_kv) {
+    iteration(j, I0{}, std::true_type{});
+    iteration(j + 1, I1{}, std::false_type{});
+  } else {
+    iteration(j, I0{}, std::false_type{});
   }
 
-  // Epilogue: O = Oᵀ/l (lane holds d = 32dt + 8(r/4) + 4h + r%4 of query qi).
-  const float l = half_sum(l_part);
+  // Epilogue: O = Oᵀ/l (lane holds d = 32dt + 8(r/4) + 4h + r%4 of its query).
+  const float l = half_sum(st.l_part);
   const float inv = 1.0f / l;
   if (qi < N) {
     bf16* Orow = O + head + (size_t)qi * D;
@@ -215,11 +327,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         i32x2 w;
-        w[0] = (int)pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv);
-        w[1] = (int)pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        w[0] = (int)pack_bf16x2(st.o[dt][4 * g] * inv, st.o[dt][4 * g + 1] * inv);
+        w[1] = (int)pack_bf16x2(st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv);
         *(i32x2*)(Orow + 32 * dt + 8 * g + 4 * h) = w;
       }
-    if (h == 0) LSE[(size_t)bh * N + qi] = (m_c + __builtin_log2f(l)) * kLn2;
+    if (h == 0) LSE[(size_t)bh * N + qi] = (st.m_c + __builtin_log2f(l)) * kLn2;
   }
 }
 

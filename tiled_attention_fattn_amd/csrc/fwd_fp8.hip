@@ -7,16 +7,15 @@
 // applied row by row with a fast Walsh–Hadamard transform in registers.
 //
 // Launches (one stream):
-//   1. fp8_init   — clear the per-head amax scratch.
-//   2. fp8_amax   — per (b,h) amax of |Q·R|, |K·R| and |V| (atomic max on the
-//                   float bits, all values non-negative).
-//   3. fp8_quant_qk — recompute Q·R, K·R; code = e4m3(t), t = x·448/amax
+//   1. fp8_amax   — amax of |Q·R|, |K·R| and |V| over each chunk of 256 rows
+//                   of each (b,h), one plain store per block (no atomics).
+//   2. fp8_quant_qk — recompute Q·R, K·R; code = e4m3(t), t = x·448/amax
 //                   (one correctly rounded division), round to nearest even;
 //                   for Q' also the residual code e4m3(16·(t − decode(code)));
 //                   write Q8, Q8lo, K8 and the scales.
-//   4. fp8_quant_v  — V codes written transposed ([d][keys]) in the key order
+//   3. fp8_quant_v  — V codes written transposed ([d][keys]) in the key order
 //                   the attention kernel's P operand uses.
-//   5. fwd_fp8    — attention: Sᵀ = K8·(Q8 + Q8lo/16)ᵀ (two MFMAs, the second
+//   4. fwd_fp8    — attention: Sᵀ = K8·(Q8 + Q8lo/16)ᵀ (two MFMAs, the second
 //                   with the block scale 2^-4) and Oᵀ += V8ᵀ·P8ᵀ on the
 //                   32x32x64 f8f6f4 MFMA; P̃ = 2^(s·c − m + 8) quantised to
 //                   e4m3 (P̃ ≤ 1 because the running max is updated whenever
@@ -82,41 +81,55 @@ __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, i
   return ok;
 }
 
-__global__ void fp8_init_kernel(uint32_t* amax, int n) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < n) amax[t] = 0u;
-}
-
-// grid (row blocks, BH, 3 tensors); 256 threads = (256/LPR) rows × LPR lanes.
+// grid (row chunks, BH, 3 tensors): block max of |x| over kFp8AmaxRows rows.
 template <int D>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ Q,
                                                       const bf16* __restrict__ K,
                                                       const bf16* __restrict__ V,
-                                                      uint32_t* __restrict__ amax, int N, int BH,
+                                                      float* __restrict__ partial, int N, int BH,
                                                       int rotate, uint64_t seed) {
   constexpr int LPR = D / 8, RPB = 256 / LPR;
   __shared__ float sgn[D];
-  const int t = blockIdx.z, bh = blockIdx.y;
+  __shared__ float wmax[4];
+  const int t = blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
   const bool rot = rotate && t < 2;
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
   __syncthreads();
   const bf16* src = (t == 0 ? Q : t == 1 ? K : V) + (size_t)bh * N * D;
-  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
-  float x[8];
-  load_row_part<D>(src, row, N, part, rot, sgn, x);
   float m = 0.0f;
+  for (int r0 = chunk * kFp8AmaxRows; r0 < min(N, (chunk + 1) * kFp8AmaxRows); r0 += RPB) {
+    float x[8];
+    load_row_part<D>(src, r0 + threadIdx.x / LPR, N, part, rot, sgn, x);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax + t * BH + bh, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int nchunks = gridDim.x;
+    partial[((size_t)t * BH + bh) * nchunks + chunk] =
+        fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  }
 }
 
-__device__ __forceinline__ float scale_from_amax(uint32_t bits) {
-  const float a = __uint_as_float(bits);
-  return a > 0.0f ? a / kE4m3Max : 1.0f;
+// amax of one (tensor, head) from its chunk partials, reduced by wave 0 and
+// broadcast through LDS. Every thread of the block must call it.
+__device__ __forceinline__ float head_amax(const float* partial, int nchunks, float* slot) {
+  if (threadIdx.x < 64) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < nchunks; i += 64) m = fmaxf(m, partial[i]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if (threadIdx.x == 0) *slot = m;
+  }
+  __syncthreads();
+  return *slot;
 }
+
+__device__ __forceinline__ float scale_from_amax(float a) { return a > 0.0f ? a / kE4m3Max : 1.0f; }
 
 // Four e4m3 codes (round to nearest even), a in the lowest byte.
 __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
@@ -142,50 +155,52 @@ __device__ __forceinline__ void dec_fp8x4(int w, float* out) {
 // so exact e4m3 midpoints stay exact.
 __device__ __forceinline__ float ratio448(float x, float am) { return __fdiv_rn(x * kE4m3Max, am); }
 
-// grid (row blocks, BH, 2 tensors)
+// grid (row chunks, BH, 2 tensors): kFp8AmaxRows rows per block.
 template <int D>
 __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restrict__ Q,
                                                           const bf16* __restrict__ K,
                                                           uint8_t* __restrict__ q8,
                                                           uint8_t* __restrict__ q8lo,
                                                           uint8_t* __restrict__ k8,
-                                                          const uint32_t* __restrict__ amax,
+                                                          const float* __restrict__ partial,
                                                           float* __restrict__ scales, int N, int BH,
                                                           int rotate, uint64_t seed) {
   constexpr int LPR = D / 8, RPB = 256 / LPR;
   __shared__ float sgn[D];
-  const int t = blockIdx.z, bh = blockIdx.y;
+  __shared__ float am_slot;
+  const int t = blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
-  __syncthreads();
+  const int nchunks = gridDim.x;
+  const float am = head_amax(partial + ((size_t)t * BH + bh) * nchunks, nchunks, &am_slot);
   const size_t head = (size_t)bh * N * D;
   const bf16* src = (t == 0 ? Q : K) + head;
   uint8_t* dst = (t == 0 ? q8 : k8) + head;
-  const uint32_t abits = amax[t * BH + bh];
-  const float am = __uint_as_float(abits);
-  if (blockIdx.x == 0 && threadIdx.x == 0) scales[t * BH + bh] = scale_from_amax(abits);
-  const int row = blockIdx.x * RPB + threadIdx.x / LPR;
+  if (chunk == 0 && threadIdx.x == 0) scales[t * BH + bh] = scale_from_amax(am);
   const int part = threadIdx.x % LPR;
-  float x[8];
-  if (!load_row_part<D>(src, row, N, part, rotate != 0, sgn, x)) return;
-  float tt[8];
+  for (int r0 = chunk * kFp8AmaxRows; r0 < min(N, (chunk + 1) * kFp8AmaxRows); r0 += RPB) {
+    const int row = r0 + threadIdx.x / LPR;
+    float x[8];
+    if (!load_row_part<D>(src, row, N, part, rotate != 0, sgn, x)) continue;
+    float tt[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) tt[e] = am > 0.0f ? clamp448(ratio448(x[e], am)) : x[e];
-  i32x2 w;
-  w[0] = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
-  w[1] = cvt_fp8x4(tt[4], tt[5], tt[6], tt[7]);
-  *(i32x2*)(dst + (size_t)row * D + part * 8) = w;
-  if (t == 0) {
-    // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
-    float dec[8];
-    dec_fp8x4(w[0], dec);
-    dec_fp8x4(w[1], dec + 4);
-    float r[8];
+    for (int e = 0; e < 8; ++e) tt[e] = am > 0.0f ? clamp448(ratio448(x[e], am)) : x[e];
+    i32x2 w;
+    w[0] = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
+    w[1] = cvt_fp8x4(tt[4], tt[5], tt[6], tt[7]);
+    *(i32x2*)(dst + (size_t)row * D + part * 8) = w;
+    if (t == 0) {
+      // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
+      float dec[8];
+      dec_fp8x4(w[0], dec);
+      dec_fp8x4(w[1], dec + 4);
+      float r[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = 16.0f * (tt[e] - dec[e]);
-    i32x2 wl;
-    wl[0] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
-    wl[1] = cvt_fp8x4(r[4], r[5], r[6], r[7]);
-    *(i32x2*)(q8lo + head + (size_t)row * D + part * 8) = wl;
+      for (int e = 0; e < 8; ++e) r[e] = 16.0f * (tt[e] - dec[e]);
+      i32x2 wl;
+      wl[0] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
+      wl[1] = cvt_fp8x4(r[4], r[5], r[6], r[7]);
+      *(i32x2*)(q8lo + head + (size_t)row * D + part * 8) = wl;
+    }
   }
 }
 
@@ -199,16 +214,16 @@ __device__ __forceinline__ int v8_pos(int r) {
 template <int D>
 __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict__ V,
                                                          uint8_t* __restrict__ v8t,
-                                                         const uint32_t* __restrict__ amax,
+                                                         const float* __restrict__ partial,
                                                          float* __restrict__ scales, int N,
-                                                         int Npad, int BH) {
+                                                         int Npad, int BH, int nchunks) {
   constexpr int CHUNKS = D / 8;
   constexpr int CPT = 64 * CHUNKS / 256;
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * 64];
   const int bh = blockIdx.y, kb = blockIdx.x;
-  const uint32_t abits = amax[2 * BH + bh];
-  const float am = __uint_as_float(abits);
-  if (kb == 0 && threadIdx.x == 0) scales[2 * BH + bh] = scale_from_amax(abits);
+  __shared__ float am_slot;
+  const float am = head_amax(partial + ((size_t)2 * BH + bh) * nchunks, nchunks, &am_slot);
+  if (kb == 0 && threadIdx.x == 0) scales[2 * BH + bh] = scale_from_amax(am);
   const bf16* src = V + (size_t)bh * N * D;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
@@ -301,7 +316,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   const int n_kv = (kv_end + kF8BN - 1) / kF8BN;
 
   i32x4 pk[KCPT], pv[VCPT];
-  auto gload = [&](int j) {
+  auto gload = [&](int j) __device__ {
     const int key0 = j * kF8BN;
 #pragma unroll
     for (int i = 0; i < KCPT; ++i) {
@@ -316,7 +331,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
       pv[i] = *(const i32x4*)(Vt + (size_t)d * Npad + key0 + part * 16);
     }
   };
-  auto lstore = [&](int stage) {
+  auto lstore = [&](int stage) __device__ {
     char* kb = lds + stage * (KB + VB);
     char* vb = kb + KB;
 #pragma unroll
@@ -441,20 +456,18 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
 template <int D, bool CAUSAL>
 static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
-                               uint32_t* amax, int BH, int N, float scale, bool rotate,
+                               float* partial, int BH, int N, float scale, bool rotate,
                                uint64_t seed, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 8);
   const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
-  hipLaunchKernelGGL(fp8_init_kernel, dim3((3 * BH + 255) / 256), dim3(256), 0, stream, amax,
-                     3 * BH);
-  const unsigned rblocks = (unsigned)((N + RPB - 1) / RPB);
-  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(rblocks, BH, 3), dim3(256), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, amax, N, BH, (int)rotate, seed);
-  hipLaunchKernelGGL((fp8_quant_qk_kernel<D>), dim3(rblocks, BH, 2), dim3(256), 0, stream,
-                     (const bf16*)q, (const bf16*)k, q8, q8lo, k8, (const uint32_t*)amax, scales, N, BH,
-                     (int)rotate, seed);
+  const unsigned nchunks = (unsigned)((N + kFp8AmaxRows - 1) / kFp8AmaxRows);
+  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(nchunks, BH, 3), dim3(256), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, partial, N, BH, (int)rotate,
+                     seed);
+  hipLaunchKernelGGL((fp8_quant_qk_kernel<D>), dim3(nchunks, BH, 2), dim3(256), 0, stream,
+                     (const bf16*)q, (const bf16*)k, q8, q8lo, k8, (const float*)partial, scales, N,
+                     BH, (int)rotate, seed);
   hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(Npad / 64, BH), dim3(256), 0, stream,
-                     (const bf16*)v, v8t, (const uint32_t*)amax, scales, N, Npad, BH);
+                     (const bf16*)v, v8t, (const float*)partial, scales, N, Npad, BH, (int)nchunks);
   const int n_qtiles = (N + kF8BM - 1) / kF8BM;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, stream,
                      (const uint8_t*)q8, (const uint8_t*)q8lo, (const uint8_t*)k8, (const uint8_t*)v8t,
@@ -464,15 +477,15 @@ static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                           uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
-                          uint32_t* amax, int B, int H, int N, int d, bool causal, float scale,
+                          float* partial, int B, int H, int N, int d, bool causal, float scale,
                           bool rotate, uint64_t seed, hipStream_t stream) {
   const int BH = B * H;
   if (d == 64) {
-    return causal ? launch_fp8_t<64, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream)
-                  : launch_fp8_t<64, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream);
+    return causal ? launch_fp8_t<64, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream)
+                  : launch_fp8_t<64, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream);
   }
-  return causal ? launch_fp8_t<128, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream)
-                : launch_fp8_t<128, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, amax, BH, N, scale, rotate, seed, stream);
+  return causal ? launch_fp8_t<128, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream)
+                : launch_fp8_t<128, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream);
 }
 
 }  // namespace fattn
