@@ -122,3 +122,34 @@ def test_fwd_exp_modes_agree():
     assert torch.equal(o_a, o_hw)
     diff = (o_hw.float() - o_p.float()).abs().max().item()
     assert diff < 1e-2, diff
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_offset_moves(causal):
+    # Inputs whose scores keep rising along the keys, so the exponent offset
+    # has to move inside the loop: head 0 has key rows whose norm grows 16x
+    # over the sequence; in head 1 every third query row is 3.0 and key 100
+    # (an inner tile) and key 690 (the last, ragged tile) are 3.0 and 3.5, so
+    # those queries meet score jumps far past 2^τ, the first one large
+    # enough (≈147 in log2 units) that 2^(s − m) overflows fp32 before the
+    # offset moves.
+    import tiled_attention_fattn_amd as fa
+    from tiled_attention_fattn_amd.inputs import bf16_round
+    B, H, N, d = 1, 2, 700, 128
+    inp = gen_workload(24, shape=(B, H, N, d))
+    q = inp["q"][0].copy()
+    k = inp["k"][0].copy()
+    k[:, 0] *= np.linspace(0.25, 4.0, N)[None, :, None]
+    q[:, 1, ::3] = 3.0
+    k[:, 1, 100] = 3.0
+    k[:, 1, 690] = 3.5
+    qv, qb = bf16_round(q)
+    kv, kb = bf16_round(k)
+    scale = d ** -0.5
+    print(f"[fwd] offset moves causal={causal}", flush=True)
+    o, lse = fa.fwd(to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(inp["v"][1]),
+                    causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref_o, ref_lse = attention_forward(qv, kv, inp["v"][0], causal, scale)
+    assert_bf16_close(to_np(o), ref_o, f"O offset moves causal={causal}")
+    assert_lse_close(to_np(lse), ref_lse, f"LSE offset moves causal={causal}")

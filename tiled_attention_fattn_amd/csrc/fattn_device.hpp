@@ -37,6 +37,31 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product in inline assembly with the register classes pinned:
+// mfma32_acc accumulates into AGPRs (B from VGPRs), mfma32_ab writes a VGPR
+// result from an A operand in VGPRs and a B operand in AGPRs (first k-step:
+// mfma32_ab0, zero accumulator). Keeping the long-lived accumulators and the
+// loop-invariant operand in AGPRs leaves the architectural VGPRs to the
+// values the VALU works on. The compiler does not see these as MFMAs, so it
+// inserts no wait states after them: callers put mfma_drain() between such a
+// product and the first VALU instruction that reads its result, unless many
+// other instructions separate the two.
+__device__ __forceinline__ void mfma32_acc(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_ab(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma32_ab0(f32x16& c, bf16x8 a, bf16x8 b) {
+  // Early clobber: the result must not share registers with the A operand.
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+// Wait states that cover the latency of a 32x32 MFMA result before a VALU
+// instruction reads it.
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
 // fp8 (e4m3fn for both operands) 32x32x64: A lane holds 32 k values of row c,
 // B lane holds 32 k values of column c; the k split between the lane halves
 // is the same for A and B, C as for mfma32.
@@ -94,37 +119,69 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// Buffer resource over `bytes` bytes from `base` (raw buffer, 32-bit data
-// format so that the range check applies): loads at byte offsets ≥ bytes
-// return zero.
-// (The buffer-resource type exists only in the device compilation; the host
-// pass sees empty bodies for these helpers, which it never runs.)
-#if defined(__HIP_DEVICE_COMPILE__)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+// Buffer descriptor in scalar registers for the inline-assembly loads below:
+// base address, stride 0, `bytes` records (loads at byte offsets ≥ bytes
+// return zero), raw 32-bit data format.
+__device__ __forceinline__ i32x4 make_rsrc_sgpr(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
 }
-#endif
 
 // Moves LOADS × 1 KB of a tile into LDS with buffer loads: wave load i takes
 // 16 bytes per lane from byte offset off[i] of the buffer [base, base + bytes)
 // (zero past the end) to LDS at dst + (first + i)·1 KB + lane·16.
+// The loads are issued by inline assembly, so the compiler does not track
+// them: it would otherwise make every later LDS read wait for all of them
+// (it cannot tell which LDS bytes they write). The caller orders them with
+// wait_vmem() and a workgroup barrier before the data is read, and before
+// the LDS range is written again.
 template <int LOADS>
 __device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, char* dst,
                                               const int (&off)[LOADS], int first) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(base, bytes);
+  const i32x4 rsrc = make_rsrc_sgpr(base, bytes);
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FATTN_LDS void*)(dst + (first + i) * 1024), 16,
-                                             off[i], 0, 0, 0);
+  for (int i = 0; i < LOADS; ++i) {
+    const int m0v = __builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)(uintptr_t)(FATTN_LDS char*)(dst + (first + i) * 1024));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0v), "v"(off[i]), "s"(rsrc)
+                 : "memory", "m0");
+  }
 #endif
 }
 
-// 64 floats from `src` into LDS at `dst` (one 4-byte element per lane).
+// One wave load of 16 bytes per lane from buffer byte offset voff (zero past
+// the buffer's end) to LDS at lds_dst + lane·16; untracked by the compiler
+// like buffer_to_lds. (The instruction's immediate offset would move the LDS
+// destination as well, so callers shift the buffer base instead.)
+__device__ __forceinline__ void dma16(const i32x4& rsrc, const char* lds_dst, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int m0v =
+      __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const FATTN_LDS char*)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+#endif
+}
+
+// 64 floats from `src` into LDS at `dst` (one 4-byte element per lane), by
+// the same untracked load as buffer_to_lds.
 __device__ __forceinline__ void stats_to_lds(const float* src, char* dst, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(src, 256);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FATTN_LDS void*)dst, 4, lane * 4, 0, 0, 0);
+  const i32x4 rsrc = make_rsrc_sgpr(src, 256);
+  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(FATTN_LDS char*)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(lane * 4), "s"(rsrc)
+               : "memory", "m0");
 #endif
 }
 

@@ -6,34 +6,34 @@
 // one head; K and V stream through LDS in 64-key tiles; the scores and the
 // probabilities never leave the compute unit.
 //
-// Layout inside a workgroup (4 waves of 64 lanes, one wave per SIMD, 64
-// queries per wave split in two 32-query sub-tiles A and B):
+// Layout inside a workgroup (4 waves of 64 lanes, 32 queries per wave, two
+// workgroups per compute unit so that each SIMD holds two waves whose VALU
+// and MFMA phases interleave):
 //  * Sᵀ = K·Qᵀ on 32x32x16 bf16 MFMA: the accumulator column is the query,
-//    so each lane owns one query row and the row max / row sum are in-lane
-//    reductions plus one exchange between the two lane halves. Each K operand
-//    read from LDS feeds the MFMAs of both sub-tiles.
+//    so each lane owns one query row and the row reductions are in-lane plus
+//    one exchange between the two lane halves. K comes from LDS, Q stays in
+//    registers for the whole loop.
 //  * Oᵀ += Vᵀ·Pᵀ on the same MFMA: Pᵀ is taken straight from the Sᵀ
 //    accumulator registers (the k order inside a 16-key step is free as long
 //    as the Vᵀ operand uses the same order); Vᵀ comes from the row-major V tile
-//    through the LDS transpose read, again shared by both sub-tiles.
-//  * The two sub-tiles are staggered so that the softmax (VALU and
-//    transcendental work) of one overlaps the MFMAs of the other:
-//      S_A | S_B ∥ softmax_A | PV_A ∥ softmax_B | PV_B
-//    (FlashAttention-4 news page, "Cómo Together AI resolvió el problema":
-//    overlap the tensor units, the exponential units and memory).
+//    through the LDS transpose read.
+//  * Software pipeline over 64-key tiles: the exponentials of tile j run
+//    beside the MFMAs of S(j+1), then PV(j) (FlashAttention-4 news page,
+//    "Cómo Together AI resolvió el problema": overlap the tensor units, the
+//    exponential units and memory).
 //  * Online softmax in the exp2 domain with conditional rescaling
-//    (FlashAttention-4 gist, technical summary 2.B): the running max used for
-//    the exponent moves only when a new tile max exceeds it by more than
-//    kRescaleTau, so most tiles skip the rescale of Oᵀ and l. Exact, because
-//    the same max is used for O, l and LSE.
-//  * Row sums are taken on the bf16 values that enter the PV product
-//    (v_dot2_f32_bf16 against (1, 1)), so numerator and denominator see the
-//    same probabilities.
-//  * K/V tiles are double-buffered: the next tile's global loads are issued
-//    before the current tile's math and written to the other LDS stage after it
-//    (FlashAttention-3 page, innovation 2: loads hidden behind compute).
-//  * Causal: key tiles past the workgroup's last query are never loaded, and a
-//    wave skips tiles that lie wholly above its diagonal.
+//    (FlashAttention-4 gist, technical summary 2.B): the exponent offset
+//    moves only when a tile's probabilities would exceed 2^τ, detected from
+//    the tile's row sum (see guard below), so the common tile needs neither
+//    a row max nor a rescale of Oᵀ and l. Exact, because the same offset is
+//    used for O, l and LSE.
+//  * Row sums are accumulated in fp32 from the probabilities before their
+//    rounding to bf16 for the PV product.
+//  * K/V tiles stream into LDS by buffer loads that write LDS directly,
+//    double-buffered and issued an iteration ahead (FlashAttention-3 page,
+//    innovation 2: loads hidden behind compute).
+//  * Causal: key tiles past the workgroup's last query are never loaded; the
+//    element mask is applied only on tiles that cross the diagonal.
 #include <type_traits>
 
 #include "fattn_device.hpp"
@@ -46,6 +46,7 @@ constexpr int kFwdQW = 32;                  // queries per wave
 constexpr int kFwdBM = kFwdQW * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBN = 64;                  // keys per K/V tile
 constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between rescales
+constexpr float kSumGuard = 256.0f;         // 2^kRescaleTau
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100, SG_TRANS = 0x400 };
@@ -70,37 +71,13 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int N, int q
     }
 }
 
-// Tile row max, conditional rescale of the sub-tile state (rare branch).
-template <int DT>
-__device__ __forceinline__ void softmax_update_max(SubTile<DT>& st, const f32x16 (&s)[2],
-                                                   float c_log2) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-  mx = half_max(mx);
-  const float mx_c = mx * c_log2;
-  const bool resc = mx_c > st.m_c + kRescaleTau;
-  if (__ballot(resc)) {
-    const float m_new = resc ? mx_c : st.m_c;
-    const float alpha = resc ? exp2_hw(st.m_c - m_new) : 1.0f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[dt][r] *= alpha;
-    st.l_part *= alpha;
-    st.m_c = m_new;
-  }
-}
-
-// P̃ = 2^(s·c − m_c) packed to bf16 in the Pᵀ operand layout (slot e of step
-// ks: key 16ks + 8(e/4) + 4h + e%4), and the row-sum update.
-template <int EXPM, int DT>
-__device__ __forceinline__ void softmax_exp(SubTile<DT>& st, const f32x16 (&s)[2], float c_log2,
-                                            bf16x8 (&p)[4]) {
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  float l = st.l_part;
+// P̃ = 2^(s·c − m_c) packed to bf16 in the Pᵀ operand layout (slot e of
+// step ks: key 16ks + 8(e/4) + 4h + e%4). Returns this lane half's fp32 sum
+// of P̃ (taken before the rounding to bf16, so the LSE keeps fp32 accuracy).
+template <int EXPM>
+__device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c_log2, float m_c,
+                                             bf16x8 (&p)[4]) {
+  float la = 0.0f, lb = 0.0f;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -108,15 +85,15 @@ __device__ __forceinline__ void softmax_exp(SubTile<DT>& st, const f32x16 (&s)[2
       i32x4 packed;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e], c_log2, -st.m_c));
-        const float p1 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e + 1], c_log2, -st.m_c));
-        const uint32_t w = pack_bf16x2(p0, p1);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, l, false);
-        packed[e] = (int)w;
+        const float p0 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e], c_log2, -m_c));
+        const float p1 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e + 1], c_log2, -m_c));
+        la += p0;
+        lb += p1;
+        packed[e] = (int)pack_bf16x2(p0, p1);
       }
       p[2 * t + half] = __builtin_bit_cast(bf16x8, packed);
     }
-  st.l_part = l;
+  return la + lb;
 }
 
 template <int D, bool CAUSAL, int EXPM>
@@ -236,9 +213,47 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   if (first_masked == 0) mask_tile<CAUSAL>(s, 0, N, qi, h);
   st.m_c = tile_max(s);
 
-  // Iteration j: exp(S(j)) ∥ S(j+1) on the MFMA pipe, then max(S(j+1)) ∥
-  // PV(j), then the (rare) conditional rescale for tile j+1. The last
-  // iteration (no tile j+1) is peeled so that each of the two phases is one
+  // Conditional rescale (FlashAttention-4 gist, technical summary 2.B). The
+  // offset m_c stays put while every P̃ of a tile is at most 2^τ. A lane
+  // half's tile sum bounds each of its P̃, so the test needs neither the row
+  // max nor the scores once the exponentials are taken: only when some sum
+  // exceeds 2^τ (rare once m_c is near the row max) does the wave take the
+  // exact branch. That branch rebuilds S(j) bit for bit (same operands, same
+  // accumulation order; K(j) is re-read from global memory because its LDS
+  // slot already receives K(j+2)), moves m_c to the row max, rescales Oᵀ and
+  // l and recomputes P̃(j).
+  auto guard = [&](int j, bf16x8 (&p)[NS], float& lt) __device__ {
+    if (__ballot(lt > kSumGuard)) {
+      const int key0 = j * kFwdBN;
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int key = key0 + t * 32 + c;
+        const bf16* krow = Kh + (size_t)min(key, N - 1) * D + 8 * h;
+        s[t] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          bf16x8 a = *(const bf16x8*)(krow + kk * 16);
+          if (key >= N) a = bf16x8{};
+          s[t] = mfma32(a, qr[kk], s[t]);
+        }
+      }
+      if (j >= first_masked) mask_tile<CAUSAL>(s, key0, N, qi, h);
+      const float m_new = fmaxf(st.m_c, tile_max(s));
+      const float alpha = exp2_hw(st.m_c - m_new);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[dt][r] *= alpha;
+      st.l_part *= alpha;
+      st.m_c = m_new;
+      lt = softmax_exp<EXPM>(s, c_log2, st.m_c, p);
+    }
+    st.l_part += lt;
+  };
+
+  // Iteration j: exp(S(j)) ∥ S(j+1) on the MFMA pipe, the guard, then PV(j).
+  // The last iteration (no tile j+1) is peeled so that each phase is one
   // basic block the scheduler can interleave.
   auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
     constexpr int PAR = decltype(parity_tag)::value;  // j & 1, a compile-time slot index
@@ -252,21 +267,22 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     bf16x8 p[NS];
     f32x16 ns[2];
-    softmax_exp<EXPM>(st, s, c_log2, p);
+    float lt = softmax_exp<EXPM>(s, c_log2, st.m_c, p);
     if constexpr (HAS_NEXT) {
       scores(k_lds + (PAR ^ 1) * TILE, ns);
 #pragma unroll
       for (int i = 0; i < 2 * KD; ++i) {
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU | SG_TRANS, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU | SG_TRANS, 4, 0);
       }
       // Keep the exponentials in this block (next to the S MFMAs) instead of
-      // letting them sink past the mask branch into the PV block.
+      // letting them sink past the branches into the PV block.
 #pragma unroll
       for (int ks = 0; ks < NS; ++ks) asm volatile("" ::"v"(p[ks]));
       if (j + 1 >= first_masked) mask_tile<CAUSAL>(ns, (j + 1) * kFwdBN, N, qi, h);
     }
+    guard(j, p, lt);
 
     // PV(j): Vᵀ operands by transpose reads.
     const char* vt = v_lds + PAR * TILE;
@@ -279,23 +295,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         st.o[dt] = mfma32(concat(lo, hi), p[ks], st.o[dt]);
       }
     if constexpr (HAS_NEXT) {
-      const float mx = tile_max(ns);
 #pragma unroll
       for (int i = 0; i < NS * DT; ++i) {
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
-      }
-      // Conditional rescale (FlashAttention-4 gist, technical summary 2.B).
-      const bool resc = mx > st.m_c + kRescaleTau;
-      if (__ballot(resc)) {
-        const float alpha = resc ? exp2_hw(st.m_c - mx) : 1.0f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) st.o[dt][r] *= alpha;
-        st.l_part *= alpha;
-        if (resc) st.m_c = mx;
       }
       s[0] = ns[0];
       s[1] = ns[1];
