@@ -86,13 +86,12 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o,
  *   dq, dk, dv  [B,H,N,d] bf16 outputs.
  *   workspace   device memory of at least fattn_bwd_workspace_bytes(B,H,N,d)
  *               bytes, 256-byte aligned; contents on entry are ignored.
- *               Layout (Npad = N rounded up to 64): fp32 dQ accumulator
- *               [B,H,Npad,d] at offset 0, then fp32 D = rowsum(dO∘O)
- *               [B,H,Npad], then fp32 LSE·log2(e) [B,H,Npad] (padded rows:
- *               D = 0, +∞), each piece 256-byte aligned.
- * dK and dV are accumulated without atomics (each key block is owned by one
- * workgroup); dQ is reduced with fp32 global atomics, so dq is reproducible
- * only up to the order of floating-point additions.
+ *               Layout (Npad = N rounded up to 64): fp32 D = rowsum(dO∘O)
+ *               [B,H,Npad] at offset 0, then fp32 LSE·log2(e) [B,H,Npad]
+ *               (padded rows: D = 0, +∞), each piece 256-byte aligned.
+ * dK and dV are accumulated by the workgroup that owns their key block and dQ
+ * by the workgroup that owns its query block (which recomputes the scores):
+ * no global atomics, so all three gradients are bitwise reproducible.
  */
 size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d);
 fattn_status fattn_bwd(const void* q, const void* k, const void* v,

@@ -1,40 +1,36 @@
 // Fused attention backward, bf16 in/out, fp32 accumulation, for gfx950.
 //
 // Gradient of ⟨O, dO⟩ for O = softmax(scale·Q·Kᵀ [causal])·V, recomputing P
-// from the forward's log-sum-exp (the pages name the dS and dQ terms and the
-// global atomic reduction: FlashAttention-4 gist, technical summary 2.C):
-//   D  = rowsum(dO ∘ O), lse2 = LSE·log2(e)    (kernel 1, also zeroes dQ_acc)
-//   P  = exp(scale·Q·Kᵀ − LSE),  dV = Pᵀ·dO,  dP = dO·Vᵀ,
-//   dS = P ∘ (dP − D),  dK = scale·dSᵀ·Q,  dQ += dS·K   (kernel 2)
-//   dQ = scale·dQ_acc → bf16                      (kernel 3)
+// from the forward's log-sum-exp (the pages name the dS and dQ terms:
+// FlashAttention-4 gist, technical summary 2.C):
+//   D  = rowsum(dO ∘ O), lse2 = LSE·log2(e)            (kernel 1)
+//   P  = exp(scale·Q·Kᵀ − LSE),  dP = dO·Vᵀ,  dS = P ∘ (dP − D)
+//   dV = Pᵀ·dO,  dK = scale·dSᵀ·Q                       (kernel 2, per key block)
+//   dQ = scale·dS·K                                      (kernel 3, per query block)
 //
-// The statistics and the dQ accumulator are padded to Npad = N rounded up to
-// 64 rows per head; padded rows carry lse2 = +∞ and D = 0, so their P (and
-// therefore every contribution they make) is exactly 0 without any mask.
-// Keys past N are loaded as zero rows of K and V, which makes their scores 0
-// and their dQ contribution 0 (dS·K with K = 0); their dK, dV are not stored.
+// The statistics are padded to Npad = N rounded up to 64 rows per head;
+// padded rows carry lse2 = +∞ and D = 0, so their P (and every contribution
+// they make) is exactly 0 without any mask.
 //
-// Kernel 2 is key-stationary: a workgroup owns 128 keys (32 per wave, one
-// wave per SIMD) of one head and walks the 64-query tiles, so dK and dV
-// accumulate in registers of the owning wave with no atomics. dQ needs a sum
-// over keys: each wave writes its dS block to LDS as dSᵀ, and after a barrier
-// the workgroup multiplies the whole 64×128 dS by the 128-key K tile, so each
-// dQ element gets one fp32 atomic add per workgroup and query tile (not one
-// per wave).
+// dQ is a sum over keys and dK, dV are sums over queries. Kernel 2 owns a
+// block of keys and walks the query tiles, so dK and dV accumulate in
+// registers; kernel 3 owns a block of queries and walks the key tiles (it
+// recomputes S and dP, two extra products), so dQ accumulates in registers
+// too. Nothing is reduced through global atomics: on gfx950 the fp32 atomic
+// traffic of a fused kernel (one add per dQ element per key block and query
+// tile) costs more time in the L2 than the recomputation, and without it the
+// gradients are bitwise reproducible.
 //
 // Operand orientation (32x32x16 bf16 MFMA, accumulator column = lane%32):
-//   S, dP   : A = Q / dO rows from LDS, B = K / V rows held in registers,
-//             so the accumulator column is the key and each lane owns one key.
+//  kernel 2 (column = key):
+//   S, dP   : A = Q / dO rows from LDS, B = K / V rows held in registers.
 //   dVᵀ, dKᵀ: A = dOᵀ / Qᵀ by the LDS transpose read, B = P / dS straight from
-//             the S / dP accumulator registers (same k-slot trick as the
-//             forward's P·V).
-//   dQ      : A = dS by the transpose read of the dSᵀ tile, B = K by the
-//             transpose read of the K tile; accumulator column = d, so the
-//             atomics of one row are coalesced.
-// The query tiles stream through LDS by buffer loads straight into LDS (no
-// staging registers), double-buffered; the per-iteration work is split by
-// 32-query halves so the exponentials of one half overlap the MFMAs of the
-// other.
+//             the S / dP accumulator registers (the forward's P·V trick).
+//  kernel 3 (column = query):
+//   Sᵀ, dPᵀ : A = K / V rows from LDS, B = Q / dO rows held in registers.
+//   dQᵀ     : A = Kᵀ by the LDS transpose read, B = dSᵀ from the accumulators.
+// Tiles stream through LDS by buffer loads straight into LDS (no staging
+// registers), double-buffered.
 #include <type_traits>
 
 #include "fattn_device.hpp"
@@ -51,15 +47,14 @@ enum : int { BG_VALU = 0x002, BG_MFMA = 0x008, BG_DS_READ = 0x100, BG_DS_WRITE =
 
 // ---------------------------------------------------------------------------
 // Kernel 1: D_i = Σ_c dO_ic·O_ic, lse2_i = LSE_i·log2(e) (padded rows: D = 0,
-// lse2 = +∞), dQ_acc = 0. One 16-byte chunk of a (padded) row per thread.
+// lse2 = +∞). One 16-byte chunk of a (padded) row per thread.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O,
                                                      const bf16* __restrict__ dO,
                                                      const float* __restrict__ LSE,
                                                      float* __restrict__ dvec,
-                                                     float* __restrict__ lse2,
-                                                     float* __restrict__ dq_acc, int N, int Npad,
+                                                     float* __restrict__ lse2, int N, int Npad,
                                                      long rows_pad) {
   constexpr int LPR = D / 8;  // lanes per row
   const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -76,11 +71,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
   }
-  if (prow < rows_pad) {
-    const f32x4 z = {};
-    *(f32x4*)(dq_acc + prow * D + part * 8) = z;
-    *(f32x4*)(dq_acc + prow * D + part * 8 + 4) = z;
-  }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
   if (prow < rows_pad && part == 0) {
@@ -90,61 +80,23 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: dQ = bf16(scale · dQ_acc) for the N real rows of each head.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ dq_acc,
-                                                    bf16* __restrict__ dq, long n8, int N,
-                                                    int Npad, float scale) {
-  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n8) return;
-  const long row = t / (D / 8);       // bh·N + n
-  const int part = (int)(t % (D / 8));
-  const long bh = row / N;
-  const long prow = bh * Npad + (row - bh * N);
-  const f32x4 a = *(const f32x4*)(dq_acc + prow * D + part * 8);
-  const f32x4 b = *(const f32x4*)(dq_acc + prow * D + part * 8 + 4);
-  i32x4 w;
-  w[0] = (int)pack_bf16x2(a[0] * scale, a[1] * scale);
-  w[1] = (int)pack_bf16x2(a[2] * scale, a[3] * scale);
-  w[2] = (int)pack_bf16x2(b[0] * scale, b[1] * scale);
-  w[3] = (int)pack_bf16x2(b[2] * scale, b[3] * scale);
-  *(i32x4*)(dq + row * D + part * 8) = w;
-}
-
-// s_waitcnt vmcnt(n) (expcnt, lgkmcnt not waited), n < 64.
-template <int n>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 2: key-stationary main loop.
+// Kernel 2: dK, dV, key-stationary.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_main_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ lse2, const float* __restrict__ dvec,
-                     float* __restrict__ dq_acc, bf16* __restrict__ dK, bf16* __restrict__ dV,
+                     bf16* __restrict__ dK, bf16* __restrict__ dV,
                      int N, int Npad, int BH, int n_kvtiles, float c_log2, float scale) {
-  constexpr int KD = D / 16, CHUNKS = D / 8, DT = D / 32;
-  constexpr int RB = D * 2;                         // bytes per Q / dO / K row
+  constexpr int KD = D / 16, DT = D / 32;
+  constexpr int RB = D * 2;                         // bytes per Q / dO row
   constexpr int QT_BYTES = kBwdBM * RB;             // one Q or dO tile
-  constexpr int K_BYTES = kBwdBN * RB;              // the workgroup's K tile
-  constexpr int DS_RB = kBwdBM * 2;                 // bytes per dSᵀ row (128)
-  constexpr int DS_BYTES = kBwdBN * DS_RB;          // dSᵀ [keys][queries]
-  constexpr int KCPT = kBwdBN * CHUNKS / 256;
-  constexpr int DQ_DT = 2 * DT / kBwdWaves;         // dQ d-tiles per wave (qt fixed per wave)
   constexpr int LD_LOADS = QT_BYTES / 1024 / kBwdWaves;  // 1 KB wave loads per tile per wave
-  // LDS: K | Q0 | dO0 | Q1 | dO1 | dSᵀ | stats[2 stages][lse2 64 | D 64]
-  __shared__ __attribute__((aligned(16))) char lds[K_BYTES + 4 * QT_BYTES + DS_BYTES +
-                                                   4 * kBwdBM * 4];
-  char* const k_lds = lds;
-  char* const q_lds = lds + K_BYTES;               // stage s: Q at s·2·QT, dO at s·2·QT + QT
-  char* const ds_lds = lds + K_BYTES + 4 * QT_BYTES;
-  char* const st_lds = ds_lds + DS_BYTES;          // stage s: lse2 at s·512, D at s·512 + 256
+  // LDS: Q0 | dO0 | Q1 | dO1 | stats[2 stages][lse2 64 | D 64]
+  __shared__ __attribute__((aligned(16))) char lds[4 * QT_BYTES + 4 * kBwdBM * 4];
+  char* const q_lds = lds;                         // stage s: Q at s·2·QT, dO at s·2·QT + QT
+  char* const st_lds = lds + 4 * QT_BYTES;         // stage s: lse2 at s·512, D at s·512 + 256
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -166,22 +118,12 @@ void bwd_main_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* dOh = dO + head;
   const float* lse_h = lse2 + (size_t)bh * Npad;
   const float* d_h = dvec + (size_t)bh * Npad;
-  float* dqh = dq_acc + (size_t)bh * Npad * D;
 
   const int kv0 = jt * kBwdBN;
   const int kw0 = kv0 + 32 * wave;  // this wave's first key
   const int key = kw0 + c;          // this lane's key (accumulator column)
 
-  // K tile → LDS (for the dQ product, zero rows past N), K and V rows of this
-  // lane → registers (zero past N).
-#pragma unroll
-  for (int i = 0; i < KCPT; ++i) {
-    const int ch = tid + i * 256;
-    const int r = ch / CHUNKS, cc = ch % CHUNKS;
-    i32x4 x = {};
-    if (kv0 + r < N) x = *(const i32x4*)(Kh + (size_t)(kv0 + r) * D + cc * 8);
-    *(i32x4*)(k_lds + tile_off<D>(r, cc)) = x;
-  }
+  // K and V rows of this lane → registers (zero past N).
   bf16x8 kreg[KD], vreg[KD];
 #pragma unroll
   for (int kk = 0; kk < KD; ++kk) {
@@ -201,28 +143,6 @@ void bwd_main_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) toff[hf][dt] = tile_off<D>(tr_row + 8 * hf, 4 * dt + tr_chunk) + tr_sub;
-  // dQ tiles of this wave: query half qtw, d-tiles dtw0 .. dtw0 + DQ_DT − 1.
-  const int qtw = wave & 1;
-  const int dtw0 = (wave >> 1) * DQ_DT;
-  int soff[2];  // dSᵀ transpose reads: rows 16ks + tr_row (+8), chunk 4qtw + tr_chunk
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) soff[hf] = tile_off_rb<DS_RB>(tr_row + 8 * hf, 4 * qtw + tr_chunk) + tr_sub;
-  int woff[4][2];  // dSᵀ writes: row 32w + c, queries 16ks + 8hf + 4h .. +3
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int qa = 16 * ks + 8 * hf + 4 * h;
-      woff[ks][hf] = tile_off_rb<DS_RB>(32 * wave + c, qa >> 3) + (qa & 7) * 2;
-    }
-
-  int kToff[DQ_DT][2];  // Kᵀ transpose reads for the dQ d-tiles: rows 16ks + tr_row (+8)
-#pragma unroll
-  for (int i = 0; i < DQ_DT; ++i)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      kToff[i][hf] = tile_off<D>(tr_row + 8 * hf, 4 * (dtw0 + i) + tr_chunk) + tr_sub;
-
   const int n_qt = (N + kBwdBM - 1) / kBwdBM;
   const int i0 = CAUSAL ? kv0 / kBwdBM : 0;
   // Query tiles that straddle this key block's diagonal need the causal mask.
@@ -336,18 +256,7 @@ void bwd_main_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         __builtin_amdgcn_sched_group_barrier(BG_VALU | BG_TRANS | BG_DS_READ, 3, 0);
       }
     }
-    // dSᵀ → LDS (row = key, 4 queries per 8-byte write) and the half-1 steps.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const i32x4 w4 = __builtin_bit_cast(i32x4, dsb[ks]);
-      i32x2 lo, hi;
-      lo[0] = w4[0];
-      lo[1] = w4[1];
-      hi[0] = w4[2];
-      hi[1] = w4[3];
-      *(i32x2*)(ds_lds + woff[ks][0]) = lo;
-      *(i32x2*)(ds_lds + woff[ks][1]) = hi;
-    }
+    // The half-1 steps.
 #pragma unroll
     for (int ks = 2; ks < 4; ++ks)
 #pragma unroll
@@ -359,33 +268,9 @@ void bwd_main_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         const bf16x4 q1 = lds_read_tr16(qb + 16 * ks * RB + toff[1][dt]);
         dk_acc[dt] = mfma32(concat(q0, q1), dsb[ks], dk_acc[dt]);
       }
-    __syncthreads();  // dSᵀ complete
-
-    // dQ[qtw half × this wave's d-tiles] += dS·K over the 128 keys.
-    f32x16 dq[DQ_DT];
-#pragma unroll
-    for (int i = 0; i < DQ_DT; ++i) dq[i] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < kBwdBN / 16; ++ks) {
-      const bf16x4 a0 = lds_read_tr16(ds_lds + 16 * ks * DS_RB + soff[0]);
-      const bf16x4 a1 = lds_read_tr16(ds_lds + 16 * ks * DS_RB + soff[1]);
-      const bf16x8 a = concat(a0, a1);
-#pragma unroll
-      for (int i = 0; i < DQ_DT; ++i) {
-        const bf16x4 b0 = lds_read_tr16(k_lds + 16 * ks * RB + kToff[i][0]);
-        const bf16x4 b1 = lds_read_tr16(k_lds + 16 * ks * RB + kToff[i][1]);
-        dq[i] = mfma32(a, concat(b0, b1), dq[i]);
-      }
-    }
-    float* dqrow = dqh + (size_t)(qs + 32 * qtw + 4 * h) * D + 32 * dtw0 + c;
-#pragma unroll
-    for (int i = 0; i < DQ_DT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        unsafeAtomicAdd(dqrow + (8 * (r >> 2) + (r & 3)) * D + 32 * i, dq[i][r]);
-    // The next tile's loads were issued before this tile's atomics; wait only
-    // for them (vmcnt counts in issue order), then release both stages.
-    wait_vmem_le<16 * DQ_DT>();
+    // Both stages are free once every wave is done with this tile and the
+    // next tile's loads have landed.
+    wait_vmem();
     __syncthreads();
   };
 
@@ -429,51 +314,224 @@ void bwd_main_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel 3: dQ, query-stationary. A workgroup owns 128 queries of one head
+// (32 per wave, one per lane column) and walks the 64-key tiles up to its
+// diagonal: Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ with Q, dO in registers, then
+// dS = P ∘ (dP − D) packed as the B operand of dQᵀ += Kᵀ·dSᵀ.
+// ---------------------------------------------------------------------------
+constexpr int kDqWaves = 4;
+constexpr int kDqBM = 32 * kDqWaves;  // queries per workgroup
+constexpr int kDqBN = 64;             // keys per tile
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                   const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                   const float* __restrict__ lse2, const float* __restrict__ dvec,
+                   bf16* __restrict__ dQ, int N, int Npad, int BH, int n_qtiles, float c_log2,
+                   float scale) {
+  constexpr int KD = D / 16, RB = D * 2, TILE = kDqBN * RB, DT = D / 32;
+  constexpr int LOADS = TILE / 1024 / kDqWaves;  // 1 KB wave loads per tensor per tile
+  // LDS: K slots 0, 1 then V slots 0, 1, row-major with the 64-bank swizzle.
+  __shared__ __attribute__((aligned(16))) char lds[4 * TILE];
+  char* const k_lds = lds;
+  char* const v_lds = lds + 2 * TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, c = lane & 31;
+
+  // Workgroup → (head, query tile), XCD-aware; causal: heaviest tiles first.
+  const int total = n_qtiles * BH;
+  int logical = blockIdx.x;
+  if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int bh = logical / n_qtiles;
+  int qt = logical - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;
+
+  const size_t head = (size_t)bh * N * D;
+  const bf16* Qh = Q + head;
+  const bf16* Kh = K + head;
+  const bf16* Vh = V + head;
+  const bf16* dOh = dO + head;
+  const int q_start = qt * kDqBM;
+  const int qi = q_start + 32 * wave + c;  // this lane's query
+  const bool qv = qi < N;
+  const float l2 = qv ? lse2[(size_t)bh * Npad + qi] : INFINITY;
+  const float dq_d = qv ? dvec[(size_t)bh * Npad + qi] : 0.0f;
+
+  // Qᵀ and dOᵀ operands: lane holds row qi, elements 16kk + 8h + 0..7.
+  bf16x8 qr[KD], dor[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) {
+    qr[kk] = qv ? *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
+    dor[kk] = qv ? *(const bf16x8*)(dOh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
+  }
+
+  // Per-lane LDS offsets: K / V rows (A operands of Sᵀ, dPᵀ) and the Kᵀ
+  // transpose reads (A operand of dQᵀ).
+  int koff[KD];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk) koff[kk] = tile_off<D>(c, 2 * kk + h);
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_sub = (lane & 1) * 8;
+  int toff[2][DT];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) toff[hf][dt] = tile_off<D>(tr_row + 8 * hf, 4 * dt + tr_chunk) + tr_sub;
+
+  const int kv_end = CAUSAL ? min(N, q_start + kDqBM) : N;
+  const int n_kv = (kv_end + kDqBN - 1) / kDqBN;
+  const int first_masked = CAUSAL ? min(q_start / kDqBN, N / kDqBN) : N / kDqBN;
+
+  int ld_off[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = (wave * LOADS + i) * (1024 / RB) + lane / (RB / 16);
+    ld_off[i] = r * RB + swz_chunk_rb<RB>(r, lane % (RB / 16)) * 16;
+  }
+  auto gload = [&](int j, int slot) __device__ {
+    const int key0 = j * kDqBN;
+    buffer_to_lds<LOADS>(Kh + (size_t)key0 * D, (N - key0) * RB, k_lds + slot * TILE, ld_off,
+                         wave * LOADS);
+    buffer_to_lds<LOADS>(Vh + (size_t)key0 * D, (N - key0) * RB, v_lds + slot * TILE, ld_off,
+                         wave * LOADS);
+  };
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
+
+  auto iteration = [&](int j, auto parity_tag, auto masked_tag) __device__ {
+    constexpr int PAR = decltype(parity_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if (j + 1 < n_kv) gload(j + 1, PAR ^ 1);
+    const char* kt = k_lds + PAR * TILE;
+    const char* vt = v_lds + PAR * TILE;
+    const int key0 = j * kDqBN;
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x16 sv = {}, dpv = {};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        sv = mfma32(*(const bf16x8*)(kt + t * 32 * RB + koff[kk]), qr[kk], sv);
+        dpv = mfma32(*(const bf16x8*)(vt + t * 32 * RB + koff[kk]), dor[kk], dpv);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        i32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float ds[2];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int r = half * 8 + 2 * e + b;
+            float p = exp2_hw(fmaf(sv[r], c_log2, -l2));
+            if (MASKED) {
+              const int key = key0 + t * 32 + acc_row(r, h);
+              if (key >= N || (CAUSAL && key > qi)) p = 0.0f;
+            }
+            ds[b] = p * (dpv[r] - dq_d);
+          }
+          w[e] = (int)pack_bf16x2(ds[0], ds[1]);
+        }
+        dsb[2 * t + half] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    // dQᵀ += Kᵀ·dSᵀ: Kᵀ operands by transpose reads of the K tile.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x4 lo = lds_read_tr16(kt + 16 * ks * RB + toff[0][dt]);
+        const bf16x4 hi = lds_read_tr16(kt + 16 * ks * RB + toff[1][dt]);
+        dq[dt] = mfma32(concat(lo, hi), dsb[ks], dq[dt]);
+      }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  gload(0, 0);
+  wait_vmem();
+  __syncthreads();
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int j = 0;
+  for (; j + 1 < first_masked; j += 2) {
+    iteration(j, I0{}, std::false_type{});
+    iteration(j + 1, I1{}, std::false_type{});
+  }
+  for (; j < n_kv; ++j) {
+    if (j & 1) iteration(j, I1{}, std::integral_constant<bool, true>{});
+    else iteration(j, I0{}, std::integral_constant<bool, true>{});
+  }
+
+  // Epilogue: dQ = scale·dQᵀ (lane holds d = 32dt + 8(r/4) + 4h + r%4).
+  if (qv) {
+    bf16* row = dQ + head + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        i32x2 w;
+        w[0] = (int)pack_bf16x2(dq[dt][4 * g] * scale, dq[dt][4 * g + 1] * scale);
+        w[1] = (int)pack_bf16x2(dq[dt][4 * g + 2] * scale, dq[dt][4 * g + 3] * scale);
+        *(i32x2*)(row + 32 * dt + 8 * g + 4 * h) = w;
+      }
+  }
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                               float* dq_acc, float* dvec, float* lse2, int BH, int N,
-                               float scale, hipStream_t stream) {
-  const int Npad = (N + kBwdBM - 1) / kBwdBM * kBwdBM;
+                               float* dvec, float* lse2, int BH, int N, float scale,
+                               hipStream_t stream) {
+  const int Npad = (N + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad;
   const long rows_pad = (long)BH * Npad;
   {
     const long threads = rows_pad * (D / 8);
     const dim3 grid((unsigned)((threads + 255) / 256));
     hipLaunchKernelGGL((bwd_pre_kernel<D>), grid, dim3(256), 0, stream, (const bf16*)o,
-                       (const bf16*)dout, lse, dvec, lse2, dq_acc, N, Npad, rows_pad);
+                       (const bf16*)dout, lse, dvec, lse2, N, Npad, rows_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     const int n_kvtiles = (N + kBwdBN - 1) / kBwdBN;
     const dim3 grid(n_kvtiles * BH);
-    hipLaunchKernelGGL((bwd_main_kernel<D, CAUSAL>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                       (const float*)lse2, (const float*)dvec, dq_acc, (bf16*)dk, (bf16*)dv, N,
+                       (const float*)lse2, (const float*)dvec, (bf16*)dk, (bf16*)dv, N,
                        Npad, BH, n_kvtiles, scale * kLog2e, scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    const long n8 = (long)BH * N * D / 8;
-    const dim3 grid((unsigned)((n8 + 255) / 256));
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), grid, dim3(256), 0, stream, (const float*)dq_acc,
-                       (bf16*)dq, n8, N, Npad, scale);
+    const int n_qtiles = (N + kDqBM - 1) / kDqBM;
+    const dim3 grid(n_qtiles * BH);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                       (const float*)lse2, (const float*)dvec, (bf16*)dq, N, Npad, BH, n_qtiles,
+                       scale * kLog2e, scale);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* dq_acc, float* dvec, float* lse2, int B, int H, int N, int d,
-                           bool causal, float scale, hipStream_t stream) {
+                           float* dvec, float* lse2, int B, int H, int N, int d, bool causal,
+                           float scale, hipStream_t stream) {
   const int BH = B * H;
   if (d == 64) {
-    return causal ? launch_bwd_t<64, true>(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, lse2, BH, N, scale, stream)
-                  : launch_bwd_t<64, false>(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, lse2, BH, N, scale, stream);
+    return causal ? launch_bwd_t<64, true>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream)
+                  : launch_bwd_t<64, false>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream);
   }
-  return causal ? launch_bwd_t<128, true>(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, lse2, BH, N, scale, stream)
-                : launch_bwd_t<128, false>(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, lse2, BH, N, scale, stream);
+  return causal ? launch_bwd_t<128, true>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream)
+                : launch_bwd_t<128, false>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream);
 }
 
 }  // namespace fattn

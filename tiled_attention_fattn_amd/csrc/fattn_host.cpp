@@ -125,7 +125,7 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o, flo
 size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
-  return round_up(n * d * sizeof(float), 256) + 2 * round_up(n * sizeof(float), 256);
+  return 2 * round_up(n * sizeof(float), 256);
 }
 
 fattn_status fattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -149,11 +149,10 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v, const void* 
     return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, need);
   FATTN_TRY(check_device());
   const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
-  float* dq_acc = (float*)workspace;
-  float* dvec = (float*)((char*)workspace + round_up(n * d * sizeof(float), 256));
+  float* dvec = (float*)workspace;
   float* lse2 = (float*)((char*)dvec + round_up(n * sizeof(float), 256));
-  return hip_status(fattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dq_acc, dvec, lse2, B,
-                                           H, N, d, causal != 0, scale, (hipStream_t)stream),
+  return hip_status(fattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B, H, N,
+                                           d, causal != 0, scale, (hipStream_t)stream),
                     "fattn_bwd launch");
 }
 

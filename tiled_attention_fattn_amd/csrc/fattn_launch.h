@@ -11,12 +11,12 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int N, int d, bool causal, float scale, int exp_mode,
                            hipStream_t stream);
 
-// Backward: `dq_acc` fp32 [B,H,Npad,d], `dvec` and `lse2` fp32 [B,H,Npad] live
-// in the caller's workspace (Npad = N rounded up to kBwdRowPad).
+// Backward: `dvec` and `lse2` fp32 [B,H,Npad] live in the caller's workspace
+// (Npad = N rounded up to kBwdRowPad).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                           float* dq_acc, float* dvec, float* lse2, int B, int H, int N, int d,
-                           bool causal, float scale, hipStream_t stream);
+                           float* dvec, float* lse2, int B, int H, int N, int d, bool causal,
+                           float scale, hipStream_t stream);
 
 constexpr int kBwdRowPad = 64;
 
