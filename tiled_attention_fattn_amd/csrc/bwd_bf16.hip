@@ -41,6 +41,7 @@ namespace fattn {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdBN = 32 * kBwdWaves;  // keys per workgroup
 constexpr int kBwdBM = 64;              // queries per inner step
+constexpr int kLeadB = 3;               // LDS operand reads in flight ahead of the MFMAs
 
 enum : int { BG_VALU = 0x002, BG_MFMA = 0x008, BG_DS_READ = 0x100, BG_DS_WRITE = 0x200,
              BG_TRANS = 0x400 };
@@ -172,39 +173,52 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     dv_acc[dt] = f32x16{};
   }
 
-  // P and dS of one 32-query half (accumulator rows = queries 32qt + acc_row,
-  // column = key), packed as the B operands of the two 16-query steps.
-  auto p_ds = [&](const f32x16& s, const f32x16& dp, const float* lse_s, const float* d_s, int qt,
-                  int qs, bool masked, bf16x8& pb0, bf16x8& pb1, bf16x8& db0, bf16x8& db1) __device__ {
+  // P and dS of one element of a 32-query half hh (accumulator register
+  // r = 4g + e: query 32hh + 8g + 4h + e, column = this lane's key), packed in
+  // pairs into the B operands of the two 16-query steps of the half. The
+  // half's statistics are read from LDS ahead of its steps (load_stats).
+  struct HalfState {
+    f32x4 l4[4], d4[4];
+    float pv[2], dsv[2];
     i32x4 pp[2], dd[2];
+  };
+  auto load_stats = [&](const float* lse_s, const float* d_s, int hh, HalfState& hs) __device__ {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int qrow = 32 * qt + 8 * g + 4 * h;
-      const f32x4 l4 = *(const f32x4*)(lse_s + qrow);
-      const f32x4 d4 = *(const f32x4*)(d_s + qrow);
-      float pv[4], dsv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float p = exp2_hw(fmaf(s[r], c_log2, -l4[e]));
-        if (CAUSAL && masked && key > qs + qrow + e) p = 0.0f;
-        pv[e] = p;
-        dsv[e] = p * (dp[r] - d4[e]);
-      }
-      pp[g >> 1][2 * (g & 1)] = (int)pack_bf16x2(pv[0], pv[1]);
-      pp[g >> 1][2 * (g & 1) + 1] = (int)pack_bf16x2(pv[2], pv[3]);
-      dd[g >> 1][2 * (g & 1)] = (int)pack_bf16x2(dsv[0], dsv[1]);
-      dd[g >> 1][2 * (g & 1) + 1] = (int)pack_bf16x2(dsv[2], dsv[3]);
+      hs.l4[g] = *(const f32x4*)(lse_s + 32 * hh + 8 * g + 4 * h);
+      hs.d4[g] = *(const f32x4*)(d_s + 32 * hh + 8 * g + 4 * h);
     }
-    pb0 = __builtin_bit_cast(bf16x8, pp[0]);
-    pb1 = __builtin_bit_cast(bf16x8, pp[1]);
-    db0 = __builtin_bit_cast(bf16x8, dd[0]);
-    db1 = __builtin_bit_cast(bf16x8, dd[1]);
+  };
+  auto pds_step = [&](const f32x16& sv, const f32x16& dpv, int hh, int qs, bool masked,
+                      HalfState& hs, int x) __device__ {
+    const int g = x / 4, e = x % 4, r = x;
+    const int qrow = 32 * hh + 8 * g + 4 * h;
+    float p = exp2_hw(fmaf(sv[r], c_log2, -hs.l4[g][e]));
+    if (CAUSAL && masked && key > qs + qrow + e) p = 0.0f;
+    const float ds = p * (dpv[r] - hs.d4[g][e]);
+    hs.pv[e & 1] = p;
+    hs.dsv[e & 1] = ds;
+    if (e & 1) {
+      const int w = 2 * (g & 1) + (e >> 1);
+      hs.pp[g >> 1][w] = (int)pack_bf16x2(hs.pv[0], hs.pv[1]);
+      hs.dd[g >> 1][w] = (int)pack_bf16x2(hs.dsv[0], hs.dsv[1]);
+      // Keep the step beside its MFMA instead of letting it sink to the use.
+      asm volatile("" ::"v"(hs.pp[g >> 1][w]), "v"(hs.dd[g >> 1][w]));
+    }
   };
 
+  // One query tile. The work is laid out in program order as pieces of one
+  // MFMA each, separated by scheduling fences; each piece issues the LDS
+  // operand read kLeadB pieces ahead and one element step of the softmax
+  // gradient, so no MFMA waits for its own operand (one wave per SIMD: there
+  // is no other wave to hide the LDS latency) and the VALU work sits beside
+  // the MFMAs:
+  //   A: S, dP of half 0 (16 MFMA)  B: S, dP of half 1 ∥ P, dS of half 0
+  //   C: dVᵀ, dKᵀ of half 0 ∥ P, dS of half 1   D: dVᵀ, dKᵀ of half 1
   auto iteration = [&](int it, auto parity_tag, auto masked_tag) __device__ {
     constexpr int PAR = decltype(parity_tag)::value;  // stage of tile it
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int NR = 4 * KD;  // S/dP operand reads: half i/(2KD), kk (i/2)%KD, Q or dO by i%2
     const int qs = it * kBwdBM;
     if (it + 1 < n_qt) gload(it + 1, PAR ^ 1);
     const char* qb = q_lds + PAR * 2 * QT_BYTES;
@@ -212,62 +226,71 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const float* lse_s = (const float*)(st_lds + PAR * 512);
     const float* d_s = lse_s + kBwdBM;
 
-    // S and dP of query half 0.
-    f32x16 s0 = {}, dp0 = {}, s1 = {}, dp1 = {};
+    auto sread = [&](int i) __device__ {
+      const int hh = i / (2 * KD), kk = (i / 2) % KD;
+      return *(const bf16x8*)((i % 2 ? db : qb) + hh * 32 * RB + qoff[kk]);
+    };
+    f32x16 sd[2][2];  // [half][S, dP]
+    bf16x8 ra[NR];
+    HalfState hs0, hs1;
 #pragma unroll
-    for (int kk = 0; kk < KD; ++kk) {
-      s0 = mfma32(*(const bf16x8*)(qb + qoff[kk]), kreg[kk], s0);
-      dp0 = mfma32(*(const bf16x8*)(db + qoff[kk]), vreg[kk], dp0);
+    for (int i = 0; i < kLeadB; ++i) ra[i] = sread(i);
+    load_stats(lse_s, d_s, 0, hs0);
+    load_stats(lse_s, d_s, 1, hs1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int hh = i / (2 * KD), kk = (i / 2) % KD, w = i % 2;
+      sd[hh][w] = mfma32(ra[i], w ? vreg[kk] : kreg[kk], kk == 0 ? f32x16{} : sd[hh][w]);
+      if (i + kLeadB < NR) ra[i + kLeadB] = sread(i + kLeadB);
+      if (hh == 1) {
+        // 16 element steps of half 0 over the 2KD pieces of phase B.
+#pragma unroll
+        for (int x = (i - 2 * KD) * 16 / (2 * KD); x < (i - 2 * KD + 1) * 16 / (2 * KD); ++x)
+          pds_step(sd[0][0], sd[0][1], 0, qs, MASKED, hs0, x);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // S and dP of half 1 ∥ P, dS of half 0.
     bf16x8 pb[4], dsb[4];
+    pb[0] = __builtin_bit_cast(bf16x8, hs0.pp[0]);
+    pb[1] = __builtin_bit_cast(bf16x8, hs0.pp[1]);
+    dsb[0] = __builtin_bit_cast(bf16x8, hs0.dd[0]);
+    dsb[1] = __builtin_bit_cast(bf16x8, hs0.dd[1]);
+
+    // dVᵀ += dOᵀ·P, dKᵀ += Qᵀ·dS: piece i = ks (i / 2DT), d tile (i / 2) % DT,
+    // dV or dK by i % 2; two transpose reads each.
+    constexpr int NT = 8 * DT;
+    bf16x4 ta[NT][2];
+    auto tread = [&](int i) __device__ {
+      const int ks = i / (2 * DT), dt = (i / 2) % DT;
+      const char* base = (i % 2 ? qb : db) + 16 * ks * RB;
+      ta[i][0] = lds_read_tr16(base + toff[0][dt]);
+      ta[i][1] = lds_read_tr16(base + toff[1][dt]);
+    };
 #pragma unroll
-    for (int kk = 0; kk < KD; ++kk) {
-      s1 = mfma32(*(const bf16x8*)(qb + 32 * RB + qoff[kk]), kreg[kk], s1);
-      dp1 = mfma32(*(const bf16x8*)(db + 32 * RB + qoff[kk]), vreg[kk], dp1);
+    for (int i = 0; i < kLeadB; ++i) tread(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int ks = i / (2 * DT), dt = (i / 2) % DT;
+      if (ks == 2 && i % (2 * DT) == 0) {
+        pb[2] = __builtin_bit_cast(bf16x8, hs1.pp[0]);
+        pb[3] = __builtin_bit_cast(bf16x8, hs1.pp[1]);
+        dsb[2] = __builtin_bit_cast(bf16x8, hs1.dd[0]);
+        dsb[3] = __builtin_bit_cast(bf16x8, hs1.dd[1]);
+      }
+      const bf16x8 a = concat(ta[i][0], ta[i][1]);
+      if (i % 2) dk_acc[dt] = mfma32(a, dsb[ks], dk_acc[dt]);
+      else dv_acc[dt] = mfma32(a, pb[ks], dv_acc[dt]);
+      if (i + kLeadB < NT) tread(i + kLeadB);
+      if (ks < 2) {
+        // 16 element steps of half 1 over the 4DT pieces of phase C.
+#pragma unroll
+        for (int x = i * 16 / (4 * DT); x < (i + 1) * 16 / (4 * DT); ++x)
+          pds_step(sd[1][0], sd[1][1], 1, qs, MASKED, hs1, x);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    p_ds(s0, dp0, lse_s, d_s, 0, qs, MASKED, pb[0], pb[1], dsb[0], dsb[1]);
-    if constexpr (!MASKED) {
-#pragma unroll
-      for (int i = 0; i < 2 * KD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(BG_DS_READ, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(BG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(BG_VALU | BG_TRANS | BG_DS_READ, 3, 0);
-      }
-    }
-    // dVᵀ, dKᵀ for the 16-query steps of half 0 ∥ P, dS of half 1.
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 g0 = lds_read_tr16(db + 16 * ks * RB + toff[0][dt]);
-        const bf16x4 g1 = lds_read_tr16(db + 16 * ks * RB + toff[1][dt]);
-        dv_acc[dt] = mfma32(concat(g0, g1), pb[ks], dv_acc[dt]);
-        const bf16x4 q0 = lds_read_tr16(qb + 16 * ks * RB + toff[0][dt]);
-        const bf16x4 q1 = lds_read_tr16(qb + 16 * ks * RB + toff[1][dt]);
-        dk_acc[dt] = mfma32(concat(q0, q1), dsb[ks], dk_acc[dt]);
-      }
-    p_ds(s1, dp1, lse_s, d_s, 1, qs, MASKED, pb[2], pb[3], dsb[2], dsb[3]);
-    if constexpr (!MASKED) {
-#pragma unroll
-      for (int i = 0; i < 2 * DT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(BG_DS_READ, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(BG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(BG_VALU | BG_TRANS | BG_DS_READ, 3, 0);
-      }
-    }
-    // The half-1 steps.
-#pragma unroll
-    for (int ks = 2; ks < 4; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 g0 = lds_read_tr16(db + 16 * ks * RB + toff[0][dt]);
-        const bf16x4 g1 = lds_read_tr16(db + 16 * ks * RB + toff[1][dt]);
-        dv_acc[dt] = mfma32(concat(g0, g1), pb[ks], dv_acc[dt]);
-        const bf16x4 q0 = lds_read_tr16(qb + 16 * ks * RB + toff[0][dt]);
-        const bf16x4 q1 = lds_read_tr16(qb + 16 * ks * RB + toff[1][dt]);
-        dk_acc[dt] = mfma32(concat(q0, q1), dsb[ks], dk_acc[dt]);
-      }
     // Both stages are free once every wave is done with this tile and the
     // next tile's loads have landed.
     wait_vmem();
