@@ -72,9 +72,10 @@ typedef enum {
  *   lse      [B,H,N] fp32 output, natural-log log-sum-exp of the masked,
  *            scaled scores of each row (required: the backward consumes it).
  *   exp_mode one of fattn_exp_mode.
- * The softmax keeps a running row max and sum and rescales the partial
- * output only when the row max has grown by more than 2^8 in the exp2
- * domain (FlashAttention-4 gist, technical summary 2.B), which is exact.
+ * The softmax keeps an exponent offset and an fp32 row sum per row and
+ * rescales the partial output only when some probability of a tile would
+ * exceed 2^8 relative to the offset in use (FlashAttention-4 gist,
+ * technical summary 2.B), which is exact.
  */
 fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o,
                        float* lse, int B, int H, int N, int d, int causal,

@@ -37,31 +37,6 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// The same product in inline assembly with the register classes pinned:
-// mfma32_acc accumulates into AGPRs (B from VGPRs), mfma32_ab writes a VGPR
-// result from an A operand in VGPRs and a B operand in AGPRs (first k-step:
-// mfma32_ab0, zero accumulator). Keeping the long-lived accumulators and the
-// loop-invariant operand in AGPRs leaves the architectural VGPRs to the
-// values the VALU works on. The compiler does not see these as MFMAs, so it
-// inserts no wait states after them: callers put mfma_drain() between such a
-// product and the first VALU instruction that reads its result, unless many
-// other instructions separate the two.
-__device__ __forceinline__ void mfma32_acc(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32_ab(f32x16& c, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
-}
-__device__ __forceinline__ void mfma32_ab0(f32x16& c, bf16x8 a, bf16x8 b) {
-  // Early clobber: the result must not share registers with the A operand.
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
-}
-// Wait states that cover the latency of a 32x32 MFMA result before a VALU
-// instruction reads it.
-__device__ __forceinline__ void mfma_drain() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-
 // fp8 (e4m3fn for both operands) 32x32x64: A lane holds 32 k values of row c,
 // B lane holds 32 k values of column c; the k split between the lane halves
 // is the same for A and B, C as for mfma32.
@@ -154,21 +129,6 @@ __device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, char*
                  : "s"(m0v), "v"(off[i]), "s"(rsrc)
                  : "memory", "m0");
   }
-#endif
-}
-
-// One wave load of 16 bytes per lane from buffer byte offset voff (zero past
-// the buffer's end) to LDS at lds_dst + lane·16; untracked by the compiler
-// like buffer_to_lds. (The instruction's immediate offset would move the LDS
-// destination as well, so callers shift the buffer base instead.)
-__device__ __forceinline__ void dma16(const i32x4& rsrc, const char* lds_dst, int voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  const int m0v =
-      __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const FATTN_LDS char*)lds_dst);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m0v), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
 #endif
 }
 
