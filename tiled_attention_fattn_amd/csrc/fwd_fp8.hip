@@ -20,12 +20,15 @@
 //                   32x32x64 f8f6f4 MFMA; P̃ = 2^(s·c − m + 8) quantised to
 //                   e4m3 (P̃ ≤ 1 because the running max is updated whenever
 //                   it grows, so P̃·2^8 ≤ 256 < 448); O = Oᵀ·s_v/l.
+#include <type_traits>
+
 #include "fattn_device.hpp"
 #include "fattn_launch.h"
 
 namespace fattn {
 
 constexpr float kE4m3Max = 448.0f;
+constexpr int kRowSets = 4;  // rows per thread processed together in the row-wise kernels
 
 // SplitMix64: state advanced by the golden-ratio increment, then mixed.
 __device__ __forceinline__ float rotation_sign(uint64_t seed, int i) {
@@ -98,11 +101,18 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ 
   const bf16* src = (t == 0 ? Q : t == 1 ? K : V) + (size_t)bh * N * D;
   const int part = threadIdx.x % LPR;
   float m = 0.0f;
-  for (int r0 = chunk * kFp8AmaxRows; r0 < min(N, (chunk + 1) * kFp8AmaxRows); r0 += RPB) {
-    float x[8];
-    load_row_part<D>(src, r0 + threadIdx.x / LPR, N, part, rot, sgn, x);
+  // kRowSets row-sets per step so that that many loads per thread are in
+  // flight together.
+  const int r_end = min(N, (chunk + 1) * kFp8AmaxRows);
+  for (int r0 = chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
+    float x[kRowSets][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+    for (int u = 0; u < kRowSets; ++u)
+      load_row_part<D>(src, r0 + u * RPB + threadIdx.x / LPR, r_end, part, rot, sgn, x[u]);
+#pragma unroll
+    for (int u = 0; u < kRowSets; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[u][e]));
   }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
@@ -177,29 +187,39 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restric
   uint8_t* dst = (t == 0 ? q8 : k8) + head;
   if (chunk == 0 && threadIdx.x == 0) scales[t * BH + bh] = scale_from_amax(am);
   const int part = threadIdx.x % LPR;
-  for (int r0 = chunk * kFp8AmaxRows; r0 < min(N, (chunk + 1) * kFp8AmaxRows); r0 += RPB) {
-    const int row = r0 + threadIdx.x / LPR;
-    float x[8];
-    if (!load_row_part<D>(src, row, N, part, rotate != 0, sgn, x)) continue;
-    float tt[8];
+  const int r_end = min(N, (chunk + 1) * kFp8AmaxRows);
+  for (int r0 = chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
+    float xs[kRowSets][8];
+    bool ok[kRowSets];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tt[e] = am > 0.0f ? clamp448(ratio448(x[e], am)) : x[e];
-    i32x2 w;
-    w[0] = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
-    w[1] = cvt_fp8x4(tt[4], tt[5], tt[6], tt[7]);
-    *(i32x2*)(dst + (size_t)row * D + part * 8) = w;
-    if (t == 0) {
-      // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
-      float dec[8];
-      dec_fp8x4(w[0], dec);
-      dec_fp8x4(w[1], dec + 4);
-      float r[8];
+    for (int u = 0; u < kRowSets; ++u)
+      ok[u] = load_row_part<D>(src, r0 + u * RPB + threadIdx.x / LPR, r_end, part, rotate != 0, sgn,
+                               xs[u]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = 16.0f * (tt[e] - dec[e]);
-      i32x2 wl;
-      wl[0] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
-      wl[1] = cvt_fp8x4(r[4], r[5], r[6], r[7]);
-      *(i32x2*)(q8lo + head + (size_t)row * D + part * 8) = wl;
+    for (int u = 0; u < kRowSets; ++u) {
+      if (!ok[u]) continue;
+      const int row = r0 + u * RPB + threadIdx.x / LPR;
+      const float (&x)[8] = xs[u];
+      float tt[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tt[e] = am > 0.0f ? clamp448(ratio448(x[e], am)) : x[e];
+      i32x2 w;
+      w[0] = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
+      w[1] = cvt_fp8x4(tt[4], tt[5], tt[6], tt[7]);
+      *(i32x2*)(dst + (size_t)row * D + part * 8) = w;
+      if (t == 0) {
+        // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
+        float dec[8];
+        dec_fp8x4(w[0], dec);
+        dec_fp8x4(w[1], dec + 4);
+        float r[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = 16.0f * (tt[e] - dec[e]);
+        i32x2 wl;
+        wl[0] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
+        wl[1] = cvt_fp8x4(r[4], r[5], r[6], r[7]);
+        *(i32x2*)(q8lo + head + (size_t)row * D + part * 8) = wl;
+      }
     }
   }
 }
@@ -251,7 +271,12 @@ __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// fp8 attention kernel: 4 waves × 32 queries, 64-key tiles.
+// fp8 attention kernel: 4 waves × 32 queries, 64-key tiles, two workgroups per
+// compute unit. K8 and V8ᵀ tiles stream into LDS by buffer loads that write
+// LDS directly (row-major, 64-bank swizzle), double-buffered and issued an
+// iteration ahead. Software pipeline as in the bf16 forward: the softmax of
+// tile j runs beside the MFMAs of S(j+1), the row max of tile j+1 beside
+// PV(j).
 // ---------------------------------------------------------------------------
 constexpr int kF8Waves = 4;
 constexpr int kF8BM = 32 * kF8Waves;
@@ -265,15 +290,18 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
                     bf16* __restrict__ O, float* __restrict__ LSE, int N, int Npad, int BH,
                     int n_qtiles, float scale_log2) {
   constexpr int KD = D / 64;           // fp8 MFMA k-steps over d
-  constexpr int KB = kF8BN * D;        // bytes of the K8 tile ([64][D])
-  constexpr int VB = D * kF8BN;        // bytes of the V8ᵀ tile ([D][64])
-  constexpr int KCH = D / 16;          // 16-byte chunks per K8 row
-  constexpr int KCPT = kF8BN * KCH / 256;
-  constexpr int VCPT = D * 4 / 256;
+  constexpr int KTILE = kF8BN * D;     // K8 tile [64 keys][D bytes]
+  constexpr int VTILE = D * kF8BN;     // V8ᵀ tile [D][64 keys]
   constexpr int DT = D / 32;
-  __shared__ __attribute__((aligned(16))) char lds[2 * (KB + VB)];
+  constexpr int KLOADS = KTILE / 1024 / kF8Waves;  // 1 KB wave loads per tile and wave
+  constexpr int VLOADS = VTILE / 1024 / kF8Waves;
+  // LDS: K slots 0, 1 then V slots 0, 1.
+  __shared__ __attribute__((aligned(16))) char lds[2 * KTILE + 2 * VTILE];
+  char* const k_lds = lds;
+  char* const v_lds = lds + 2 * KTILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
 
   const int total = n_qtiles * BH;
@@ -312,94 +340,133 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
     }
   }
 
+  // Per-lane LDS offsets of the MFMA A operands: K8 row c (key), bytes
+  // kk·64 + 32h .. +32 (two 16-byte chunks); V8ᵀ row c (d within a 32-row
+  // tile), key bytes 32h .. +32.
+  int koff[KD][2], voff[2];
+#pragma unroll
+  for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) koff[kk][u] = tile_off_rb<D>(c, 4 * kk + 2 * h + u);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) voff[u] = tile_off_rb<64>(c, 2 * h + u);
+
   const int kv_end = CAUSAL ? min(N, q_start + kF8BM) : N;
   const int n_kv = (kv_end + kF8BN - 1) / kF8BN;
+  const int first_masked = CAUSAL ? min(q_start / kF8BN, N / kF8BN) : N / kF8BN;
 
-  i32x4 pk[KCPT], pv[VCPT];
-  auto gload = [&](int j) __device__ {
+  // Wave loads of the tiles (swizzle applied on the source side). K8 rows
+  // past N read as zero (buffer range check); V8ᵀ is zero-padded to Npad.
+  int ldk[KLOADS], ldv[VLOADS];
+#pragma unroll
+  for (int i = 0; i < KLOADS; ++i) {
+    const int r = (wave * KLOADS + i) * (1024 / D) + lane / (D / 16);
+    ldk[i] = r * D + swz_chunk_rb<D>(r, lane % (D / 16)) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) {
+    const int r = (wave * VLOADS + i) * 16 + lane / 4;
+    ldv[i] = r * Npad + swz_chunk_rb<64>(r, lane % 4) * 16;
+  }
+  auto gload_k = [&](char* tile, int j) __device__ {
     const int key0 = j * kF8BN;
-#pragma unroll
-    for (int i = 0; i < KCPT; ++i) {
-      const int ch = tid + i * 256;
-      const int r = ch / KCH, cc = ch % KCH;
-      pk[i] = (key0 + r < N) ? *(const i32x4*)(Kh + (size_t)(key0 + r) * D + cc * 16) : i32x4{};
-    }
-#pragma unroll
-    for (int i = 0; i < VCPT; ++i) {
-      const int ch = tid + i * 256;
-      const int d = ch >> 2, part = ch & 3;
-      pv[i] = *(const i32x4*)(Vt + (size_t)d * Npad + key0 + part * 16);
-    }
+    buffer_to_lds<KLOADS>(Kh + (size_t)key0 * D, (N - key0) * D, tile, ldk, wave * KLOADS);
   };
-  auto lstore = [&](int stage) __device__ {
-    char* kb = lds + stage * (KB + VB);
-    char* vb = kb + KB;
-#pragma unroll
-    for (int i = 0; i < KCPT; ++i) {
-      const int ch = tid + i * 256;
-      const int r = ch / KCH, cc = ch % KCH;
-      *(i32x4*)(kb + tile_off_rb<D>(r, cc)) = pk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCPT; ++i) {
-      const int ch = tid + i * 256;
-      const int d = ch >> 2, part = ch & 3;
-      *(i32x4*)(vb + tile_off_rb<64>(d, part)) = pv[i];
-    }
+  auto gload_v = [&](char* tile, int j) __device__ {
+    const int key0 = j * kF8BN;
+    buffer_to_lds<VLOADS>(Vt + key0, D * Npad - key0, tile, ldv, wave * VLOADS);
   };
 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  float m_c = -INFINITY;
   float l_part = 0.0f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  auto scores = [&](const char* kt, f32x16 (&s)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        const i32x4 a0 = *(const i32x4*)(kt + t * 32 * D + koff[kk][0]);
+        const i32x4 a1 = *(const i32x4*)(kt + t * 32 * D + koff[kk][1]);
+        const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        s[t] = mfma32_fp8(a, qreg[kk], s[t]);
+        s[t] = mfma32_fp8_bscale(a, qlo[kk], s[t]);
+      }
+    }
+  };
+  auto mask = [&](f32x16 (&s)[2], int key0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * t + acc_row(r, h);
+        if (key >= N || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
+      }
+  };
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    return half_max(mx) * c_log2;
+  };
 
-  for (int j = 0; j < n_kv; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < n_kv) gload(j + 1);
-    const char* kb = lds + stage * (KB + VB);
-    const char* vb = kb + KB;
-    const int key0 = j * kF8BN;
-    const bool active = !CAUSAL || key0 <= q0 + 31;
-    if (active) {
-      f32x16 s[2];
+  gload_k(k_lds, 0);
+  if (n_kv > 1) gload_k(k_lds + KTILE, 1);
+  gload_v(v_lds, 0);
+  wait_vmem();
+  __syncthreads();
+  f32x16 s[2];
+  scores(k_lds, s);
+  if (first_masked == 0) mask(s, 0);
+  // The running max moves whenever it grows (τ = 0), so P̃ ≤ 1 and
+  // P̃·2^8 ≤ 256 < 448 fits e4m3.
+  float m_c = tile_max(s);
+
+  auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
+    constexpr int PAR = decltype(parity_tag)::value;
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    if constexpr (HAS_NEXT) {
+      if (j + 2 < n_kv) gload_k(k_lds + PAR * KTILE, j + 2);
+      gload_v(v_lds + (PAR ^ 1) * VTILE, j + 1);
+    }
+    // P̃·2^8 in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
+    const float off = 8.0f - m_c;
+    i32x8 p8;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = f32x16{};
-        const int row = 32 * t + c;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          const i32x4 a0 = *(const i32x4*)(kb + tile_off_rb<D>(row, 4 * kk + 2 * h));
-          const i32x4 a1 = *(const i32x4*)(kb + tile_off_rb<D>(row, 4 * kk + 2 * h + 1));
-          const i32x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-          s[t] = mfma32_fp8(a, qreg[kk], s[t]);
-          s[t] = mfma32_fp8_bscale(a, qlo[kk], s[t]);
+      for (int wd = 0; wd < 4; ++wd) {
+        float pv4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv4[e] = exp2_hw(fmaf(s[t][4 * wd + e], c_log2, off));
+          l_part += pv4[e];
         }
+        p8[4 * t + wd] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
       }
-      const bool need_mask = (key0 + kF8BN > N) || (CAUSAL && key0 + kF8BN - 1 > q0);
-      if (need_mask) {
+    f32x16 ns[2];
+    if constexpr (HAS_NEXT) {
+      scores(k_lds + (PAR ^ 1) * KTILE, ns);
+      // Keep the softmax of tile j beside these MFMAs.
+      asm volatile("" ::"v"(p8));
+      if (j + 1 >= first_masked) mask(ns, (j + 1) * kF8BN);
+    }
+    const char* vt = v_lds + PAR * VTILE;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * t + acc_row(r, h);
-            if (key >= N || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = half_max(mx);
-      const float mx_c = mx * c_log2;
-      const bool resc = mx_c > m_c;
-      if (__ballot(resc)) {
-        const float m_new = resc ? mx_c : m_c;
+    for (int dt = 0; dt < DT; ++dt) {
+      const i32x4 a0 = *(const i32x4*)(vt + dt * 32 * 64 + voff[0]);
+      const i32x4 a1 = *(const i32x4*)(vt + dt * 32 * 64 + voff[1]);
+      oacc[dt] = mfma32_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8, oacc[dt]);
+    }
+    if constexpr (HAS_NEXT) {
+      const float mx = tile_max(ns);
+      if (__ballot(mx > m_c)) {
+        const bool resc = mx > m_c;
+        const float m_new = resc ? mx : m_c;
         const float alpha = resc ? exp2_hw(m_c - m_new) : 1.0f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -408,31 +475,24 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
         l_part *= alpha;
         m_c = m_new;
       }
-      // P̃·2^8 in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
-      const float off = 8.0f - m_c;
-      i32x8 p8;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          float pv4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pv4[e] = exp2_hw(fmaf(s[t][4 * wd + e], c_log2, off));
-            l_part += pv4[e];
-          }
-          p8[4 * t + wd] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
-        }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int row = 32 * dt + c;
-        const i32x4 a0 = *(const i32x4*)(vb + tile_off_rb<64>(row, 2 * h));
-        const i32x4 a1 = *(const i32x4*)(vb + tile_off_rb<64>(row, 2 * h + 1));
-        oacc[dt] = mfma32_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8, oacc[dt]);
-      }
+      s[0] = ns[0];
+      s[1] = ns[1];
+      wait_vmem();
+      __syncthreads();
     }
-    if (j + 1 < n_kv) lstore(stage ^ 1);
-    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  int j = 0;
+  for (; j + 2 < n_kv; j += 2) {
+    iteration(j, I0{}, std::true_type{});
+    iteration(j + 1, I1{}, std::true_type{});
+  }
+  if (j + 1 < n_kv) {
+    iteration(j, I0{}, std::true_type{});
+    iteration(j + 1, I1{}, std::false_type{});
+  } else {
+    iteration(j, I0{}, std::false_type{});
   }
 
   const float l = half_sum(l_part);
