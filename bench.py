@@ -35,13 +35,13 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--parts", default=",".join(PARTS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-exp-variants", action="store_true",
-                    help="skip the separate hw/poly exp2 timing of the forward")
+                    help="skip the separate hw/poly/split exp2 timing of the forward")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device-to-device copy of this many bytes "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -110,9 +110,16 @@ def setup_part(part, torch, fa):
         return lambda: fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=w["causal"],
                               scale=scale, workspace=ws, out=grads)
     o = torch.empty_like(t["q"])
+    o2 = torch.empty_like(t["q"])
     ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
-    return lambda: fa.fwd_fp8(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
-                              rotate=w["rotate"], seed=k, want_lse=False, workspace=ws, out=o)
+
+    def run(mode="full"):
+        if mode == "attend":  # the attention step alone on the operands of the last full call
+            return fa.fwd_fp8_attend(ws, B, H, N, d, causal=w["causal"], scale=scale,
+                                     want_lse=False, out=o2)
+        return fa.fwd_fp8(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
+                          rotate=w["rotate"], seed=k, want_lse=False, workspace=ws, out=o)
+    return run
 
 
 def cpu_baseline(parts, heads):
@@ -164,6 +171,7 @@ def main():
 
     parts = [p for p in args.parts.split(",") if p]
     torch.cuda.set_device(0)
+    clocks_before = gpu_clocks()
     launch = {p: setup_part(p, torch, fa) for p in parts}
     torch.cuda.synchronize()
 
@@ -187,7 +195,8 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
 
-    part_ms = {p: float(np.mean([a.elapsed_time(b) for a, b in ev[p]])) for p in parts}
+    samples = {p: [a.elapsed_time(b) for a, b in ev[p]] for p in parts}
+    part_ms = {p: float(np.mean(samples[p])) for p in parts}
     flops = {p: part_flops(p) for p in parts}
     step_flop = sum(flops.values())
     value = step_flop / (ms_per_step * 1e-3) / 1e12
@@ -197,12 +206,14 @@ def main():
         tf = flops[p] / (part_ms[p] * 1e-3) / 1e12
         peak = PEAK_FP8 if p == "fp8" else PEAK_BF16
         info[p] = {"workload": fa_workload_name(p), "ms": round(part_ms[p], 4),
+                   "ms_median": round(float(np.median(samples[p])), 4),
+                   "ms_min": round(float(np.min(samples[p])), 4),
                    "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
 
     # The C3 forward is also reported with each exp2 variant.
     if "fwd" in parts and not args.no_exp_variants:
         variants = {}
-        for mode in ("hw", "poly"):
+        for mode in ("hw", "poly", "split"):
             for _ in range(3):
                 launch["fwd"](mode)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -226,6 +237,24 @@ def main():
                 "peak": dom_peak, "unit": "TFLOP/s", "frac": round(achieved / dom_peak, 4),
                 "traffic": committed_traffic(dom)}
 
+    # The fp8 attention step alone (after the quantisation the timed calls did).
+    if "fp8" in parts:
+        for _ in range(3):
+            launch["fp8"]("attend")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            launch["fp8"]("attend")
+        b.record()
+        torch.cuda.synchronize()
+        ams = a.elapsed_time(b) / 20
+        atf = flops["fp8"] / (ams * 1e-3) / 1e12
+        info["fp8"]["attention_only"] = {"ms": round(ams, 4), "tflops": round(atf, 1),
+                                         "frac_of_peak": round(atf / PEAK_FP8, 4)}
+    clocks = gpu_clocks()
+    if clocks_before or clocks:
+        info["gpu_clock_mhz"] = {"before": clocks_before, "after": clocks}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(parts, args.cpu_heads)
@@ -242,6 +271,19 @@ def main():
         "parts": info, "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def gpu_clocks():
+    """Current shader clock (MHz) of GPU 0 from rocm-smi, or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True,
+                             text=True, timeout=20).stdout
+    except Exception:  # noqa: BLE001 (no rocm-smi: report nothing)
+        return None
+    m = re.search(r"sclk.*?\((\d+)Mhz\)", out)
+    return int(m.group(1)) if m else None
 
 
 def fa_workload_name(p):

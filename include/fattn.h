@@ -61,7 +61,10 @@ typedef enum {
 typedef enum {
   FATTN_EXP_AUTO = 0,    /* the variant measured fastest on gfx950 (hardware) */
   FATTN_EXP_HW = 1,      /* v_exp_f32 on the transcendental unit */
-  FATTN_EXP_POLY = 2     /* Cody–Waite split + degree-3 polynomial on FMA units */
+  FATTN_EXP_POLY = 2,    /* Cody–Waite split + degree-3 polynomial on FMA units */
+  FATTN_EXP_SPLIT = 3    /* a static quarter of the exponentials (one in four
+                            element pairs) on the polynomial, the rest on
+                            the hardware unit */
 } fattn_exp_mode;
 
 /*
@@ -136,6 +139,22 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                            float* lse, int B, int H, int N, int d, int causal,
                            float scale, int rotate, uint64_t seed,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The attention step of fattn_fwd_fp8 alone (FlashAttention-3 page,
+ * "Nuevas capacidades…" (FP8): the fp8 matrix products with the softmax
+ * between them), on a workspace that a previous fattn_fwd_fp8 call with the
+ * same B, H, N, d filled: it reads the e4m3 operands Q8, Q8lo, K8, V8ᵀ and
+ * the scales from the workspace and writes o (and lse if non-NULL) exactly as
+ * that call did for the same causal and scale. The workspace is only read.
+ * For re-running attention on operands already quantised and rotated, and
+ * for timing the attention step apart from the quantisation.
+ * Errors as fattn_fwd_fp8 (a workspace never filled gives meaningless o,
+ * not an error).
+ */
+fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int d,
+                                  int causal, float scale, const void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* fattn_strerror(int status);

@@ -52,7 +52,7 @@ def fwd(**kw):
     (dict(lse=NUL), EINVAL), (dict(q=MIS), EINVAL), (dict(B=0), EINVAL), (dict(H=-1), EINVAL),
     (dict(N=0), EINVAL), (dict(d=96), ENOTSUP), (dict(d=256), ENOTSUP), (dict(causal=2), EINVAL),
     (dict(scale=0.0), EINVAL), (dict(scale=-1.0), EINVAL), (dict(scale=float("inf")), EINVAL),
-    (dict(scale=float("nan")), EINVAL), (dict(exp=3), EINVAL),
+    (dict(scale=float("nan")), EINVAL), (dict(exp=4), EINVAL), (dict(exp=-1), EINVAL),
     (dict(B=4096, H=64, N=8192, d=128), ENOTSUP),
 ])
 def test_fwd_rejects_bad_arguments(kw, code):
@@ -102,3 +102,24 @@ def test_fp8_workspace_layout_and_checks():
     assert call(P, need, rotate=2) == EINVAL
     assert call(P, need, lse=MIS) == EINVAL
     assert call(P, need, d=80) == ENOTSUP
+
+
+def test_fp8_attend_checks():
+    lib = fa.lib()
+    B, H, N, d = 2, 3, 100, 128
+    need = lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
+
+    def call(ws, nbytes, **kw):
+        a = dict(o=P, lse=NUL, B=B, H=H, N=N, d=d, causal=0, scale=0.1)
+        a.update(kw)
+        return lib.fattn_fwd_fp8_attend(a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                        a["causal"], ctypes.c_float(a["scale"]), ws, nbytes, NUL)
+    assert call(NUL, need) == EWORKSPACE
+    assert call(P, need - 1) == EWORKSPACE
+    assert call(MIS, need) in (EINVAL, EWORKSPACE)
+    assert call(P, need, o=NUL) == EINVAL
+    assert call(P, need, lse=MIS) == EINVAL
+    assert call(P, need, d=96) == ENOTSUP
+    assert call(P, need, N=0) == EINVAL
+    assert call(P, need, scale=float("nan")) == EINVAL
+    assert call(P, need, causal=3) == EINVAL

@@ -142,3 +142,20 @@ def test_fp8_full_size_sampled_and_rotation_ratio():
             json.dump({"rel_rms_rotate": err[True], "rel_rms_no_rotate": err[False],
                        "ratio": ratio, "workload": w["name"], "rows": len(rows),
                        "heads": heads}, fh)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_attend_reuses_workspace(causal):
+    # The attention step alone on the operands a full call left in the
+    # workspace reproduces that call's O and LSE bit for bit.
+    import tiled_attention_fattn_amd as fa
+    shape = (2, 3, 300, 128)
+    inp = _inputs(61, shape)
+    q, k, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    B, H, N, d = shape
+    ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    print(f"[fp8] attend on workspace shape={shape} causal={causal}", flush=True)
+    o1, l1 = fa.fwd_fp8(q, k, v, causal=causal, rotate=True, seed=3, workspace=ws)
+    o2, l2 = fa.fwd_fp8_attend(ws, B, H, N, d, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

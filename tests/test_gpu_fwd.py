@@ -44,7 +44,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("exp_mode", ["hw", "poly"])
+@pytest.mark.parametrize("exp_mode", ["hw", "poly", "split"])
 @pytest.mark.parametrize("k,shape,causal", SMALL)
 def test_fwd_matches_oracle(k, shape, causal, exp_mode):
     inp, o, lse, scale = _run(k, shape, causal, exp_mode)
@@ -57,7 +57,7 @@ def test_fwd_matches_oracle(k, shape, causal, exp_mode):
 def test_fwd_full_size_sampled(wk):
     w = WORKLOADS[wk]
     shape = (w["B"], w["H"], w["N"], w["d"])
-    for exp_mode in (["hw", "poly"] if wk == 3 else ["auto"]):
+    for exp_mode in (["hw", "poly", "split"] if wk == 3 else ["auto"]):
         inp, o, lse, scale = _run(wk, shape, w["causal"], exp_mode)
         o_np = o.view(-1, w["N"], w["d"])
         lse_np = lse.view(-1, w["N"])
@@ -118,10 +118,12 @@ def test_fwd_exp_modes_agree():
     q, k, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
     o_hw, l_hw = fa.fwd(q, k, v, exp_mode="hw")
     o_p, l_p = fa.fwd(q, k, v, exp_mode="poly")
+    o_s, l_s = fa.fwd(q, k, v, exp_mode="split")
     o_a, l_a = fa.fwd(q, k, v, exp_mode="auto")
     assert torch.equal(o_a, o_hw)
-    diff = (o_hw.float() - o_p.float()).abs().max().item()
-    assert diff < 1e-2, diff
+    for other in (o_p, o_s):
+        diff = (o_hw.float() - other.float()).abs().max().item()
+        assert diff < 1e-2, diff
 
 
 @pytest.mark.parametrize("causal", [False, True])

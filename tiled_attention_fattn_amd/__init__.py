@@ -17,13 +17,13 @@ import os
 
 from ._lib import FattnError, lib, lib_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_fp8", "fp8_workspace_views", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
            "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
-           "EXP_AUTO", "EXP_HW", "EXP_POLY"]
+           "EXP_AUTO", "EXP_HW", "EXP_POLY", "EXP_SPLIT"]
 
-EXP_AUTO, EXP_HW, EXP_POLY = 0, 1, 2
-_EXP = {"auto": EXP_AUTO, "hw": EXP_HW, "poly": EXP_POLY,
-        EXP_AUTO: EXP_AUTO, EXP_HW: EXP_HW, EXP_POLY: EXP_POLY}
+EXP_AUTO, EXP_HW, EXP_POLY, EXP_SPLIT = 0, 1, 2, 3
+_EXP = {"auto": EXP_AUTO, "hw": EXP_HW, "poly": EXP_POLY, "split": EXP_SPLIT,
+        EXP_AUTO: EXP_AUTO, EXP_HW: EXP_HW, EXP_POLY: EXP_POLY, EXP_SPLIT: EXP_SPLIT}
 
 
 def _torch():
@@ -80,6 +80,22 @@ def fwd(q, k, v, causal=False, scale=None, exp_mode="auto", out=None, lse=None):
         _call(lib().fattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
                               int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
                               _stream(q)))
+    return o, lse_t
+
+
+def fwd_fp8_attend(workspace, B, H, N, d, causal=False, scale=None, want_lse=True, out=None,
+                   device=None):
+    """The attention step of fwd_fp8 alone, on a workspace a previous fwd_fp8
+    call of the same (B, H, N, d) filled. Returns (O, LSE or None)."""
+    torch = _torch()
+    scale = float(d ** -0.5 if scale is None else scale)
+    dev = workspace.device if device is None else device
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=dev) if want_lse else None
+    with torch.cuda.device(dev):
+        _call(lib().fattn_fwd_fp8_attend(_ptr(o), _ptr(lse_t), B, H, N, d, int(bool(causal)),
+                                         ctypes.c_float(scale), _ptr(workspace),
+                                         ctypes.c_size_t(workspace.numel()), _stream(o)))
     return o, lse_t
 
 

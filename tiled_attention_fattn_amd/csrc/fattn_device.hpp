@@ -167,7 +167,7 @@ __device__ __forceinline__ float half_sum(float x) {
 // exp2 variants (FlashAttention-4 gist, technical summary 2.B: 2^x computed
 // either by the special-function unit or by a polynomial on FMA units).
 // ---------------------------------------------------------------------------
-enum { EXP_HW = 1, EXP_POLY = 2 };
+enum { EXP_HW = 1, EXP_POLY = 2, EXP_SPLIT = 3 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -113,10 +113,10 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o, flo
   FATTN_TRY(check_ptr(o, "o"));
   FATTN_TRY(check_ptr(lse, "lse"));
   FATTN_TRY(check_shape(B, H, N, d, causal, scale));
-  if (exp_mode < FATTN_EXP_AUTO || exp_mode > FATTN_EXP_POLY)
-    return fail(FATTN_EINVAL, "exp_mode must be 0, 1 or 2 (got %d)", exp_mode);
+  if (exp_mode < FATTN_EXP_AUTO || exp_mode > FATTN_EXP_SPLIT)
+    return fail(FATTN_EINVAL, "exp_mode must be 0, 1, 2 or 3 (got %d)", exp_mode);
   FATTN_TRY(check_device());
-  const int mode = exp_mode == FATTN_EXP_POLY ? 2 : 1;
+  const int mode = exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode;
   return hip_status(fattn::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, mode,
                                            (hipStream_t)stream),
                     "fattn_fwd launch");
@@ -199,6 +199,30 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                                           H, N, d, causal != 0, scale,
                                           rotate != 0, seed, (hipStream_t)stream),
                     "fattn_fwd_fp8 launch");
+}
+
+fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int d, int causal,
+                                  float scale, const void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  FATTN_TRY(check_ptr(o, "o"));
+  if (lse != nullptr && !aligned16(lse)) return fail(FATTN_EINVAL, "lse is not 16-byte aligned");
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  if ((long long)B * H > 65535)
+    return fail(FATTN_ENOTSUP, "fp8 forward supports B*H <= 65535 (got %lld)", (long long)B * H);
+  if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
+  if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
+  const Fp8Layout L = fp8_layout(B, H, N, d);
+  if (workspace_bytes < L.total)
+    return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, L.total);
+  FATTN_TRY(check_device());
+  const char* ws = (const char*)workspace;
+  return hip_status(fattn::launch_fwd_fp8_attend(o, lse, (const uint8_t*)(ws + L.q8),
+                                                 (const uint8_t*)(ws + L.q8lo),
+                                                 (const uint8_t*)(ws + L.k8),
+                                                 (const uint8_t*)(ws + L.v8t),
+                                                 (const float*)(ws + L.scales), B, H, N, d,
+                                                 causal != 0, scale, (hipStream_t)stream),
+                    "fattn_fwd_fp8_attend launch");
 }
 
 const char* fattn_strerror(int status) {

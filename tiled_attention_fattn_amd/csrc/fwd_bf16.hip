@@ -85,8 +85,12 @@ __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c_log2,
       i32x4 packed;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e], c_log2, -m_c));
-        const float p1 = exp2_sel<EXPM>(fmaf(s[t][half * 8 + 2 * e + 1], c_log2, -m_c));
+        // SPLIT: the pair e = 3 of every group of four goes to the polynomial.
+        constexpr int M = EXPM == EXP_SPLIT ? EXP_HW : EXPM;
+        const float x0 = fmaf(s[t][half * 8 + 2 * e], c_log2, -m_c);
+        const float x1 = fmaf(s[t][half * 8 + 2 * e + 1], c_log2, -m_c);
+        const float p0 = (EXPM == EXP_SPLIT && e == 3) ? exp2_poly(x0) : exp2_sel<M>(x0);
+        const float p1 = (EXPM == EXP_SPLIT && e == 3) ? exp2_poly(x1) : exp2_sel<M>(x1);
         la += p0;
         lb += p1;
         packed[e] = (int)pack_bf16x2(p0, p1);
@@ -353,13 +357,14 @@ template <int D>
 static hipError_t launch_fwd_d(const void* q, const void* k, const void* v, void* o, float* lse,
                                int BH, int N, bool causal, float scale, int exp_mode,
                                hipStream_t stream) {
-  const bool poly = exp_mode == EXP_POLY;
   if (causal) {
-    return poly ? launch_fwd_t<D, true, EXP_POLY>(q, k, v, o, lse, BH, N, scale, stream)
-                : launch_fwd_t<D, true, EXP_HW>(q, k, v, o, lse, BH, N, scale, stream);
+    if (exp_mode == EXP_POLY) return launch_fwd_t<D, true, EXP_POLY>(q, k, v, o, lse, BH, N, scale, stream);
+    if (exp_mode == EXP_SPLIT) return launch_fwd_t<D, true, EXP_SPLIT>(q, k, v, o, lse, BH, N, scale, stream);
+    return launch_fwd_t<D, true, EXP_HW>(q, k, v, o, lse, BH, N, scale, stream);
   }
-  return poly ? launch_fwd_t<D, false, EXP_POLY>(q, k, v, o, lse, BH, N, scale, stream)
-              : launch_fwd_t<D, false, EXP_HW>(q, k, v, o, lse, BH, N, scale, stream);
+  if (exp_mode == EXP_POLY) return launch_fwd_t<D, false, EXP_POLY>(q, k, v, o, lse, BH, N, scale, stream);
+  if (exp_mode == EXP_SPLIT) return launch_fwd_t<D, false, EXP_SPLIT>(q, k, v, o, lse, BH, N, scale, stream);
+  return launch_fwd_t<D, false, EXP_HW>(q, k, v, o, lse, BH, N, scale, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -514,6 +514,17 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
 }
 
 template <int D, bool CAUSAL>
+static hipError_t launch_attend_t(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
+                                  const uint8_t* k8, const uint8_t* v8t, const float* scales, int BH,
+                                  int N, float scale, hipStream_t stream) {
+  const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
+  const int n_qtiles = (N + kF8BM - 1) / kF8BM;
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, stream, q8,
+                     q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles, scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
 static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
                                float* partial, int BH, int N, float scale, bool rotate,
@@ -528,11 +539,7 @@ static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void
                      BH, (int)rotate, seed);
   hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(Npad / 64, BH), dim3(256), 0, stream,
                      (const bf16*)v, v8t, (const float*)partial, scales, N, Npad, BH, (int)nchunks);
-  const int n_qtiles = (N + kF8BM - 1) / kF8BM;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, stream,
-                     (const uint8_t*)q8, (const uint8_t*)q8lo, (const uint8_t*)k8, (const uint8_t*)v8t,
-                     (const float*)scales, (bf16*)o, lse, N, Npad, BH, n_qtiles, scale * kLog2e);
-  return hipGetLastError();
+  return launch_attend_t<D, CAUSAL>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -546,6 +553,18 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
   }
   return causal ? launch_fp8_t<128, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream)
                 : launch_fp8_t<128, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream);
+}
+
+hipError_t launch_fwd_fp8_attend(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
+                                 const uint8_t* k8, const uint8_t* v8t, const float* scales, int B,
+                                 int H, int N, int d, bool causal, float scale, hipStream_t stream) {
+  const int BH = B * H;
+  if (d == 64) {
+    return causal ? launch_attend_t<64, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream)
+                  : launch_attend_t<64, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+  }
+  return causal ? launch_attend_t<128, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream)
+                : launch_attend_t<128, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
 }
 
 }  // namespace fattn
