@@ -18,8 +18,10 @@
 //   4. fwd_fp8    — attention: Sᵀ = K8·(Q8 + Q8lo/16)ᵀ (two MFMAs, the second
 //                   with the block scale 2^-4) and Oᵀ += V8ᵀ·P8ᵀ on the
 //                   32x32x64 f8f6f4 MFMA; P̃ = 2^(s·c − m + 8) quantised to
-//                   e4m3 (P̃ ≤ 1 because the running max is updated whenever
-//                   it grows, so P̃·2^8 ≤ 256 < 448); O = Oᵀ·s_v/l.
+//                   e4m3 as P̃·2^(8−τ) with τ = 1: the exponent offset moves
+//                   only when a tile max exceeds it by more than τ
+//                   (FlashAttention-4 gist, technical summary 2.B), so
+//                   P̃ ≤ 2^τ and P̃·2^(8−τ) ≤ 256 < 448; O = Oᵀ·s_v/l.
 #include <type_traits>
 
 #include "fattn_device.hpp"
@@ -28,6 +30,10 @@
 namespace fattn {
 
 constexpr float kE4m3Max = 448.0f;
+// Conditional-rescale threshold of the fp8 softmax (log2 units) and the
+// matching exponent of the fixed P scale: P̃ ≤ 2^τ, stored as P̃·2^(8−τ).
+constexpr float kF8Tau = 1.0f;
+constexpr float kF8PExp = 8.0f - kF8Tau;
 constexpr int kRowSets = 4;  // rows per thread processed together in the row-wise kernels
 
 // SplitMix64: state advanced by the golden-ratio increment, then mixed.
@@ -422,8 +428,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   f32x16 s[2];
   scores(k_lds, s);
   if (first_masked == 0) mask(s, 0);
-  // The running max moves whenever it grows (τ = 0), so P̃ ≤ 1 and
-  // P̃·2^8 ≤ 256 < 448 fits e4m3.
+  // The exponent offset starts at tile 0's row max; P̃ ≤ 2^τ afterwards.
   float m_c = tile_max(s);
 
   auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
@@ -433,8 +438,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
       if (j + 2 < n_kv) gload_k(k_lds + PAR * KTILE, j + 2);
       gload_v(v_lds + (PAR ^ 1) * VTILE, j + 1);
     }
-    // P̃·2^8 in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
-    const float off = 8.0f - m_c;
+    // P̃·2^(8−τ) in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
+    const float off = kF8PExp - m_c;
     i32x8 p8;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -464,8 +469,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
     }
     if constexpr (HAS_NEXT) {
       const float mx = tile_max(ns);
-      if (__ballot(mx > m_c)) {
-        const bool resc = mx > m_c;
+      if (__ballot(mx > m_c + kF8Tau)) {
+        const bool resc = mx > m_c + kF8Tau;
         const float m_new = resc ? mx : m_c;
         const float alpha = resc ? exp2_hw(m_c - m_new) : 1.0f;
 #pragma unroll
@@ -509,7 +514,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
         *(i32x2*)(Orow + 32 * dt + 8 * g + 4 * h) = w;
       }
     if (LSE != nullptr && h == 0)
-      LSE[(size_t)bh * N + qi] = (m_c + __builtin_log2f(l) - 8.0f) * kLn2;
+      LSE[(size_t)bh * N + qi] = (m_c + __builtin_log2f(l) - kF8PExp) * kLn2;
   }
 }
 
