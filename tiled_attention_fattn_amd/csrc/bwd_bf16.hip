@@ -435,45 +435,66 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const char* kt = k_lds + PAR * TILE;
     const char* vt = v_lds + PAR * TILE;
     const int key0 = j * kDqBN;
-    bf16x8 dsb[4];
+    // Program-order pieces with LDS operand reads kLeadB MFMAs ahead: Sᵀ, dPᵀ
+    // of keys 0..31, their dS; Sᵀ, dPᵀ of keys 32..63, their dS; then dQᵀ.
+    // (Two waves share each SIMD: the other wave's MFMAs cover this wave's
+    // dS steps, which keeps only one key half's scores live.)
+    constexpr int NR = 4 * KD;  // piece i: key half t = i/(2KD), kk = (i/2)%KD, S or dP by i%2
+    auto sread = [&](int i) __device__ {
+      const int t = i / (2 * KD), kk = (i / 2) % KD;
+      return *(const bf16x8*)((i % 2 ? vt : kt) + t * 32 * RB + koff[kk]);
+    };
+    // dS of one element pair (registers 2x, 2x+1 of key half t), packed.
+    i32x4 dw[4];
+    auto ds_step = [&](const f32x16& sv, const f32x16& dpv, int t, int x) __device__ {
+      float ds[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int r = 2 * x + b;
+        float p = exp2_hw(fmaf(sv[r], c_log2, -l2));
+        if (MASKED) {
+          const int key = key0 + t * 32 + acc_row(r, h);
+          if (key >= N || (CAUSAL && key > qi)) p = 0.0f;
+        }
+        ds[b] = p * (dpv[r] - dq_d);
+      }
+      dw[2 * t + x / 4][x % 4] = (int)pack_bf16x2(ds[0], ds[1]);
+    };
+    bf16x8 ra[NR];
+#pragma unroll
+    for (int i = 0; i < kLeadB; ++i) ra[i] = sread(i);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      f32x16 sv = {}, dpv = {};
+      f32x16 sd[2];  // S, dP of key half t
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        sv = mfma32(*(const bf16x8*)(kt + t * 32 * RB + koff[kk]), qr[kk], sv);
-        dpv = mfma32(*(const bf16x8*)(vt + t * 32 * RB + koff[kk]), dor[kk], dpv);
+      for (int i = 2 * KD * t; i < 2 * KD * (t + 1); ++i) {
+        const int kk = (i / 2) % KD, w = i % 2;
+        sd[w] = mfma32(ra[i], w ? dor[kk] : qr[kk], kk == 0 ? f32x16{} : sd[w]);
+        if (i + kLeadB < NR) ra[i + kLeadB] = sread(i + kLeadB);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        i32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float ds[2];
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const int r = half * 8 + 2 * e + b;
-            float p = exp2_hw(fmaf(sv[r], c_log2, -l2));
-            if (MASKED) {
-              const int key = key0 + t * 32 + acc_row(r, h);
-              if (key >= N || (CAUSAL && key > qi)) p = 0.0f;
-            }
-            ds[b] = p * (dpv[r] - dq_d);
-          }
-          w[e] = (int)pack_bf16x2(ds[0], ds[1]);
-        }
-        dsb[2 * t + half] = __builtin_bit_cast(bf16x8, w);
-      }
+      for (int x = 0; x < 8; ++x) ds_step(sd[0], sd[1], t, x);
     }
     // dQᵀ += Kᵀ·dSᵀ: Kᵀ operands by transpose reads of the K tile.
+    constexpr int NT = 4 * DT;  // piece i: step ks = i/DT, d tile i%DT
+    bf16x4 ta[NT][2];
+    auto tread = [&](int i) __device__ {
+      const char* base = kt + 16 * (i / DT) * RB;
+      ta[i][0] = lds_read_tr16(base + toff[0][i % DT]);
+      ta[i][1] = lds_read_tr16(base + toff[1][i % DT]);
+    };
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int i = 0; i < kLeadB; ++i) tread(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 lo = lds_read_tr16(kt + 16 * ks * RB + toff[0][dt]);
-        const bf16x4 hi = lds_read_tr16(kt + 16 * ks * RB + toff[1][dt]);
-        dq[dt] = mfma32(concat(lo, hi), dsb[ks], dq[dt]);
-      }
+    for (int i = 0; i < NT; ++i) {
+      const int ks = i / DT, dt = i % DT;
+      dq[dt] = mfma32(concat(ta[i][0], ta[i][1]), __builtin_bit_cast(bf16x8, dw[ks]), dq[dt]);
+      if (i + kLeadB < NT) tread(i + kLeadB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     wait_vmem();
     __syncthreads();
   };

@@ -2,7 +2,7 @@
 //
 // What is computed (FlashAttention-4 news page, "Por qué el enfoque estándar
 // ya no funciona"; FlashAttention-3 page, "FlashAttention y FlashAttention-2"):
-// O = softmax(scale·Q·Kᵀ [causal]) · V, one workgroup per 256 query rows of
+// O = softmax(scale·Q·Kᵀ [causal]) · V, one workgroup per block of query rows of
 // one head; K and V stream through LDS in 64-key tiles; the scores and the
 // probabilities never leave the compute unit.
 //
@@ -101,7 +101,7 @@ __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c_log2,
 }
 
 template <int D, bool CAUSAL, int EXPM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
                      int N, int BH, int n_qtiles, float c_log2) {
@@ -346,7 +346,7 @@ template <int D, bool CAUSAL, int EXPM>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                int BH, int N, float scale, hipStream_t stream) {
   const int n_qtiles = (N + kFwdBM - 1) / kFwdBM;
-  const dim3 grid(n_qtiles * BH), block(256);
+  const dim3 grid(n_qtiles * BH), block(64 * kFwdWaves);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXPM>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, BH, n_qtiles,
                      scale * kLog2e);
