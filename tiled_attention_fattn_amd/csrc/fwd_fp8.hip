@@ -34,7 +34,7 @@ constexpr float kE4m3Max = 448.0f;
 // matching exponent of the fixed P scale: P̃ ≤ 2^τ, stored as P̃·2^(8−τ).
 constexpr float kF8Tau = 1.0f;
 constexpr float kF8PExp = 8.0f - kF8Tau;
-constexpr int kRowSets = 4;  // rows per thread processed together in the row-wise kernels
+constexpr int kRowSets = 2;  // rows per thread processed together in the row-wise kernels
 
 // SplitMix64: state advanced by the golden-ratio increment, then mixed.
 __device__ __forceinline__ float rotation_sign(uint64_t seed, int i) {
@@ -45,47 +45,72 @@ __device__ __forceinline__ float rotation_sign(uint64_t seed, int i) {
   return (z >> 63) ? -1.0f : 1.0f;
 }
 
-// Unnormalised Walsh–Hadamard transform of one row held by LPR lanes with 8
-// consecutive elements each (element index = lane_in_row·8 + e).
+// Row-wise work of the prep kernels: a row of D elements is held by
+// kLpr = D/32 consecutive lanes (a quad for D = 128), kEpl = 32 consecutive
+// elements each (element index = lane_in_row·32 + e).
+constexpr int kEpl = 32;
+
+// x ↦ the value of the lane whose index differs in bit 0 (dpp = 0xB1) or
+// bit 1 (dpp = 0x4E) within each quad (DPP quad_perm; no LDS traffic).
+template <int DPP>
+__device__ __forceinline__ float quad_xor(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), DPP, 0xF, 0xF, false));
+}
+
+// Unnormalised Walsh–Hadamard transform (Sylvester order) of one row: five
+// butterfly stages inside each lane's 32 elements, then one stage per lane
+// bit across the quad. In every butterfly the lower index takes a + b and
+// the upper a − b.
 template <int LPR>
-__device__ __forceinline__ void fwht_row(float (&x)[8], int lane_in_row) {
+__device__ __forceinline__ void fwht_row(float (&x)[kEpl], int lane_in_row) {
 #pragma unroll
-  for (int w = 1; w < 8; w <<= 1)
+  for (int w = 1; w < kEpl; w <<= 1)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < kEpl; ++e)
       if (!(e & w)) {
         const float a = x[e], b = x[e + w];
         x[e] = a + b;
         x[e + w] = a - b;
       }
+  if constexpr (LPR >= 2) {
+    const bool upper = lane_in_row & 1;
 #pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) {
-    const bool upper = lane_in_row & m;
+    for (int e = 0; e < kEpl; ++e) {
+      const float y = quad_xor<0xB1>(x[e]);
+      x[e] = upper ? (y - x[e]) : (x[e] + y);
+    }
+  }
+  if constexpr (LPR >= 4) {
+    const bool upper = lane_in_row & 2;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float y = __shfl_xor(x[e], m, LPR);
+    for (int e = 0; e < kEpl; ++e) {
+      const float y = quad_xor<0x4E>(x[e]);
       x[e] = upper ? (y - x[e]) : (x[e] + y);
     }
   }
 }
 
-// Loads the 8 values of (row, part), rotated when `rot`; false if row >= N.
+// Loads the 32 values of (row, part), rotated when `rot`; false if row >= N.
+// Every lane of a row must call it (the rotation exchanges values).
 template <int D>
 __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, int part, bool rot,
-                                              const float* sgn, float (&x)[8]) {
-  constexpr int LPR = D / 8;
+                                              const float* sgn, float (&x)[kEpl]) {
+  constexpr int LPR = D / kEpl;
   const bool ok = row < N;
-  bf16x8 v = {};
-  if (ok) v = *(const bf16x8*)(src + (size_t)row * D + part * 8);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+  for (int c = 0; c < kEpl / 8; ++c) {
+    bf16x8 v = {};
+    if (ok) v = *(const bf16x8*)(src + (size_t)row * D + part * kEpl + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[c * 8 + e] = (float)v[e];
+  }
   if (rot) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= sgn[part * 8 + e];
+    for (int e = 0; e < kEpl; ++e) x[e] *= sgn[part * kEpl + e];
     fwht_row<LPR>(x, part);
     const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= inv_sqrt_d;
+    for (int e = 0; e < kEpl; ++e) x[e] *= inv_sqrt_d;
   }
   return ok;
 }
@@ -97,7 +122,7 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ 
                                                       const bf16* __restrict__ V,
                                                       float* __restrict__ partial, int N, int BH,
                                                       int rotate, uint64_t seed) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  constexpr int LPR = D / kEpl, RPB = 256 / LPR;
   __shared__ float sgn[D];
   __shared__ float wmax[4];
   const int t = blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
@@ -111,14 +136,14 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ 
   // flight together.
   const int r_end = min(N, (chunk + 1) * kFp8AmaxRows);
   for (int r0 = chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
-    float x[kRowSets][8];
+    float x[kRowSets][kEpl];
 #pragma unroll
     for (int u = 0; u < kRowSets; ++u)
       load_row_part<D>(src, r0 + u * RPB + threadIdx.x / LPR, r_end, part, rot, sgn, x[u]);
 #pragma unroll
     for (int u = 0; u < kRowSets; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[u][e]));
+      for (int e = 0; e < kEpl; ++e) m = fmaxf(m, fabsf(x[u][e]));
   }
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
@@ -181,7 +206,7 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restric
                                                           const float* __restrict__ partial,
                                                           float* __restrict__ scales, int N, int BH,
                                                           int rotate, uint64_t seed) {
-  constexpr int LPR = D / 8, RPB = 256 / LPR;
+  constexpr int LPR = D / kEpl, RPB = 256 / LPR;
   __shared__ float sgn[D];
   __shared__ float am_slot;
   const int t = blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
@@ -195,7 +220,7 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restric
   const int part = threadIdx.x % LPR;
   const int r_end = min(N, (chunk + 1) * kFp8AmaxRows);
   for (int r0 = chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
-    float xs[kRowSets][8];
+    float xs[kRowSets][kEpl];
     bool ok[kRowSets];
 #pragma unroll
     for (int u = 0; u < kRowSets; ++u)
@@ -205,26 +230,33 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restric
     for (int u = 0; u < kRowSets; ++u) {
       if (!ok[u]) continue;
       const int row = r0 + u * RPB + threadIdx.x / LPR;
-      const float (&x)[8] = xs[u];
-      float tt[8];
+      const size_t off = (size_t)row * D + part * kEpl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tt[e] = am > 0.0f ? clamp448(ratio448(x[e], am)) : x[e];
-      i32x2 w;
-      w[0] = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
-      w[1] = cvt_fp8x4(tt[4], tt[5], tt[6], tt[7]);
-      *(i32x2*)(dst + (size_t)row * D + part * 8) = w;
-      if (t == 0) {
-        // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
-        float dec[8];
-        dec_fp8x4(w[0], dec);
-        dec_fp8x4(w[1], dec + 4);
-        float r[8];
+      for (int c = 0; c < kEpl / 16; ++c) {  // 16 elements → one 16-byte store of codes
+        float tt[16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = 16.0f * (tt[e] - dec[e]);
-        i32x2 wl;
-        wl[0] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
-        wl[1] = cvt_fp8x4(r[4], r[5], r[6], r[7]);
-        *(i32x2*)(q8lo + head + (size_t)row * D + part * 8) = wl;
+        for (int e = 0; e < 16; ++e) {
+          const float x = xs[u][16 * c + e];
+          tt[e] = am > 0.0f ? clamp448(ratio448(x, am)) : x;
+        }
+        i32x4 w;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          w[g] = cvt_fp8x4(tt[4 * g], tt[4 * g + 1], tt[4 * g + 2], tt[4 * g + 3]);
+        *(i32x4*)(dst + off + 16 * c) = w;
+        if (t == 0) {
+          // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
+          i32x4 wl;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float dec[4], r[4];
+            dec_fp8x4(w[g], dec);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = 16.0f * (tt[4 * g + e] - dec[e]);
+            wl[g] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
+          }
+          *(i32x4*)(q8lo + head + off + 16 * c) = wl;
+        }
       }
     }
   }
