@@ -177,11 +177,6 @@ __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
-// Two e4m3 codes in the low 16 bits.
-__device__ __forceinline__ int cvt_fp8x2(float a, float b) {
-  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-}
-
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -kE4m3Max), kE4m3Max); }
 
 // Decode the four e4m3 codes of a packed word (lowest byte first).
@@ -194,7 +189,21 @@ __device__ __forceinline__ void dec_fp8x4(int w, float* out) {
 
 // x·448/amax with one correctly rounded division (x·448 is exact for bf16 x),
 // so exact e4m3 midpoints stay exact.
-__device__ __forceinline__ float ratio448(float x, float am) { return __fdiv_rn(x * kE4m3Max, am); }
+//
+// The quotient is formed by multiplying with the correctly rounded reciprocal
+// of amax and one FMA correction from the exact remainder (Markstein's
+// division step), which yields the correctly rounded fp32 quotient for
+// normal operands at a quarter of the cost of a general division.
+struct Ratio448 {
+  float am, inv;
+  __device__ explicit Ratio448(float a) : am(a), inv(a > 0.0f ? __frcp_rn(a) : 0.0f) {}
+};
+__device__ __forceinline__ float ratio448(float x, const Ratio448& r) {
+  const float a = x * kE4m3Max;          // exact: 8 significant bits times 7·2^6
+  const float q0 = a * r.inv;
+  const float e = fmaf(-q0, r.am, a);    // exact remainder a − q0·amax
+  return fmaf(e, r.inv, q0);
+}
 
 // grid (row chunks, BH, 2 tensors): kFp8AmaxRows rows per block.
 template <int D>
@@ -213,6 +222,7 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restric
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
   const int nchunks = gridDim.x;
   const float am = head_amax(partial + ((size_t)t * BH + bh) * nchunks, nchunks, &am_slot);
+  const Ratio448 rq(am);
   const size_t head = (size_t)bh * N * D;
   const bf16* src = (t == 0 ? Q : K) + head;
   uint8_t* dst = (t == 0 ? q8 : k8) + head;
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restric
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float x = xs[u][16 * c + e];
-          tt[e] = am > 0.0f ? clamp448(ratio448(x, am)) : x;
+          tt[e] = am > 0.0f ? clamp448(ratio448(x, rq)) : x;
         }
         i32x4 w;
 #pragma unroll
@@ -268,7 +278,11 @@ __device__ __forceinline__ int v8_pos(int r) {
   return 32 * ((r >> 2) & 1) + s;
 }
 
-// grid (Npad/64, BH): one 64-key block of one head, transposed through LDS.
+// grid (Npad/64, BH): one 64-key block of one head. Thread (m, cc) reads the
+// 8 values of d-chunk cc of keys 4m .. 4m+3 and writes, for each of those 8
+// d, the 4 codes of the 4 keys as one 4-byte word: the four keys are
+// adjacent in the P-operand key order (v8_pos), and the 16 threads of one
+// chunk fill 64 contiguous bytes of each V8ᵀ row. Keys past N give code 0.
 template <int D>
 __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict__ V,
                                                          uint8_t* __restrict__ v8t,
@@ -276,35 +290,31 @@ __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict
                                                          float* __restrict__ scales, int N,
                                                          int Npad, int BH, int nchunks) {
   constexpr int CHUNKS = D / 8;
-  constexpr int CPT = 64 * CHUNKS / 256;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[D * 64];
   const int bh = blockIdx.y, kb = blockIdx.x;
   __shared__ float am_slot;
   const float am = head_amax(partial + ((size_t)2 * BH + bh) * nchunks, nchunks, &am_slot);
+  const Ratio448 rv(am);
   if (kb == 0 && threadIdx.x == 0) scales[2 * BH + bh] = scale_from_amax(am);
   const bf16* src = V + (size_t)bh * N * D;
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int ch = threadIdx.x + i * 256;
-    const int r = ch / CHUNKS, cc = ch % CHUNKS;
-    const int key = kb * 64 + r;
-    bf16x8 v = {};
-    if (key < N) v = *(const bf16x8*)(src + (size_t)key * D + cc * 8);
-    const int p = v8_pos(r);
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float a = (float)v[e], b = (float)v[e + 1];
-      const int w = am > 0.0f ? cvt_fp8x2(clamp448(ratio448(a, am)), clamp448(ratio448(b, am)))
-                              : cvt_fp8x2(a, b);
-      tile[(cc * 8 + e) * 64 + p] = (uint8_t)(w & 0xff);
-      tile[(cc * 8 + e + 1) * 64 + p] = (uint8_t)((w >> 8) & 0xff);
-    }
-  }
-  __syncthreads();
   uint8_t* dst = v8t + (size_t)bh * D * Npad + (size_t)kb * 64;
-  for (int ch = threadIdx.x; ch < D * 4; ch += 256) {
-    const int d = ch >> 2, part = ch & 3;
-    *(i32x4*)(dst + (size_t)d * Npad + part * 16) = *(const i32x4*)(tile + d * 64 + part * 16);
+  for (int ch = threadIdx.x; ch < 16 * CHUNKS; ch += 256) {
+    const int m = ch % 16, cc = ch / 16;
+    float x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key = kb * 64 + 4 * m + u;
+      bf16x8 v = {};
+      if (key < N) v = *(const bf16x8*)(src + (size_t)key * D + cc * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = (float)v[e];
+        x[u][e] = am > 0.0f ? clamp448(ratio448(a, rv)) : a;
+      }
+    }
+    const int p = v8_pos(4 * m);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *(int*)(dst + (size_t)(cc * 8 + e) * Npad + p) = cvt_fp8x4(x[0][e], x[1][e], x[2][e], x[3][e]);
   }
 }
 
