@@ -21,7 +21,9 @@
 //                   e4m3 as P̃·2^(8−τ) with τ = 1: the exponent offset moves
 //                   only when a tile max exceeds it by more than τ
 //                   (FlashAttention-4 gist, technical summary 2.B), so
-//                   P̃ ≤ 2^τ and P̃·2^(8−τ) ≤ 256 < 448; O = Oᵀ·s_v/l.
+//                   P̃ ≤ 2^τ and P̃·2^(8−τ) ≤ 256 < 448; O = Oᵀ·s_v/l with
+//                   l the sum of the quantised P̃ (formed by one more MFMA);
+//                   the optional LSE uses the fp32 sum before quantisation.
 #include <type_traits>
 
 #include "fattn_device.hpp"
@@ -330,7 +332,7 @@ constexpr int kF8Waves = 4;
 constexpr int kF8BM = 32 * kF8Waves;
 constexpr int kF8BN = 64;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WANT_LSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ q8lo,
                     const uint8_t* __restrict__ k8,
@@ -428,6 +430,15 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  // Row sums: the normalisation of O uses the sum of the quantised P̃·2^(8−τ)
+  // that enter the PV product, formed by the MFMA itself with an A operand of
+  // e4m3 ones (every accumulator register of lane c then holds the sum for
+  // query c), so numerator and denominator see the same probabilities. The
+  // LSE, when requested, uses the fp32 sum of P̃ before quantisation.
+  f32x16 lacc = {};
+  i32x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;  // e4m3 1.0 in every byte
   float l_part = 0.0f;
 
   auto scores = [&](const char* kt, f32x16 (&s)[2]) {
@@ -491,7 +502,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           pv4[e] = exp2_hw(fmaf(s[t][4 * wd + e], c_log2, off));
-          l_part += pv4[e];
+          if constexpr (WANT_LSE) l_part += pv4[e];
         }
         p8[4 * t + wd] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
       }
@@ -509,6 +520,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
       const i32x4 a1 = *(const i32x4*)(vt + dt * 32 * 64 + voff[1]);
       oacc[dt] = mfma32_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8, oacc[dt]);
     }
+    lacc = mfma32_fp8(ones, p8, lacc);
     if constexpr (HAS_NEXT) {
       const float mx = tile_max(ns);
       if (__ballot(mx > m_c + kF8Tau)) {
@@ -519,6 +531,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+        lacc[0] *= alpha;  // only register 0 of the row-sum accumulator is read
         l_part *= alpha;
         m_c = m_new;
       }
@@ -542,8 +555,7 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
     iteration(j, I0{}, std::false_type{});
   }
 
-  const float l = half_sum(l_part);
-  const float inv = sv / l;
+  const float inv = sv / lacc[0];
   if (qi < N) {
     bf16* Orow = O + head + (size_t)qi * D;
 #pragma unroll
@@ -555,8 +567,10 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
         w[1] = (int)pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
         *(i32x2*)(Orow + 32 * dt + 8 * g + 4 * h) = w;
       }
-    if (LSE != nullptr && h == 0)
-      LSE[(size_t)bh * N + qi] = (m_c + __builtin_log2f(l) - kF8PExp) * kLn2;
+    if constexpr (WANT_LSE) {
+      const float l = half_sum(l_part);
+      if (h == 0) LSE[(size_t)bh * N + qi] = (m_c + __builtin_log2f(l) - kF8PExp) * kLn2;
+    }
   }
 }
 
@@ -566,8 +580,14 @@ static hipError_t launch_attend_t(void* o, float* lse, const uint8_t* q8, const 
                                   int N, float scale, hipStream_t stream) {
   const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
   const int n_qtiles = (N + kF8BM - 1) / kF8BM;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(n_qtiles * BH), dim3(256), 0, stream, q8,
-                     q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles, scale * kLog2e);
+  if (lse != nullptr)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true>), dim3(n_qtiles * BH), dim3(256), 0, stream,
+                       q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
+                       scale * kLog2e);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false>), dim3(n_qtiles * BH), dim3(256), 0, stream,
+                       q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
+                       scale * kLog2e);
   return hipGetLastError();
 }
 
