@@ -210,20 +210,26 @@ def main():
                    "ms_min": round(float(np.min(samples[p])), 4),
                    "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
 
-    # The C3 forward is also reported with each exp2 variant.
+    # The C3 forward is also reported with each exp2 variant. The variants are
+    # timed in interleaved rounds (order reversed every other round) so that
+    # clock drift over the run does not favour whichever variant runs last.
     if "fwd" in parts and not args.no_exp_variants:
-        variants = {}
-        for mode in ("hw", "poly", "split"):
-            for _ in range(3):
+        modes = ("hw", "poly", "split")
+        for mode in modes:
+            for _ in range(2):
                 launch["fwd"](mode)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(10):
-                launch["fwd"](mode)
-            b.record()
-            torch.cuda.synchronize()
-            variants[mode] = round(flops["fwd"] / (a.elapsed_time(b) / 10 * 1e-3) / 1e12, 1)
-        info["fwd"]["tflops_by_exp2"] = variants
+        times = {m: [] for m in modes}
+        for r in range(6):
+            for mode in (modes if r % 2 == 0 else modes[::-1]):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(4):
+                    launch["fwd"](mode)
+                b.record()
+                torch.cuda.synchronize()
+                times[mode].append(a.elapsed_time(b) / 4)
+        info["fwd"]["tflops_by_exp2"] = {
+            m: round(flops["fwd"] / (float(np.median(t)) * 1e-3) / 1e12, 1) for m, t in times.items()}
 
     # The roofline is reported for the step's longest single kernel: the C3
     # forward is one launch of one kernel (the bwd and fp8 parts are several
