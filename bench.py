@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-exp-variants", action="store_true",
                     help="skip the separate hw/poly/split exp2 timing of the forward")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the sequence-length / head-dimension sweep: N = 4096 to "
+                         "32768 at a fixed B*H*N = 262144 tokens, d = 64 and 128")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device-to-device copy of this many bytes "
                          "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -157,6 +160,86 @@ def cpu_baseline(parts, heads):
                       f"float64 numpy, {secs:.1f} s"}
 
 
+SWEEP_TOKENS = 262144   # B·H·N per point (that of the B=2 H=16 N=8192 forward)
+SWEEP_N = (4096, 8192, 16384, 32768)
+
+
+def sweep(args):
+    """Throughput over sequence length and head dimension at a fixed token count.
+
+    For each N and d, B·H = 262144 / N heads (B = 1) of seeded N(0,1) inputs
+    rounded to bf16; forward non-causal and causal, backward causal, and the
+    fp8 attention step (non-causal, on operands quantised with the rotation).
+    Prints one JSON line with every point.
+    """
+    import torch
+    import tiled_attention_fattn_amd as fa
+    from tiled_attention_fattn_amd.inputs import flops_bwd, flops_fwd
+    torch.cuda.set_device(0)
+    reps, warm = 10, 3
+    points = []
+
+    def timed(fn):
+        for _ in range(warm):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    # Bring the shader clock up before the first point (a few calls are not
+    # enough for the first configuration measured).
+    g = torch.Generator(device="cuda").manual_seed(999)
+    x = torch.randn(1, 64, 4096, 128, device="cuda", generator=g).to(torch.bfloat16)
+    for _ in range(300):
+        fa.fwd(x, x, x)
+    torch.cuda.synchronize()
+    del x
+
+    for d in (128, 64):
+        for N in SWEEP_N:
+            H = SWEEP_TOKENS // N
+            g = torch.Generator(device="cuda").manual_seed(1000 + N + d)
+            q, k, v, do = (torch.randn(1, H, N, d, device="cuda", generator=g).to(torch.bfloat16)
+                           for _ in range(4))
+            scale = d ** -0.5
+            o = torch.empty_like(q)
+            lse = torch.empty((1, H, N), dtype=torch.float32, device="cuda")
+            for causal in (False, True):
+                ms = timed(lambda: fa.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse))
+                tf = flops_fwd(1, H, N, d, causal) / (ms * 1e-3) / 1e12
+                points.append({"part": "fwd", "causal": causal, "B": 1, "H": H, "N": N, "d": d,
+                               "ms": round(ms, 4), "tflops": round(tf, 1),
+                               "frac_of_peak": round(tf / PEAK_BF16, 4)})
+            # The backward consumes the causal forward's O and LSE (left in o, lse).
+            grads = tuple(torch.empty_like(q) for _ in range(3))
+            ws = torch.empty(fa.bwd_workspace_bytes(1, H, N, d), dtype=torch.uint8, device="cuda")
+            ms = timed(lambda: fa.bwd(q, k, v, o, lse, do, causal=True, scale=scale,
+                                      workspace=ws, out=grads))
+            tf = flops_bwd(1, H, N, d, True) / (ms * 1e-3) / 1e12
+            points.append({"part": "bwd", "causal": True, "B": 1, "H": H, "N": N, "d": d,
+                           "ms": round(ms, 4), "tflops": round(tf, 1),
+                           "frac_of_peak": round(tf / PEAK_BF16, 4)})
+            del grads, ws
+            ws8 = torch.empty(fa.fp8_workspace_bytes(1, H, N, d), dtype=torch.uint8, device="cuda")
+            fa.fwd_fp8(q, k, v, scale=scale, rotate=True, seed=N, want_lse=False, workspace=ws8,
+                       out=o)
+            ms = timed(lambda: fa.fwd_fp8_attend(ws8, 1, H, N, d, scale=scale, want_lse=False,
+                                                 out=o))
+            tf = flops_fwd(1, H, N, d, False) / (ms * 1e-3) / 1e12
+            points.append({"part": "fp8_attend", "causal": False, "B": 1, "H": H, "N": N, "d": d,
+                           "ms": round(ms, 4), "tflops": round(tf, 1),
+                           "frac_of_peak": round(tf / PEAK_FP8, 4)})
+            print(f"[sweep] d={d} N={N} done", file=sys.stderr, flush=True)
+            del q, k, v, do, o, lse, ws8
+    print(json.dumps({"sweep": "tokens per point B*H*N = %d, B = 1" % SWEEP_TOKENS,
+                      "data": "synthetic: seeded N(0,1) rounded to bf16", "reps": reps,
+                      "warmup": warm, "points": points}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -165,6 +248,9 @@ def main():
         sys.exit(2)
     if args.copy_bytes:
         copy_calibration(args.copy_bytes, max(1, args.steps))
+        return
+    if args.sweep:
+        sweep(args)
         return
     import torch
     import tiled_attention_fattn_amd as fa

@@ -1,0 +1,108 @@
+"""GPU parity at long sequences (N = 16384 to 32768) and both head dimensions.
+
+The long-sequence points of the throughput sweep: the forward at N = 32768
+(and a ragged N = 32731) on sampled rows against the float64 oracle, the
+causal backward at N = 16384 against the full float64 gradients of one head,
+and the fp8 forward at N = 32768 on sampled rows against exact attention
+(without outliers) or against the operand-quantised model (with them).
+Inputs are the seeded N(0,1) draws rounded to bf16 (seed ids 60 and up).
+"""
+import numpy as np
+import pytest
+
+from oracle.attention import attention_backward, attention_forward_rows
+from tests.parity import (FP8_REL_RMS, assert_bf16_close, assert_lse_close, rel_rms,
+                          to_np)
+from tiled_attention_fattn_amd.inputs import gen_workload, to_device_bf16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _rows(N, seed):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, N // 2, N - 129, N - 65, N - 64, N - 2, N - 1]
+    return np.unique(np.concatenate([fixed, rng.integers(0, N, 36)]))
+
+
+@pytest.mark.parametrize("k,d,causal,N", [(60, 128, False, 32768), (61, 128, True, 32768),
+                                          (62, 64, False, 32731), (63, 64, True, 32768)])
+def test_fwd_long_sequence_sampled(k, d, causal, N):
+    import tiled_attention_fattn_amd as fa
+    shape = (1, 2, N, d)
+    inp = gen_workload(k, shape=shape, names=("q", "k", "v"))
+    q, kk, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    scale = d ** -0.5
+    print(f"[long fwd] seed={k} shape={shape} causal={causal}", flush=True)
+    o, lse = fa.fwd(q, kk, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rows = _rows(N, k)
+    idx = torch.as_tensor(rows, device=o.device)
+    for h in range(2):
+        ref_o, ref_lse = attention_forward_rows(inp["q"][0], inp["k"][0], inp["v"][0], causal,
+                                                scale, 0, h, rows)
+        assert_bf16_close(to_np(o[0, h][idx]), ref_o, f"O N={N} d={d} causal={causal} h={h}")
+        assert_lse_close(to_np(lse[0, h][idx]), ref_lse, f"LSE N={N} d={d} h={h}")
+
+
+@pytest.mark.parametrize("k,d", [(64, 64), (65, 128)])
+def test_bwd_long_sequence_one_head(k, d):
+    import tiled_attention_fattn_amd as fa
+    N = 16384
+    shape = (1, 1, N, d)
+    inp = gen_workload(k, shape=shape, names=("q", "k", "v", "do"))
+    q, kk, v, do = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v", "do"))
+    scale = d ** -0.5
+    print(f"[long bwd] seed={k} shape={shape} causal=True", flush=True)
+    o, lse = fa.fwd(q, kk, v, causal=True, scale=scale)
+    grads = fa.bwd(q, kk, v, o, lse, do, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ref = attention_backward(inp["q"][0], inp["k"][0], inp["v"][0], inp["do"][0], True, scale)
+    for name, got, r in zip(("dQ", "dK", "dV"), grads, ref[:3]):
+        assert_bf16_close(to_np(got), r, f"{name} N={N} d={d}")
+
+
+@pytest.mark.parametrize("outliers", [False, True])
+def test_fp8_long_sequence_sampled(outliers):
+    # Without outliers the output is held to the fp8 bound against exact
+    # attention. With the 0.1% x20 outliers of the fp8 workload, per-head e4m3
+    # operands alone already put the exact-arithmetic model about 6.4% from
+    # exact attention at this length (more rows, larger per-head amax), so
+    # there the kernel is compared with that model on the same rows: what is
+    # left is the kernel's own error (P in e4m3, fp32 accumulation), held to
+    # 4e-2 against the 2.5% the quantisation of P contributes on its own.
+    import tiled_attention_fattn_amd as fa
+    from oracle.fp8_model import (dequantize, dequantize_split, quantize_per_head,
+                                  quantize_per_head_split)
+    from oracle.hadamard import rotate
+    N, d, k = 32768, 128, 66 + int(outliers)
+    shape = (1, 2, N, d)
+    kw = dict(outlier_frac=0.001, outlier_factor=20.0) if outliers else {}
+    inp = gen_workload(k, shape=shape, names=("q", "k", "v"), **kw)
+    q, kk, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    scale = d ** -0.5
+    print(f"[long fp8] seed={k} shape={shape} outliers={outliers}", flush=True)
+    o, _ = fa.fwd_fp8(q, kk, v, scale=scale, rotate=True, seed=k, want_lse=False)
+    torch.cuda.synchronize()
+    rows = _rows(N, k)
+    idx = torch.as_tensor(rows, device=o.device)
+    if outliers:
+        q8, q8lo, sq = quantize_per_head_split(rotate(inp["q"][0], k))
+        k8, sk = quantize_per_head(rotate(inp["k"][0], k))
+        v8, sv = quantize_per_head(inp["v"][0])
+        model = (dequantize_split(q8, q8lo, sq), dequantize(k8, sk), dequantize(v8, sv))
+    for h in range(2):
+        got = to_np(o[0, h][idx])
+        assert np.all(np.isfinite(got))
+        ref_o, _ = attention_forward_rows(inp["q"][0], inp["k"][0], inp["v"][0], False, scale,
+                                          0, h, rows)
+        err = rel_rms(got, ref_o)
+        print(f"[long fp8] h={h} rel-RMS vs exact {err:.4e}", flush=True)
+        if not outliers:
+            assert err <= FP8_REL_RMS, f"fp8 N={N} h={h}: rel-RMS {err:.3e}"
+        else:
+            mod_o, _ = attention_forward_rows(*model, False, scale, 0, h, rows)
+            em = rel_rms(got, mod_o)
+            print(f"[long fp8] h={h} rel-RMS vs operand-quantised model {em:.4e}", flush=True)
+            assert em <= 4e-2, f"fp8 N={N} h={h}: rel-RMS vs model {em:.3e}"
