@@ -116,10 +116,10 @@ def setup_part(part, torch, fa):
     o2 = torch.empty_like(t["q"])
     ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
 
-    def run(mode="full"):
+    def run(mode="full", exp_mode="auto"):
         if mode == "attend":  # the attention step alone on the operands of the last full call
             return fa.fwd_fp8_attend(ws, B, H, N, d, causal=w["causal"], scale=scale,
-                                     want_lse=False, out=o2)
+                                     want_lse=False, out=o2, exp_mode=exp_mode)
         return fa.fwd_fp8(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
                           rotate=w["rotate"], seed=k, want_lse=False, workspace=ws, out=o)
     return run
@@ -329,7 +329,8 @@ def main():
                 "peak": dom_peak, "unit": "TFLOP/s", "frac": round(achieved / dom_peak, 4),
                 "traffic": committed_traffic(dom)}
 
-    # The fp8 attention step alone (after the quantisation the timed calls did).
+    # The fp8 attention step alone (after the quantisation the timed calls did),
+    # with the default exp2 and, in interleaved rounds, with each variant.
     if "fp8" in parts:
         for _ in range(3):
             launch["fp8"]("attend")
@@ -343,6 +344,21 @@ def main():
         atf = flops["fp8"] / (ams * 1e-3) / 1e12
         info["fp8"]["attention_only"] = {"ms": round(ams, 4), "tflops": round(atf, 1),
                                          "frac_of_peak": round(atf / PEAK_FP8, 4)}
+        if not args.no_exp_variants:
+            modes = ("hw", "poly", "split")
+            times = {m: [] for m in modes}
+            for r in range(6):
+                for mode in (modes if r % 2 == 0 else modes[::-1]):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for _ in range(4):
+                        launch["fp8"]("attend", mode)
+                    b.record()
+                    torch.cuda.synchronize()
+                    times[mode].append(a.elapsed_time(b) / 4)
+            info["fp8"]["attention_only"]["tflops_by_exp2"] = {
+                m: round(flops["fp8"] / (float(np.median(t)) * 1e-3) / 1e12, 1)
+                for m, t in times.items()}
     clocks = gpu_clocks()
     if clocks_before or clocks:
         info["gpu_clock_mhz"] = {"before": clocks_before, "after": clocks}

@@ -57,9 +57,10 @@ typedef enum {
   FATTN_EDEVICE = 5      /* the current device is not gfx950 */
 } fattn_status;
 
-/* Which exp2 the softmax uses (forward kernels). */
+/* Which exp2 the softmax uses (the bf16 and fp8 forward kernels). */
 typedef enum {
-  FATTN_EXP_AUTO = 0,    /* the variant measured fastest on gfx950 (hardware) */
+  FATTN_EXP_AUTO = 0,    /* the variant measured fastest on gfx950: hardware,
+                            for both forwards and both head dimensions */
   FATTN_EXP_HW = 1,      /* v_exp_f32 on the transcendental unit */
   FATTN_EXP_POLY = 2,    /* Cody–Waite split + degree-3 polynomial on FMA units */
   FATTN_EXP_SPLIT = 3    /* a static quarter of the exponentials (one in four
@@ -109,6 +110,8 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v,
  * (FlashAttention-3 page, innovation 3).
  *   q, k, v     [B,H,N,d] bf16 inputs; o [B,H,N,d] bf16 output.
  *   lse         optional [B,H,N] fp32 output (NULL to skip).
+ *   exp_mode    one of fattn_exp_mode, for the exponentials of the softmax
+ *               (FlashAttention-4 gist, technical summary 2.B).
  *   rotate      1: Q' = Q·R, K' = K·R with R = diag(s)·H_d/√d, H_d the
  *               Sylvester Hadamard matrix, s_i = ±1 from the top bit of the
  *               i-th SplitMix64 output for state `seed`; 0: no rotation.
@@ -137,7 +140,7 @@ fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d,
                                             size_t* off_scales);
 fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                            float* lse, int B, int H, int N, int d, int causal,
-                           float scale, int rotate, uint64_t seed,
+                           float scale, int exp_mode, int rotate, uint64_t seed,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -146,15 +149,17 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
  * between them), on a workspace that a previous fattn_fwd_fp8 call with the
  * same B, H, N, d filled: it reads the e4m3 operands Q8, Q8lo, K8, V8ᵀ and
  * the scales from the workspace and writes o (and lse if non-NULL) exactly as
- * that call did for the same causal and scale. The workspace is only read.
+ * that call did for the same causal, scale and exp_mode. The workspace is
+ * only read.
  * For re-running attention on operands already quantised and rotated, and
  * for timing the attention step apart from the quantisation.
  * Errors as fattn_fwd_fp8 (a workspace never filled gives meaningless o,
  * not an error).
  */
 fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int d,
-                                  int causal, float scale, const void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  int causal, float scale, int exp_mode,
+                                  const void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Static description of a status code. */
 const char* fattn_strerror(int status);

@@ -93,13 +93,15 @@ def test_fp8_workspace_layout_and_checks():
     assert all(x % 256 == 0 for x in (oq, oql, ok, ov, osc))
 
     def call(ws, nbytes, **kw):
-        a = dict(rotate=1, lse=P, d=d)
+        a = dict(rotate=1, lse=P, d=d, exp=0)
         a.update(kw)
         return lib.fattn_fwd_fp8(P, P, P, P, a["lse"], B, H, N, a["d"], 0, ctypes.c_float(0.1),
-                                 a["rotate"], ctypes.c_uint64(7), ws, nbytes, NUL)
+                                 a["exp"], a["rotate"], ctypes.c_uint64(7), ws, nbytes, NUL)
     assert call(P, need - 1) == EWORKSPACE
     assert call(NUL, need) == EWORKSPACE
     assert call(P, need, rotate=2) == EINVAL
+    assert call(P, need, exp=4) == EINVAL
+    assert call(P, need, exp=-1) == EINVAL
     assert call(P, need, lse=MIS) == EINVAL
     assert call(P, need, d=80) == ENOTSUP
 
@@ -110,10 +112,11 @@ def test_fp8_attend_checks():
     need = lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
 
     def call(ws, nbytes, **kw):
-        a = dict(o=P, lse=NUL, B=B, H=H, N=N, d=d, causal=0, scale=0.1)
+        a = dict(o=P, lse=NUL, B=B, H=H, N=N, d=d, causal=0, scale=0.1, exp=0)
         a.update(kw)
         return lib.fattn_fwd_fp8_attend(a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
-                                        a["causal"], ctypes.c_float(a["scale"]), ws, nbytes, NUL)
+                                        a["causal"], ctypes.c_float(a["scale"]), a["exp"], ws,
+                                        nbytes, NUL)
     assert call(NUL, need) == EWORKSPACE
     assert call(P, need - 1) == EWORKSPACE
     assert call(MIS, need) in (EINVAL, EWORKSPACE)
@@ -123,3 +126,4 @@ def test_fp8_attend_checks():
     assert call(P, need, N=0) == EINVAL
     assert call(P, need, scale=float("nan")) == EINVAL
     assert call(P, need, causal=3) == EINVAL
+    assert call(P, need, exp=5) == EINVAL

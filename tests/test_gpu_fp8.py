@@ -159,3 +159,36 @@ def test_fp8_attend_reuses_workspace(causal):
     o2, l2 = fa.fwd_fp8_attend(ws, B, H, N, d, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("exp_mode", ["poly", "split"])
+@pytest.mark.parametrize("shape,causal", [((1, 2, 256, 128), False), ((1, 3, 300, 64), True),
+                                          ((1, 2, 1000, 128), False)])
+def test_fp8_exp_modes(shape, causal, exp_mode):
+    # The polynomial exp2 (all elements, or one in four) feeds P̃ to the same
+    # e4m3 rounding; the output stays within the fp8 bound of exact attention,
+    # within 2e-2 (relative RMS) of the hardware-exp2 output, and the LSE
+    # within the model's tolerance.
+    import tiled_attention_fattn_amd as fa
+    inp = _inputs(70 + shape[2], shape)
+    q, k, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    B, H, N, d = shape
+    scale = d ** -0.5
+    ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    print(f"[fp8] exp={exp_mode} shape={shape} causal={causal}", flush=True)
+    o_hw, _ = fa.fwd_fp8(q, k, v, causal=causal, rotate=True, seed=5, workspace=ws,
+                         exp_mode="hw")
+    o_x, l_x = fa.fwd_fp8(q, k, v, causal=causal, rotate=True, seed=5, workspace=ws,
+                          exp_mode=exp_mode)
+    o_a, l_a = fa.fwd_fp8_attend(ws, B, H, N, d, causal=causal, scale=scale, exp_mode=exp_mode)
+    torch.cuda.synchronize()
+    assert torch.equal(o_x, o_a) and torch.equal(l_x, l_a)
+    ref_o, _ = attention_forward(inp["q"][0], inp["k"][0], inp["v"][0], causal, scale)
+    got = to_np(o_x)
+    assert np.all(np.isfinite(got))
+    assert rel_rms(got, ref_o) <= FP8_REL_RMS
+    assert rel_rms(got, to_np(o_hw)) <= 2e-2
+    model = fp8_attention_model(inp["q"][0], inp["k"][0], inp["v"][0], causal, scale,
+                                rotate=True, seed=5)
+    lse_err = np.abs(to_np(l_x) - model["lse"])
+    assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()

@@ -84,7 +84,7 @@ def fwd(q, k, v, causal=False, scale=None, exp_mode="auto", out=None, lse=None):
 
 
 def fwd_fp8_attend(workspace, B, H, N, d, causal=False, scale=None, want_lse=True, out=None,
-                   device=None):
+                   device=None, exp_mode="auto"):
     """The attention step of fwd_fp8 alone, on a workspace a previous fwd_fp8
     call of the same (B, H, N, d) filled. Returns (O, LSE or None)."""
     torch = _torch()
@@ -94,7 +94,7 @@ def fwd_fp8_attend(workspace, B, H, N, d, causal=False, scale=None, want_lse=Tru
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=dev) if want_lse else None
     with torch.cuda.device(dev):
         _call(lib().fattn_fwd_fp8_attend(_ptr(o), _ptr(lse_t), B, H, N, d, int(bool(causal)),
-                                         ctypes.c_float(scale), _ptr(workspace),
+                                         ctypes.c_float(scale), _EXP[exp_mode], _ptr(workspace),
                                          ctypes.c_size_t(workspace.numel()), _stream(o)))
     return o, lse_t
 
@@ -151,7 +151,7 @@ def fp8_workspace_views(ws, B, H, N, d):
 
 
 def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=True,
-            workspace=None, out=None):
+            workspace=None, out=None, exp_mode="auto"):
     """fp8 (e4m3) forward with optional Hadamard rotation. Returns (O, LSE or None)."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -164,7 +164,8 @@ def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=Tru
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
     with torch.cuda.device(q.device):
         _call(lib().fattn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
-                                  int(bool(causal)), ctypes.c_float(scale), int(bool(rotate)),
+                                  int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
+                                  int(bool(rotate)),
                                   ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
                                   ctypes.c_size_t(ws.numel()), _stream(q)))
     return o, lse_t

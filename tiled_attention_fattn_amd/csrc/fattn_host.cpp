@@ -101,6 +101,12 @@ Fp8Layout fp8_layout(int B, int H, int N, int d) {
   return L;
 }
 
+fattn_status check_exp_mode(int exp_mode) {
+  if (exp_mode < FATTN_EXP_AUTO || exp_mode > FATTN_EXP_SPLIT)
+    return fail(FATTN_EINVAL, "exp_mode must be 0, 1, 2 or 3 (got %d)", exp_mode);
+  return FATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,8 +119,7 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o, flo
   FATTN_TRY(check_ptr(o, "o"));
   FATTN_TRY(check_ptr(lse, "lse"));
   FATTN_TRY(check_shape(B, H, N, d, causal, scale));
-  if (exp_mode < FATTN_EXP_AUTO || exp_mode > FATTN_EXP_SPLIT)
-    return fail(FATTN_EINVAL, "exp_mode must be 0, 1, 2 or 3 (got %d)", exp_mode);
+  FATTN_TRY(check_exp_mode(exp_mode));
   FATTN_TRY(check_device());
   const int mode = exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode;
   return hip_status(fattn::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, mode,
@@ -175,14 +180,15 @@ fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d, size_t* 
 }
 
 fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                           int H, int N, int d, int causal, float scale, int rotate, uint64_t seed,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           int H, int N, int d, int causal, float scale, int exp_mode, int rotate,
+                           uint64_t seed, void* workspace, size_t workspace_bytes, void* stream) {
   FATTN_TRY(check_ptr(q, "q"));
   FATTN_TRY(check_ptr(k, "k"));
   FATTN_TRY(check_ptr(v, "v"));
   FATTN_TRY(check_ptr(o, "o"));
   if (lse != nullptr && !aligned16(lse)) return fail(FATTN_EINVAL, "lse is not 16-byte aligned");
   FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  FATTN_TRY(check_exp_mode(exp_mode));
   if (rotate != 0 && rotate != 1) return fail(FATTN_EINVAL, "rotate must be 0 or 1 (got %d)", rotate);
   if ((long long)B * H > 65535)
     return fail(FATTN_ENOTSUP, "fp8 forward supports B*H <= 65535 (got %lld)", (long long)B * H);
@@ -197,16 +203,18 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                                           (uint8_t*)(ws + L.q8lo), (uint8_t*)(ws + L.k8), (uint8_t*)(ws + L.v8t),
                                           (float*)(ws + L.scales), (float*)(ws + L.partial), B,
                                           H, N, d, causal != 0, scale,
+                                          exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode,
                                           rotate != 0, seed, (hipStream_t)stream),
                     "fattn_fwd_fp8 launch");
 }
 
 fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int d, int causal,
-                                  float scale, const void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  float scale, int exp_mode, const void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   FATTN_TRY(check_ptr(o, "o"));
   if (lse != nullptr && !aligned16(lse)) return fail(FATTN_EINVAL, "lse is not 16-byte aligned");
   FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  FATTN_TRY(check_exp_mode(exp_mode));
   if ((long long)B * H > 65535)
     return fail(FATTN_ENOTSUP, "fp8 forward supports B*H <= 65535 (got %lld)", (long long)B * H);
   if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
@@ -221,7 +229,9 @@ fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int 
                                                  (const uint8_t*)(ws + L.k8),
                                                  (const uint8_t*)(ws + L.v8t),
                                                  (const float*)(ws + L.scales), B, H, N, d,
-                                                 causal != 0, scale, (hipStream_t)stream),
+                                                 causal != 0, scale,
+                                                 exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode,
+                                                 (hipStream_t)stream),
                     "fattn_fwd_fp8_attend launch");
 }
 
@@ -239,6 +249,6 @@ const char* fattn_strerror(int status) {
 
 const char* fattn_last_error(void) { return g_last_error; }
 
-int fattn_version(void) { return 100; }
+int fattn_version(void) { return 200; }
 
 }  // extern "C"

@@ -25,14 +25,15 @@ constexpr int kBwdRowPad = 64;
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                           uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
                           float* partial,
-                          int B, int H, int N, int d, bool causal, float scale, bool rotate,
-                          uint64_t seed, hipStream_t stream);
+                          int B, int H, int N, int d, bool causal, float scale, int exp_mode,
+                          bool rotate, uint64_t seed, hipStream_t stream);
 
 // fp8 attention only (the last launch of launch_fwd_fp8) on operands a
 // previous launch_fwd_fp8 of the same shape left in q8/q8lo/k8/v8t/scales.
 hipError_t launch_fwd_fp8_attend(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
                                  const uint8_t* k8, const uint8_t* v8t, const float* scales, int B,
-                                 int H, int N, int d, bool causal, float scale, hipStream_t stream);
+                                 int H, int N, int d, bool causal, float scale, int exp_mode,
+                                 hipStream_t stream);
 
 constexpr int kFp8Npad = 64;
 constexpr int kFp8AmaxRows = 256;  // rows per amax chunk

@@ -332,7 +332,7 @@ constexpr int kF8Waves = 4;
 constexpr int kF8BM = 32 * kF8Waves;
 constexpr int kF8BN = 64;
 
-template <int D, bool CAUSAL, bool WANT_LSE>
+template <int D, bool CAUSAL, bool WANT_LSE, int EXPM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ q8lo,
                     const uint8_t* __restrict__ k8,
@@ -501,7 +501,9 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
         float pv4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pv4[e] = exp2_hw(fmaf(s[t][4 * wd + e], c_log2, off));
+          // SPLIT: element e = 3 of every group of four on the polynomial.
+          const float x = fmaf(s[t][4 * wd + e], c_log2, off);
+          pv4[e] = (EXPM == EXP_POLY || (EXPM == EXP_SPLIT && e == 3)) ? exp2_poly(x) : exp2_hw(x);
           if constexpr (WANT_LSE) l_part += pv4[e];
         }
         p8[4 * t + wd] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
@@ -574,28 +576,39 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   }
 }
 
-template <int D, bool CAUSAL>
-static hipError_t launch_attend_t(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
+template <int D, bool CAUSAL, int EXPM>
+static hipError_t launch_attend_m(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
                                   const uint8_t* k8, const uint8_t* v8t, const float* scales, int BH,
                                   int N, float scale, hipStream_t stream) {
   const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
   const int n_qtiles = (N + kF8BM - 1) / kF8BM;
   if (lse != nullptr)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true>), dim3(n_qtiles * BH), dim3(256), 0, stream,
-                       q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, EXPM>), dim3(n_qtiles * BH), dim3(256), 0,
+                       stream, q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
                        scale * kLog2e);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false>), dim3(n_qtiles * BH), dim3(256), 0, stream,
-                       q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, EXPM>), dim3(n_qtiles * BH), dim3(256), 0,
+                       stream, q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
                        scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
+static hipError_t launch_attend_t(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
+                                  const uint8_t* k8, const uint8_t* v8t, const float* scales, int BH,
+                                  int N, float scale, int exp_mode, hipStream_t stream) {
+  if (exp_mode == EXP_POLY)
+    return launch_attend_m<D, CAUSAL, EXP_POLY>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+  if (exp_mode == EXP_SPLIT)
+    return launch_attend_m<D, CAUSAL, EXP_SPLIT>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+  return launch_attend_m<D, CAUSAL, EXP_HW>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+}
+
+template <int D, bool CAUSAL>
 static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
-                               float* partial, int BH, int N, float scale, bool rotate,
-                               uint64_t seed, hipStream_t stream) {
+                               float* partial, int BH, int N, float scale, int exp_mode,
+                               bool rotate, uint64_t seed, hipStream_t stream) {
   const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
   const unsigned nchunks = (unsigned)((N + kFp8AmaxRows - 1) / kFp8AmaxRows);
   hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(nchunks, BH, 3), dim3(256), 0, stream,
@@ -606,32 +619,34 @@ static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void
                      BH, (int)rotate, seed);
   hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(Npad / 64, BH), dim3(256), 0, stream,
                      (const bf16*)v, v8t, (const float*)partial, scales, N, Npad, BH, (int)nchunks);
-  return launch_attend_t<D, CAUSAL>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+  return launch_attend_t<D, CAUSAL>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode,
+                                    stream);
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                           uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
                           float* partial, int B, int H, int N, int d, bool causal, float scale,
-                          bool rotate, uint64_t seed, hipStream_t stream) {
+                          int exp_mode, bool rotate, uint64_t seed, hipStream_t stream) {
   const int BH = B * H;
   if (d == 64) {
-    return causal ? launch_fp8_t<64, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream)
-                  : launch_fp8_t<64, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream);
+    return causal ? launch_fp8_t<64, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream)
+                  : launch_fp8_t<64, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream);
   }
-  return causal ? launch_fp8_t<128, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream)
-                : launch_fp8_t<128, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, rotate, seed, stream);
+  return causal ? launch_fp8_t<128, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream)
+                : launch_fp8_t<128, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream);
 }
 
 hipError_t launch_fwd_fp8_attend(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
                                  const uint8_t* k8, const uint8_t* v8t, const float* scales, int B,
-                                 int H, int N, int d, bool causal, float scale, hipStream_t stream) {
+                                 int H, int N, int d, bool causal, float scale, int exp_mode,
+                                 hipStream_t stream) {
   const int BH = B * H;
   if (d == 64) {
-    return causal ? launch_attend_t<64, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream)
-                  : launch_attend_t<64, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+    return causal ? launch_attend_t<64, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream)
+                  : launch_attend_t<64, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream);
   }
-  return causal ? launch_attend_t<128, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream)
-                : launch_attend_t<128, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+  return causal ? launch_attend_t<128, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream)
+                : launch_attend_t<128, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream);
 }
 
 }  // namespace fattn
