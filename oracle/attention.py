@@ -20,6 +20,13 @@ Backward (standard gradient of ⟨O, dO⟩; the pages name only dS and dQ, in
     dV = Pᵀ·dO,  dP = dO·Vᵀ,  D_i = Σ_j P_ij dP_ij,
     dS = P ∘ (dP − D),  dQ = scale·dS·K,  dK = scale·dSᵀ·Q.
 
+Variable-length sequences packed along N (varlen; the pages name it only as a
+variant the tiled design enables, [FA4-gist-pt] "Significado e Impacto"):
+offsets cu_seqlens = [c_0, …, c_n] split the rows into segments
+[c_s, c_{s+1}); reading: key j is visible to query i iff both lie in the same
+segment (and, when causal, j ≤ i). Each segment is then an independent
+attention problem; rows outside every segment see no key.
+
 A row with no visible key (impossible for square causal attention, kept for
 completeness) has O = 0, LSE = −∞ and contributes no gradient.
 
@@ -29,14 +36,31 @@ of the bf16 inputs the GPU consumes.
 import numpy as np
 
 
-def _scores(q, k, causal, scale):
-    """S = scale·q·kᵀ for one head, with the causal mask applied."""
+def segment_ids(n, cu_seqlens):
+    """Segment index of each of n rows for the offsets cu_seqlens (−1 for rows
+    outside every segment)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    ids = np.full(n, -1, dtype=np.int64)
+    for s in range(len(cu) - 1):
+        ids[cu[s]:cu[s + 1]] = s
+    return ids
+
+
+def _scores(q, k, causal, scale, rows=None, seg=None):
+    """S = scale·q·kᵀ for one head with the causal and segment masks applied.
+
+    rows: the global row index of each query row (default 0..n_q−1); seg: the
+    segment id of every key row (None: one segment holding all rows).
+    """
     s = scale * (q @ k.T)
+    n_q, n_k = s.shape
+    r = np.arange(n_q) if rows is None else np.asarray(rows, dtype=np.int64)
+    cols = np.arange(n_k)[None, :]
     if causal:
-        n_q, n_k = s.shape
-        rows = np.arange(n_q)[:, None]
-        cols = np.arange(n_k)[None, :]
-        s = np.where(cols <= rows, s, -np.inf)
+        s = np.where(cols <= r[:, None], s, -np.inf)
+    if seg is not None:
+        sq = seg[r][:, None]
+        s = np.where((seg[None, :] == sq) & (sq >= 0), s, -np.inf)
     return s
 
 
@@ -56,26 +80,28 @@ def softmax_rows(s):
     return p, lse
 
 
-def attention_forward(q, k, v, causal, scale):
-    """O = softmax(scale·Q·Kᵀ [causal]) · V and LSE, per (b, h), in float64.
+def attention_forward(q, k, v, causal, scale, cu_seqlens=None):
+    """O = softmax(scale·Q·Kᵀ [causal] [segments]) · V and LSE, per (b, h), in float64.
 
-    q, k, v: [B, H, N, d] float64. Returns (O [B,H,N,d], LSE [B,H,N]).
+    q, k, v: [B, H, N, d] float64; cu_seqlens: optional segment offsets (the
+    same for every (b, h)). Returns (O [B,H,N,d], LSE [B,H,N]).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, N, d = q.shape
+    seg = None if cu_seqlens is None else segment_ids(N, cu_seqlens)
     o = np.empty((B, H, N, v.shape[-1]), dtype=np.float64)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            s = _scores(q[b, h], k[b, h], causal, scale)
+            s = _scores(q[b, h], k[b, h], causal, scale, seg=seg)
             p, lse[b, h] = softmax_rows(s)
             o[b, h] = p @ v[b, h]
     return o, lse
 
 
-def attention_forward_rows(q, k, v, causal, scale, b, h, rows):
+def attention_forward_rows(q, k, v, causal, scale, b, h, rows, cu_seqlens=None):
     """Forward for selected query rows of one head (b, h); same definition.
 
     Used to check outputs at full problem sizes on sampled rows. Returns
@@ -85,15 +111,13 @@ def attention_forward_rows(q, k, v, causal, scale, b, h, rows):
     qh = np.asarray(q[b, h], dtype=np.float64)[rows]
     kh = np.asarray(k[b, h], dtype=np.float64)
     vh = np.asarray(v[b, h], dtype=np.float64)
-    s = scale * (qh @ kh.T)
-    if causal:
-        cols = np.arange(kh.shape[0])[None, :]
-        s = np.where(cols <= rows[:, None], s, -np.inf)
+    seg = None if cu_seqlens is None else segment_ids(kh.shape[0], cu_seqlens)
+    s = _scores(qh, kh, causal, scale, rows=rows, seg=seg)
     p, lse = softmax_rows(s)
     return p @ vh, lse
 
 
-def attention_backward(q, k, v, do, causal, scale):
+def attention_backward(q, k, v, do, causal, scale, cu_seqlens=None):
     """Gradients of ⟨O, dO⟩ with respect to Q, K, V, in float64.
 
     P is formed again from the definition (not from any saved statistic).
@@ -108,9 +132,10 @@ def attention_backward(q, k, v, do, causal, scale):
     dk = np.empty_like(k)
     dv = np.empty_like(v)
     dvec = np.empty((B, H, N), dtype=np.float64)
+    seg = None if cu_seqlens is None else segment_ids(N, cu_seqlens)
     for b in range(B):
         for h in range(H):
-            s = _scores(q[b, h], k[b, h], causal, scale)
+            s = _scores(q[b, h], k[b, h], causal, scale, seg=seg)
             p, _ = softmax_rows(s)
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T

@@ -11,8 +11,12 @@ computation from the vectorised oracle.
 import math
 
 
-def brute_forward(q, k, v, causal, scale):
-    """q, k, v: nested lists [N][d] (one head). Returns (O [N][d], LSE [N])."""
+def brute_forward(q, k, v, causal, scale, cu_seqlens=None):
+    """q, k, v: nested lists [N][d] (one head). Returns (O [N][d], LSE [N]).
+
+    cu_seqlens: optional segment offsets; key j then counts for query i only
+    if some segment [c_s, c_{s+1}) holds both.
+    """
     n = len(q)
     d = len(q[0])
     dv = len(v[0])
@@ -24,6 +28,14 @@ def brute_forward(q, k, v, causal, scale):
             if causal and j > i:
                 weights.append(0.0)
                 continue
+            if cu_seqlens is not None:
+                same = False
+                for s in range(len(cu_seqlens) - 1):
+                    if cu_seqlens[s] <= i < cu_seqlens[s + 1] and cu_seqlens[s] <= j < cu_seqlens[s + 1]:
+                        same = True
+                if not same:
+                    weights.append(0.0)
+                    continue
             dot = 0.0
             for c in range(d):
                 dot += q[i][c] * k[j][c]

@@ -113,3 +113,44 @@ def test_causal_last_key_only_seen_by_last_query():
     p_last = np.exp(s_last - s_last.max())
     p_last /= p_last.sum()
     np.testing.assert_allclose(dv[0, 0, -1], p_last[-1] * do[0, 0, -1], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_gradients_equal_independent_segments(causal):
+    # Packed segments do not interact: every gradient equals that of the
+    # segment's own attention problem.
+    cu = [0, 1, 9, 10, 33]
+    rng = np.random.default_rng(77)
+    q, k, v, do = (rng.standard_normal((1, 2, 33, 6)) for _ in range(4))
+    dq, dk, dv, dvec = attention_backward(q, k, v, do, causal, 0.5, cu_seqlens=cu)
+    for a, b in zip(cu[:-1], cu[1:]):
+        sl = (slice(None), slice(None), slice(a, b))
+        rq, rk, rv, rd = attention_backward(q[sl], k[sl], v[sl], do[sl], causal, 0.5)
+        for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+            np.testing.assert_allclose(got[sl], ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dvec[sl], rd, rtol=0, atol=1e-13)
+
+
+def test_varlen_finite_differences():
+    # Central differences of L = <O, dO> through the segment-masked forward.
+    cu = [0, 2, 3, 7]
+    rng = np.random.default_rng(78)
+    q, k, v, do = (rng.standard_normal((1, 1, 7, 3)) for _ in range(4))
+    dq, dk, dv, _ = attention_backward(q, k, v, do, True, 0.9, cu_seqlens=cu)
+
+    def loss(qq, kk, vv):
+        return float(np.sum(attention_forward(qq, kk, vv, True, 0.9, cu_seqlens=cu)[0] * do))
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"])
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)

@@ -159,3 +159,47 @@ def test_rows_variant_matches_full(causal):
     o_r, lse_r = attention_forward_rows(q, k, v, causal, 0.35, 1, 0, rows)
     np.testing.assert_allclose(o_r, o[1, 0, rows], atol=1e-14)
     np.testing.assert_allclose(lse_r, lse[1, 0, rows], atol=1e-14)
+
+
+# Variable-length (packed) sequences: segments [c_s, c_{s+1}) of the rows.
+VARLEN_CU = [[0, 3, 4, 11, 16], [0, 16], [0, 1, 2, 3, 16], [0, 0, 9, 9, 16]]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cu", VARLEN_CU)
+def test_varlen_matches_brute_force(cu, causal):
+    n, d = 16, 5
+    q, k, v = (_rand((1, 1, n, d), s) for s in (31, 32, 33))
+    o, lse = attention_forward(q, k, v, causal, 0.6, cu_seqlens=cu)
+    bo, bl = brute_forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal, 0.6,
+                           cu_seqlens=cu)
+    np.testing.assert_allclose(o[0, 0], np.array(bo), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], np.array(bl), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equals_independent_segments(causal):
+    # Each segment is its own attention problem: the packed result equals the
+    # plain attention of every slice, and a single segment is plain attention.
+    cu = [0, 5, 6, 40, 41, 77]
+    q, k, v = (_rand((2, 2, 77, 8), s) for s in (41, 42, 43))
+    o, lse = attention_forward(q, k, v, causal, 0.4, cu_seqlens=cu)
+    for a, b in zip(cu[:-1], cu[1:]):
+        so, sl = attention_forward(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], causal, 0.4)
+        np.testing.assert_allclose(o[:, :, a:b], so, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, a:b], sl, rtol=0, atol=1e-13)
+    o1, l1 = attention_forward(q, k, v, causal, 0.4, cu_seqlens=[0, 77])
+    o2, l2 = attention_forward(q, k, v, causal, 0.4)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_varlen_rows_variant_and_uncovered_rows():
+    cu = [0, 7, 20]
+    q, k, v = (_rand((1, 2, 24, 4), s) for s in (51, 52, 53))
+    o, lse = attention_forward(q, k, v, True, 0.5, cu_seqlens=cu)
+    rows = np.array([0, 6, 7, 13, 19, 21, 23])
+    ro, rl = attention_forward_rows(q, k, v, True, 0.5, 0, 1, rows, cu_seqlens=cu)
+    np.testing.assert_allclose(ro, o[0, 1][rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(rl, lse[0, 1][rows], rtol=0, atol=1e-14)
+    # rows 20..23 lie in no segment: they see no key
+    assert np.all(o[:, :, 20:] == 0) and np.all(np.isneginf(lse[:, :, 20:]))
