@@ -235,6 +235,41 @@ def sweep(args):
                            "frac_of_peak": round(tf / PEAK_FP8, 4)})
             print(f"[sweep] d={d} N={N} done", file=sys.stderr, flush=True)
             del q, k, v, do, o, lse, ws8
+    # Packed variable-length sequences: B = 1, H = 8, N = 32768 rows split into
+    # segments of seeded lengths uniform in [1, 8192] (the last one cut to fit).
+    rng = np.random.default_rng(2024)
+    lengths = []
+    while sum(lengths) < 32768:
+        lengths.append(int(min(rng.integers(1, 8193), 32768 - sum(lengths))))
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device="cuda")
+    H, N, d = 8, 32768, 128
+    g = torch.Generator(device="cuda").manual_seed(77)
+    q, k, v, do = (torch.randn(1, H, N, d, device="cuda", generator=g).to(torch.bfloat16)
+                   for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, H, N), dtype=torch.float32, device="cuda")
+    maxl = max(lengths)
+    scale = d ** -0.5
+    for causal in (False, True):
+        ms = timed(lambda: fa.fwd_varlen(q, k, v, cu, maxl, causal=causal, scale=scale, out=o,
+                                         lse=lse))
+        fl = sum(flops_fwd(1, H, n, d, causal) for n in lengths)
+        points.append({"part": "fwd_varlen", "causal": causal, "B": 1, "H": H, "N": N, "d": d,
+                       "segments": len(lengths), "max_seqlen": maxl, "ms": round(ms, 4),
+                       "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                       "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16, 4)})
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.bwd_workspace_bytes(1, H, N, d), dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: fa.bwd_varlen(q, k, v, o, lse, do, cu, maxl, causal=True, scale=scale,
+                                     workspace=ws, out=grads))
+    fl = sum(flops_bwd(1, H, n, d, True) for n in lengths)
+    points.append({"part": "bwd_varlen", "causal": True, "B": 1, "H": H, "N": N, "d": d,
+                   "segments": len(lengths), "max_seqlen": maxl, "ms": round(ms, 4),
+                   "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                   "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16, 4)})
+    print(f"[sweep] varlen done ({len(lengths)} segments, max {maxl})", file=sys.stderr,
+          flush=True)
+
     print(json.dumps({"sweep": "tokens per point B*H*N = %d, B = 1" % SWEEP_TOKENS,
                       "data": "synthetic: seeded N(0,1) rounded to bf16", "reps": reps,
                       "warmup": warm, "points": points}), flush=True)

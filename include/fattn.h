@@ -19,7 +19,9 @@
  *  - "FlashAttention-4: Algorithm and Kernel Pipelining Co-Design for
  *    Asymmetric Hardware Scaling" (gist.science) — technical summary 2.B
  *    (software exp2 on FMA units, conditional rescaling past a threshold),
- *    2.C (backward: dS, dQ and global atomic reductions).
+ *    2.C (backward: dS, dQ and global atomic reductions); the Portuguese
+ *    summary of the same paper, "Significado e Impacto", names variable-length
+ *    (varlen) attention as a variant the design enables.
  *
  * Conventions for every entry point
  *  - Tensors are device pointers to contiguous [B, H, N, d] arrays (d fastest)
@@ -104,6 +106,36 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v,
                        void* dq, void* dk, void* dv, int B, int H, int N, int d,
                        int causal, float scale, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * Packed variable-length sequences (varlen), bf16 forward and backward.
+ *   cu_seqlens  device int32 [nseq + 1], non-decreasing offsets into the N rows
+ *               of every head: rows [cu_seqlens[s], cu_seqlens[s+1]) form
+ *               segment s, and a query attends only to the keys of its own
+ *               segment (and, when causal, to those at or before its row).
+ *               The same offsets apply to every (b, h).
+ *   nseq        number of segments, >= 1.
+ *   max_seqlen  an upper bound on every segment's length, 1..N: it sizes the
+ *               launch grid (B·H·nseq·ceil(max_seqlen/128) workgroups,
+ *               ENOTSUP past 2^31 − 1).
+ * Everything else as fattn_fwd / fattn_bwd (same workspace). Each segment is
+ * computed exactly as fattn_fwd / fattn_bwd would compute it as a sequence of
+ * its own. The offsets live in device memory, so they are not checked on the
+ * host: the kernels clamp them to [0, N] (no access outside the tensors for
+ * any contents), and the caller must keep cu_seqlens[0] = 0,
+ * cu_seqlens[nseq] = N and every length <= max_seqlen — rows outside every
+ * segment, and rows of a segment past max_seqlen, are not written.
+ */
+fattn_status fattn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                              float* lse, const int32_t* cu_seqlens, int nseq,
+                              int max_seqlen, int B, int H, int N, int d, int causal,
+                              float scale, int exp_mode, void* stream);
+fattn_status fattn_bwd_varlen(const void* q, const void* k, const void* v,
+                              const void* o, const float* lse, const void* dout,
+                              void* dq, void* dk, void* dv,
+                              const int32_t* cu_seqlens, int nseq, int max_seqlen,
+                              int B, int H, int N, int d, int causal, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Forward with fp8 (OCP e4m3fn) operands and bf16 in/out

@@ -127,3 +127,42 @@ def test_fp8_attend_checks():
     assert call(P, need, scale=float("nan")) == EINVAL
     assert call(P, need, causal=3) == EINVAL
     assert call(P, need, exp=5) == EINVAL
+
+
+def fwd_varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cu=P, nseq=3, maxl=16, B=1, H=2, N=40, d=128, causal=1,
+             scale=0.1, exp=0)
+    a.update(kw)
+    return fa.lib().fattn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"],
+                                     a["nseq"], a["maxl"], a["B"], a["H"], a["N"], a["d"],
+                                     a["causal"], ctypes.c_float(a["scale"]), a["exp"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=NUL), EINVAL), (dict(cu=ctypes.c_void_p(0x10002)), EINVAL), (dict(nseq=0), EINVAL),
+    (dict(maxl=0), EINVAL), (dict(maxl=41), EINVAL), (dict(q=NUL), EINVAL), (dict(d=80), ENOTSUP),
+    (dict(causal=2), EINVAL), (dict(exp=7), EINVAL), (dict(N=0), EINVAL),
+    (dict(B=1, H=1, N=16384, d=64, nseq=1 << 24, maxl=16384), ENOTSUP),  # grid size
+])
+def test_fwd_varlen_rejects_bad_arguments(kw, code):
+    assert fwd_varlen(**kw) == code
+    assert fa.lib().fattn_last_error()
+
+
+def test_bwd_varlen_checks():
+    lib = fa.lib()
+    B, H, N, d = 1, 2, 40, 64
+    need = lib.fattn_bwd_workspace_bytes(B, H, N, d)
+
+    def call(ws, nbytes, **kw):
+        a = dict(cu=P, nseq=2, maxl=30, dq=P)
+        a.update(kw)
+        return lib.fattn_bwd_varlen(P, P, P, P, P, P, a["dq"], P, P, a["cu"], a["nseq"], a["maxl"],
+                                    B, H, N, d, 0, ctypes.c_float(0.125), ws, nbytes, NUL)
+    assert call(P, need - 1) == EWORKSPACE
+    assert call(NUL, need) == EWORKSPACE
+    assert call(MIS, need) == EWORKSPACE
+    assert call(P, need, cu=NUL) == EINVAL
+    assert call(P, need, nseq=-1) == EINVAL
+    assert call(P, need, maxl=N + 1) == EINVAL
+    assert call(P, need, dq=MIS) == EINVAL

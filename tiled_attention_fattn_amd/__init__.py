@@ -8,6 +8,8 @@ an exception is raised.
     o, lse = fwd(q, k, v, causal=False, scale=None, exp_mode="auto")
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
     o, lse = fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0)
+    o, lse = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False)
+    dq, dk, dv = bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False)
 
 Tensors are contiguous CUDA (HIP) bfloat16 [B, H, N, d], d ∈ {64, 128};
 ``scale`` defaults to 1/√d.
@@ -17,7 +19,7 @@ import os
 
 from ._lib import FattnError, lib, lib_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
            "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
            "EXP_AUTO", "EXP_HW", "EXP_POLY", "EXP_SPLIT"]
 
@@ -83,6 +85,40 @@ def fwd(q, k, v, causal=False, scale=None, exp_mode="auto", out=None, lse=None):
     return o, lse_t
 
 
+def _cu(cu_seqlens, q):
+    torch = _torch()
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 \
+            or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous() \
+            or cu_seqlens.device != q.device or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor of nseq+1 >= 2 "
+                         "offsets on the device of q")
+    return cu_seqlens.numel() - 1
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, exp_mode="auto",
+               out=None, lse=None):
+    """Forward over packed variable-length sequences: rows [cu[s], cu[s+1]) of
+    every head are segment s. Returns (O, LSE) like fwd."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16)
+    B, H, N, d = _shape(q)
+    if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    nseq = _cu(cu_seqlens, q)
+    scale = float(d ** -0.5 if scale is None else scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(o, "out", torch.bfloat16)
+    _check(lse_t, "lse", torch.float32)
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
+                                     _ptr(cu_seqlens), nseq, int(max_seqlen), B, H, N, d,
+                                     int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
+                                     _stream(q)))
+    return o, lse_t
+
+
 def fwd_fp8_attend(workspace, B, H, N, d, causal=False, scale=None, want_lse=True, out=None,
                    device=None, exp_mode="auto"):
     """The attention step of fwd_fp8 alone, on a workspace a previous fwd_fp8
@@ -122,6 +158,31 @@ def bwd(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, out=None)
                               _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
                               ctypes.c_float(scale), _ptr(ws), ctypes.c_size_t(ws.numel()),
                               _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, scale=None,
+               workspace=None, out=None):
+    """Backward of fwd_varlen from its O and LSE. Returns (dQ, dK, dV) bf16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, torch.bfloat16)
+    _check(lse, "lse", torch.float32)
+    B, H, N, d = _shape(q)
+    nseq = _cu(cu_seqlens, q)
+    scale = float(d ** -0.5 if scale is None else scale)
+    if out is None:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    else:
+        dq, dk, dv = out
+    need = bwd_workspace_bytes(B, H, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), nseq,
+                                     int(max_seqlen), B, H, N, d, int(bool(causal)),
+                                     ctypes.c_float(scale), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                     _stream(q)))
     return dq, dk, dv
 
 

@@ -12,6 +12,13 @@
 // padded rows carry lse2 = +∞ and D = 0, so their P (and every contribution
 // they make) is exactly 0 without any mask.
 //
+// Packed variable-length sequences (VARLEN): kernels 2 and 3 run over
+// (head, segment, tile) and treat each segment as a sequence of its own
+// (rows offset to the segment start, length = the segment's). Rows past the
+// segment end read as zero from every buffer load (Q, dO, K, V and the
+// statistics alike), so they contribute nothing: their Q and dO are zero and
+// so is every product they enter.
+//
 // dQ is a sum over keys and dK, dV are sums over queries. Kernel 2 owns a
 // block of keys and walks the query tiles, so dK and dV accumulate in
 // registers; kernel 3 owns a block of queries and walks the key tiles (it
@@ -83,13 +90,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
 // ---------------------------------------------------------------------------
 // Kernel 2: dK, dV, key-stationary.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ lse2, const float* __restrict__ dvec,
                      bf16* __restrict__ dK, bf16* __restrict__ dV,
-                     int N, int Npad, int BH, int n_kvtiles, float c_log2, float scale) {
+                     int N, int Npad, int BH, int n_kvtiles, float c_log2, float scale,
+                     const int* __restrict__ cu, int nseq) {
   constexpr int KD = D / 16, DT = D / 32;
   constexpr int RB = D * 2;                         // bytes per Q / dO row
   constexpr int QT_BYTES = kBwdBM * RB;             // one Q or dO tile
@@ -106,30 +114,38 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // Workgroup → (head, key tile): heads contiguous per XCD (they share Q, dO
   // in that XCD's L2), key tiles of a head in increasing order (heaviest first
   // under the causal mask).
-  const int total = n_kvtiles * BH;
+  const int total = n_kvtiles * BH * (VARLEN ? nseq : 1);
   int logical = blockIdx.x;
   if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int bh = logical / n_kvtiles;
-  const int jt = logical - bh * n_kvtiles;
+  const int unit = logical / n_kvtiles;
+  const int jt = logical - unit * n_kvtiles;
+  const int bh = VARLEN ? unit / nseq : unit;
+  int row0 = 0, L = N;  // rows of the sequence or segment (offsets clamped to [0, N])
+  if constexpr (VARLEN) {
+    const int sg = unit - bh * nseq;
+    row0 = min(max(cu[sg], 0), N);
+    L = min(max(cu[sg + 1], row0), N) - row0;
+  }
+  const int kv0 = jt * kBwdBN;
+  if (kv0 >= L) return;  // whole workgroup
 
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = ((size_t)bh * N + row0) * D;
   const bf16* Qh = Q + head;
   const bf16* Kh = K + head;
   const bf16* Vh = V + head;
   const bf16* dOh = dO + head;
-  const float* lse_h = lse2 + (size_t)bh * Npad;
-  const float* d_h = dvec + (size_t)bh * Npad;
+  const float* lse_h = lse2 + (size_t)bh * Npad + row0;
+  const float* d_h = dvec + (size_t)bh * Npad + row0;
 
-  const int kv0 = jt * kBwdBN;
   const int kw0 = kv0 + 32 * wave;  // this wave's first key
   const int key = kw0 + c;          // this lane's key (accumulator column)
 
-  // K and V rows of this lane → registers (zero past N).
+  // K and V rows of this lane → registers (zero past the end).
   bf16x8 kreg[KD], vreg[KD];
 #pragma unroll
   for (int kk = 0; kk < KD; ++kk) {
-    kreg[kk] = key < N ? *(const bf16x8*)(Kh + (size_t)key * D + kk * 16 + 8 * h) : bf16x8{};
-    vreg[kk] = key < N ? *(const bf16x8*)(Vh + (size_t)key * D + kk * 16 + 8 * h) : bf16x8{};
+    kreg[kk] = key < L ? *(const bf16x8*)(Kh + (size_t)key * D + kk * 16 + 8 * h) : bf16x8{};
+    vreg[kk] = key < L ? *(const bf16x8*)(Vh + (size_t)key * D + kk * 16 + 8 * h) : bf16x8{};
   }
 
   // Per-lane LDS offsets (loop constants).
@@ -144,7 +160,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) toff[hf][dt] = tile_off<D>(tr_row + 8 * hf, 4 * dt + tr_chunk) + tr_sub;
-  const int n_qt = (N + kBwdBM - 1) / kBwdBM;
+  const int n_qt = (L + kBwdBM - 1) / kBwdBM;
   const int i0 = CAUSAL ? kv0 / kBwdBM : 0;
   // Query tiles that straddle this key block's diagonal need the causal mask.
   const int first_unmasked = CAUSAL ? min(n_qt, (kv0 + kBwdBN + kBwdBM - 1) / kBwdBM) : i0;
@@ -159,11 +175,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   auto gload = [&](int it, int stage) __device__ {
     const int qs = it * kBwdBM;
     char* qb = q_lds + stage * 2 * QT_BYTES;
-    buffer_to_lds<LD_LOADS>(Qh + (size_t)qs * D, (N - qs) * RB, qb, ld_off, wave * LD_LOADS);
-    buffer_to_lds<LD_LOADS>(dOh + (size_t)qs * D, (N - qs) * RB, qb + QT_BYTES, ld_off,
+    buffer_to_lds<LD_LOADS>(Qh + (size_t)qs * D, (L - qs) * RB, qb, ld_off, wave * LD_LOADS);
+    buffer_to_lds<LD_LOADS>(dOh + (size_t)qs * D, (L - qs) * RB, qb + QT_BYTES, ld_off,
                             wave * LD_LOADS);
-    // lse2 (wave 0) and D (wave 1): 64 floats = one 4-byte element per lane.
-    if (wave < 2) stats_to_lds((wave == 0 ? lse_h : d_h) + qs, st_lds + stage * 512 + wave * 256, lane);
+    // lse2 (wave 0) and D (wave 1): 64 floats = one 4-byte element per lane
+    // (a segment's rows only: rows past its end read as zero).
+    if (wave < 2)
+      stats_to_lds((wave == 0 ? lse_h : d_h) + qs, st_lds + stage * 512 + wave * 256, lane,
+                   VARLEN ? min(kBwdBM, L - qs) * 4 : kBwdBM * 4);
   };
 
   f32x16 dk_acc[DT], dv_acc[DT];
@@ -319,7 +338,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   if (it < n_qt) iteration(it, I0{}, std::false_type{});
 
   // Epilogue: lane holds dKᵀ/dVᵀ[d = 32dt + 8g + 4h + 0..3][key].
-  if (key < N) {
+  if (key < L) {
     bf16* dk_row = dK + head + (size_t)key * D;
     bf16* dv_row = dV + head + (size_t)key * D;
 #pragma unroll
@@ -347,13 +366,13 @@ constexpr int kDqWaves = 4;
 constexpr int kDqBM = 32 * kDqWaves;  // queries per workgroup
 constexpr int kDqBN = 64;             // keys per tile
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ lse2, const float* __restrict__ dvec,
                    bf16* __restrict__ dQ, int N, int Npad, int BH, int n_qtiles, float c_log2,
-                   float scale) {
+                   float scale, const int* __restrict__ cu, int nseq) {
   constexpr int KD = D / 16, RB = D * 2, TILE = kDqBN * RB, DT = D / 32;
   constexpr int LOADS = TILE / 1024 / kDqWaves;  // 1 KB wave loads per tensor per tile
   // LDS: K slots 0, 1 then V slots 0, 1, row-major with the 64-bank swizzle.
@@ -365,24 +384,33 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
 
-  // Workgroup → (head, query tile), XCD-aware; causal: heaviest tiles first.
-  const int total = n_qtiles * BH;
+  // Workgroup → (head[, segment], query tile), XCD-aware; causal: heaviest
+  // tiles first.
+  const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
   int logical = blockIdx.x;
   if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int bh = logical / n_qtiles;
-  int qt = logical - bh * n_qtiles;
+  const int unit = logical / n_qtiles;
+  int qt = logical - unit * n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int bh = VARLEN ? unit / nseq : unit;
+  int row0 = 0, L = N;  // rows of the sequence or segment (offsets clamped to [0, N])
+  if constexpr (VARLEN) {
+    const int sg = unit - bh * nseq;
+    row0 = min(max(cu[sg], 0), N);
+    L = min(max(cu[sg + 1], row0), N) - row0;
+  }
+  const int q_start = qt * kDqBM;
+  if (q_start >= L) return;  // whole workgroup
 
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = ((size_t)bh * N + row0) * D;
   const bf16* Qh = Q + head;
   const bf16* Kh = K + head;
   const bf16* Vh = V + head;
   const bf16* dOh = dO + head;
-  const int q_start = qt * kDqBM;
   const int qi = q_start + 32 * wave + c;  // this lane's query
-  const bool qv = qi < N;
-  const float l2 = qv ? lse2[(size_t)bh * Npad + qi] : INFINITY;
-  const float dq_d = qv ? dvec[(size_t)bh * Npad + qi] : 0.0f;
+  const bool qv = qi < L;
+  const float l2 = qv ? lse2[(size_t)bh * Npad + row0 + qi] : INFINITY;
+  const float dq_d = qv ? dvec[(size_t)bh * Npad + row0 + qi] : 0.0f;
 
   // Qᵀ and dOᵀ operands: lane holds row qi, elements 16kk + 8h + 0..7.
   bf16x8 qr[KD], dor[KD];
@@ -406,9 +434,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) toff[hf][dt] = tile_off<D>(tr_row + 8 * hf, 4 * dt + tr_chunk) + tr_sub;
 
-  const int kv_end = CAUSAL ? min(N, q_start + kDqBM) : N;
+  const int kv_end = CAUSAL ? min(L, q_start + kDqBM) : L;
   const int n_kv = (kv_end + kDqBN - 1) / kDqBN;
-  const int first_masked = CAUSAL ? min(q_start / kDqBN, N / kDqBN) : N / kDqBN;
+  const int first_masked = CAUSAL ? min(q_start / kDqBN, L / kDqBN) : L / kDqBN;
 
   int ld_off[LOADS];
 #pragma unroll
@@ -418,9 +446,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   auto gload = [&](int j, int slot) __device__ {
     const int key0 = j * kDqBN;
-    buffer_to_lds<LOADS>(Kh + (size_t)key0 * D, (N - key0) * RB, k_lds + slot * TILE, ld_off,
+    buffer_to_lds<LOADS>(Kh + (size_t)key0 * D, (L - key0) * RB, k_lds + slot * TILE, ld_off,
                          wave * LOADS);
-    buffer_to_lds<LOADS>(Vh + (size_t)key0 * D, (N - key0) * RB, v_lds + slot * TILE, ld_off,
+    buffer_to_lds<LOADS>(Vh + (size_t)key0 * D, (L - key0) * RB, v_lds + slot * TILE, ld_off,
                          wave * LOADS);
   };
 
@@ -454,7 +482,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         float p = exp2_hw(fmaf(sv[r], c_log2, -l2));
         if (MASKED) {
           const int key = key0 + t * 32 + acc_row(r, h);
-          if (key >= N || (CAUSAL && key > qi)) p = 0.0f;
+          if (key >= L || (CAUSAL && key > qi)) p = 0.0f;
         }
         ds[b] = p * (dpv[r] - dq_d);
       }
@@ -529,13 +557,15 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                float* dvec, float* lse2, int BH, int N, float scale,
-                               hipStream_t stream) {
+                               const int* cu, int nseq, int max_len, hipStream_t stream) {
   const int Npad = (N + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad;
   const long rows_pad = (long)BH * Npad;
+  const int len = VARLEN ? max_len : N;  // longest sequence the grid covers
+  const int units = BH * (VARLEN ? nseq : 1);
   {
     const long threads = rows_pad * (D / 8);
     const dim3 grid((unsigned)((threads + 255) / 256));
@@ -545,37 +575,55 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
     if (e != hipSuccess) return e;
   }
   {
-    const int n_kvtiles = (N + kBwdBN - 1) / kBwdBN;
-    const dim3 grid(n_kvtiles * BH);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), grid, dim3(256), 0, stream,
+    const int n_kvtiles = (len + kBwdBN - 1) / kBwdBN;
+    const dim3 grid(n_kvtiles * units);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), grid, dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                        (const float*)lse2, (const float*)dvec, (bf16*)dk, (bf16*)dv, N,
-                       Npad, BH, n_kvtiles, scale * kLog2e, scale);
+                       Npad, BH, n_kvtiles, scale * kLog2e, scale, cu, nseq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
-    const int n_qtiles = (N + kDqBM - 1) / kDqBM;
-    const dim3 grid(n_qtiles * BH);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), grid, dim3(256), 0, stream,
+    const int n_qtiles = (len + kDqBM - 1) / kDqBM;
+    const dim3 grid(n_qtiles * units);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), grid, dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                        (const float*)lse2, (const float*)dvec, (bf16*)dq, N, Npad, BH, n_qtiles,
-                       scale * kLog2e, scale);
+                       scale * kLog2e, scale, cu, nseq);
   }
   return hipGetLastError();
+}
+
+template <bool VARLEN>
+static hipError_t launch_bwd_v(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               float* dvec, float* lse2, int BH, int N, int d, bool causal,
+                               float scale, const int* cu, int nseq, int max_len,
+                               hipStream_t stream) {
+  if (d == 64) {
+    return causal ? launch_bwd_t<64, true, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream)
+                  : launch_bwd_t<64, false, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream);
+  }
+  return causal ? launch_bwd_t<128, true, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream)
+                : launch_bwd_t<128, false, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* dvec, float* lse2, int B, int H, int N, int d, bool causal,
                            float scale, hipStream_t stream) {
-  const int BH = B * H;
-  if (d == 64) {
-    return causal ? launch_bwd_t<64, true>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream)
-                  : launch_bwd_t<64, false>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream);
-  }
-  return causal ? launch_bwd_t<128, true>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream)
-                : launch_bwd_t<128, false>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, stream);
+  return launch_bwd_v<false>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B * H, N, d, causal,
+                             scale, nullptr, 1, N, stream);
+}
+
+hipError_t launch_bwd_bf16_varlen(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk,
+                                  void* dv, float* dvec, float* lse2, const int* cu_seqlens,
+                                  int nseq, int max_seqlen, int B, int H, int N, int d,
+                                  bool causal, float scale, hipStream_t stream) {
+  return launch_bwd_v<true>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B * H, N, d, causal,
+                            scale, cu_seqlens, nseq, max_seqlen, stream);
 }
 
 }  // namespace fattn

@@ -134,9 +134,10 @@ __device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, char*
 
 // 64 floats from `src` into LDS at `dst` (one 4-byte element per lane), by
 // the same untracked load as buffer_to_lds.
-__device__ __forceinline__ void stats_to_lds(const float* src, char* dst, int lane) {
+__device__ __forceinline__ void stats_to_lds(const float* src, char* dst, int lane,
+                                             int bytes = 256) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const i32x4 rsrc = make_rsrc_sgpr(src, 256);
+  const i32x4 rsrc = make_rsrc_sgpr(src, bytes);
   const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(FATTN_LDS char*)dst);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :

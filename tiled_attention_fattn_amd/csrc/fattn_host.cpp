@@ -101,6 +101,20 @@ Fp8Layout fp8_layout(int B, int H, int N, int d) {
   return L;
 }
 
+fattn_status check_varlen(const int32_t* cu_seqlens, int nseq, int max_seqlen, int B, int H,
+                          int N) {
+  if (cu_seqlens == nullptr) return fail(FATTN_EINVAL, "cu_seqlens is NULL");
+  if (((uintptr_t)cu_seqlens & 3) != 0) return fail(FATTN_EINVAL, "cu_seqlens is not 4-byte aligned");
+  if (nseq < 1) return fail(FATTN_EINVAL, "nseq must be >= 1 (got %d)", nseq);
+  if (max_seqlen < 1 || max_seqlen > N)
+    return fail(FATTN_EINVAL, "max_seqlen must be in [1, N=%d] (got %d)", N, max_seqlen);
+  // Grid of (head, segment, 128-row tile) workgroups.
+  const unsigned long long wgs = (unsigned long long)B * H * nseq * ((max_seqlen + 127) / 128);
+  if (wgs >= (1ull << 31))
+    return fail(FATTN_ENOTSUP, "%llu workgroups (B*H*nseq*ceil(max_seqlen/128)) exceed 2^31-1", wgs);
+  return FATTN_OK;
+}
+
 fattn_status check_exp_mode(int exp_mode) {
   if (exp_mode < FATTN_EXP_AUTO || exp_mode > FATTN_EXP_SPLIT)
     return fail(FATTN_EINVAL, "exp_mode must be 0, 1, 2 or 3 (got %d)", exp_mode);
@@ -125,6 +139,25 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o, flo
   return hip_status(fattn::launch_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal != 0, scale, mode,
                                            (hipStream_t)stream),
                     "fattn_fwd launch");
+}
+
+fattn_status fattn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int32_t* cu_seqlens, int nseq, int max_seqlen, int B, int H,
+                              int N, int d, int causal, float scale, int exp_mode, void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  FATTN_TRY(check_ptr(lse, "lse"));
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  FATTN_TRY(check_varlen(cu_seqlens, nseq, max_seqlen, B, H, N));
+  FATTN_TRY(check_exp_mode(exp_mode));
+  FATTN_TRY(check_device());
+  const int mode = exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode;
+  return hip_status(fattn::launch_fwd_bf16_varlen(q, k, v, o, lse, cu_seqlens, nseq, max_seqlen,
+                                                  B, H, N, d, causal != 0, scale, mode,
+                                                  (hipStream_t)stream),
+                    "fattn_fwd_varlen launch");
 }
 
 size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -159,6 +192,37 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v, const void* 
   return hip_status(fattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B, H, N,
                                            d, causal != 0, scale, (hipStream_t)stream),
                     "fattn_bwd launch");
+}
+
+fattn_status fattn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              const int32_t* cu_seqlens, int nseq, int max_seqlen, int B, int H,
+                              int N, int d, int causal, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  FATTN_TRY(check_ptr(lse, "lse"));
+  FATTN_TRY(check_ptr(dout, "dout"));
+  FATTN_TRY(check_ptr(dq, "dq"));
+  FATTN_TRY(check_ptr(dk, "dk"));
+  FATTN_TRY(check_ptr(dv, "dv"));
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  FATTN_TRY(check_varlen(cu_seqlens, nseq, max_seqlen, B, H, N));
+  if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
+  if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
+  const size_t need = fattn_bwd_workspace_bytes(B, H, N, d);
+  if (workspace_bytes < need)
+    return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, need);
+  FATTN_TRY(check_device());
+  const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
+  float* dvec = (float*)workspace;
+  float* lse2 = (float*)((char*)dvec + round_up(n * sizeof(float), 256));
+  return hip_status(fattn::launch_bwd_bf16_varlen(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2,
+                                                  cu_seqlens, nseq, max_seqlen, B, H, N, d,
+                                                  causal != 0, scale, (hipStream_t)stream),
+                    "fattn_bwd_varlen launch");
 }
 
 size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
@@ -249,6 +313,6 @@ const char* fattn_strerror(int status) {
 
 const char* fattn_last_error(void) { return g_last_error; }
 
-int fattn_version(void) { return 200; }
+int fattn_version(void) { return 300; }
 
 }  // extern "C"

@@ -11,12 +11,26 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
                            int B, int H, int N, int d, bool causal, float scale, int exp_mode,
                            hipStream_t stream);
 
+// Packed variable-length sequences: rows [cu_seqlens[s], cu_seqlens[s+1]) of
+// every head form segment s (device int32 [nseq+1]); max_seqlen bounds the
+// segment lengths the grid covers.
+hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int* cu_seqlens, int nseq, int max_seqlen,
+                                  int B, int H, int N, int d, bool causal, float scale,
+                                  int exp_mode, hipStream_t stream);
+
 // Backward: `dvec` and `lse2` fp32 [B,H,Npad] live in the caller's workspace
 // (Npad = N rounded up to kBwdRowPad).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* dvec, float* lse2, int B, int H, int N, int d, bool causal,
                            float scale, hipStream_t stream);
+
+hipError_t launch_bwd_bf16_varlen(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk,
+                                  void* dv, float* dvec, float* lse2, const int* cu_seqlens,
+                                  int nseq, int max_seqlen, int B, int H, int N, int d,
+                                  bool causal, float scale, hipStream_t stream);
 
 constexpr int kBwdRowPad = 64;
 

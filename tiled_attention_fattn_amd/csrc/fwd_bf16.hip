@@ -34,6 +34,10 @@
 //    innovation 2: loads hidden behind compute).
 //  * Causal: key tiles past the workgroup's last query are never loaded; the
 //    element mask is applied only on tiles that cross the diagonal.
+//  * Packed variable-length sequences (VARLEN): the grid runs over (head,
+//    segment, query tile) and each workgroup works on its segment as on a
+//    sequence of its own (base rows offset to the segment start, length =
+//    the segment's), so no tile ever mixes two segments.
 #include <type_traits>
 
 #include "fattn_device.hpp"
@@ -100,11 +104,12 @@ __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c_log2,
   return la + lb;
 }
 
-template <int D, bool CAUSAL, int EXPM>
+template <int D, bool CAUSAL, int EXPM, bool VARLEN>
 __global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
-                     int N, int BH, int n_qtiles, float c_log2) {
+                     int N, int BH, int n_qtiles, float c_log2, const int* __restrict__ cu,
+                     int nseq) {
   constexpr int KD = D / 16;          // MFMA k-steps over the head dimension
   constexpr int RB = D * 2;           // bytes per K/V row
   constexpr int TILE = kFwdBN * RB;
@@ -119,21 +124,32 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int h = lane >> 5, c = lane & 31;
 
-  // Workgroup → (head, query tile). Consecutive workgroup ids go to different
-  // XCDs; the remap gives each XCD a contiguous run of logical tiles so the
-  // tiles of one head share that XCD's L2. Causal: heaviest tiles first.
-  const int total = n_qtiles * BH;
+  // Workgroup → (head[, segment], query tile). Consecutive workgroup ids go
+  // to different XCDs; the remap gives each XCD a contiguous run of logical
+  // tiles so the tiles of one head share that XCD's L2. Causal: heaviest
+  // tiles first.
+  const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
   int logical = blockIdx.x;
   if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int bh = logical / n_qtiles;
-  int qt = logical - bh * n_qtiles;
+  const int unit = logical / n_qtiles;
+  int qt = logical - unit * n_qtiles;
   if (CAUSAL) qt = n_qtiles - 1 - qt;
+  const int bh = VARLEN ? unit / nseq : unit;
+  // Rows [row0, row0 + L) of the head: the whole head, or one segment (its
+  // offsets clamped to [0, N] so that no offset can address outside the head).
+  int row0 = 0, L = N;
+  if constexpr (VARLEN) {
+    const int sg = unit - bh * nseq;
+    row0 = min(max(cu[sg], 0), N);
+    L = min(max(cu[sg + 1], row0), N) - row0;
+  }
+  const int q_start = qt * kFwdBM;
+  if (q_start >= L) return;  // whole workgroup: a segment shorter than the grid's longest
 
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = ((size_t)bh * N + row0) * D;
   const bf16* Qh = Q + head;
   const bf16* Kh = K + head;
   const bf16* Vh = V + head;
-  const int q_start = qt * kFwdBM;
   const int q0 = q_start + wave * kFwdQW;
   const int qi = q0 + c;  // this lane's query
 
@@ -141,7 +157,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   bf16x8 qr[KD];
 #pragma unroll
   for (int kk = 0; kk < KD; ++kk)
-    qr[kk] = qi < N ? *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
+    qr[kk] = qi < L ? *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
 
   // Per-lane LDS offsets, constant over the loop (the swizzle depends on the
   // row only through bits that do not change between the 32-row tiles or the
@@ -159,17 +175,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int dt = 0; dt < DT; ++dt)
       voff[hf][dt] = tile_off<D>(tr_row + 8 * hf, 4 * dt + tr_chunk) + tr_sub;
 
-  const int kv_end = CAUSAL ? min(N, q_start + kFwdBM) : N;
+  const int kv_end = CAUSAL ? min(L, q_start + kFwdBM) : L;
   const int n_kv = (kv_end + kFwdBN - 1) / kFwdBN;
   // First tile whose scores need the element mask (ragged end or diagonal).
-  const int first_masked = CAUSAL ? min(q_start / kFwdBN, N / kFwdBN) : N / kFwdBN;
+  const int first_masked = CAUSAL ? min(q_start / kFwdBN, L / kFwdBN) : L / kFwdBN;
 
   // Global → LDS without staging registers: each wave moves 1 KB (64 lanes ×
   // 16 B) per load straight into LDS at a wave-uniform base. The source is a
-  // buffer resource starting at the tile's first row and ending at row N, so
-  // rows past N read as zero (range check) and the per-lane byte offset is a
-  // loop constant; the swizzle is applied on the source side (the XOR
-  // swizzle is its own inverse).
+  // buffer resource starting at the tile's first row and ending at row L (the
+  // end of the sequence or segment), so rows past L read as zero (range
+  // check) and the per-lane byte offset is a loop constant; the swizzle is
+  // applied on the source side (the XOR swizzle is its own inverse).
   constexpr int ROWS_PER_LOAD = 1024 / RB;          // rows per 1 KB wave load
   constexpr int LOADS = TILE / 1024 / kFwdWaves;    // wave loads per tensor per tile
   int ld_off[LOADS];
@@ -180,7 +196,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   auto gload = [&](const bf16* src, char* dst_tile, int j) __device__ {
     const int key0 = j * kFwdBN;
-    buffer_to_lds<LOADS>(src + (size_t)key0 * D, (N - key0) * RB, dst_tile, ld_off, wave * LOADS);
+    buffer_to_lds<LOADS>(src + (size_t)key0 * D, (L - key0) * RB, dst_tile, ld_off, wave * LOADS);
   };
 
   SubTile<DT> st;
@@ -214,7 +230,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   __syncthreads();
   f32x16 s[2];
   scores(k_lds, s);
-  if (first_masked == 0) mask_tile<CAUSAL>(s, 0, N, qi, h);
+  if (first_masked == 0) mask_tile<CAUSAL>(s, 0, L, qi, h);
   st.m_c = tile_max(s);
 
   // Conditional rescale (FlashAttention-4 gist, technical summary 2.B). The
@@ -233,16 +249,16 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int key = key0 + t * 32 + c;
-        const bf16* krow = Kh + (size_t)min(key, N - 1) * D + 8 * h;
+        const bf16* krow = Kh + (size_t)min(key, L - 1) * D + 8 * h;
         s[t] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) {
           bf16x8 a = *(const bf16x8*)(krow + kk * 16);
-          if (key >= N) a = bf16x8{};
+          if (key >= L) a = bf16x8{};
           s[t] = mfma32(a, qr[kk], s[t]);
         }
       }
-      if (j >= first_masked) mask_tile<CAUSAL>(s, key0, N, qi, h);
+      if (j >= first_masked) mask_tile<CAUSAL>(s, key0, L, qi, h);
       const float m_new = fmaxf(st.m_c, tile_max(s));
       const float alpha = exp2_hw(st.m_c - m_new);
 #pragma unroll
@@ -284,7 +300,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       // letting them sink past the branches into the PV block.
 #pragma unroll
       for (int ks = 0; ks < NS; ++ks) asm volatile("" ::"v"(p[ks]));
-      if (j + 1 >= first_masked) mask_tile<CAUSAL>(ns, (j + 1) * kFwdBN, N, qi, h);
+      if (j + 1 >= first_masked) mask_tile<CAUSAL>(ns, (j + 1) * kFwdBN, L, qi, h);
     }
     guard(j, p, lt);
 
@@ -327,7 +343,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // Epilogue: O = Oᵀ/l (lane holds d = 32dt + 8(r/4) + 4h + r%4 of its query).
   const float l = half_sum(st.l_part);
   const float inv = 1.0f / l;
-  if (qi < N) {
+  if (qi < L) {
     bf16* Orow = O + head + (size_t)qi * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -338,41 +354,58 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         w[1] = (int)pack_bf16x2(st.o[dt][4 * g + 2] * inv, st.o[dt][4 * g + 3] * inv);
         *(i32x2*)(Orow + 32 * dt + 8 * g + 4 * h) = w;
       }
-    if (h == 0) LSE[(size_t)bh * N + qi] = (st.m_c + __builtin_log2f(l)) * kLn2;
+    if (h == 0) LSE[(size_t)bh * N + row0 + qi] = (st.m_c + __builtin_log2f(l)) * kLn2;
   }
 }
 
-template <int D, bool CAUSAL, int EXPM>
+template <int D, bool CAUSAL, int EXPM, bool VARLEN>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int BH, int N, float scale, hipStream_t stream) {
-  const int n_qtiles = (N + kFwdBM - 1) / kFwdBM;
-  const dim3 grid(n_qtiles * BH), block(64 * kFwdWaves);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXPM>), grid, block, 0, stream,
+                               int BH, int N, float scale, const int* cu, int nseq, int max_len,
+                               hipStream_t stream) {
+  const int n_qtiles = ((VARLEN ? max_len : N) + kFwdBM - 1) / kFwdBM;
+  const dim3 grid(n_qtiles * BH * (VARLEN ? nseq : 1)), block(64 * kFwdWaves);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXPM, VARLEN>), grid, block, 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, BH, n_qtiles,
-                     scale * kLog2e);
+                     scale * kLog2e, cu, nseq);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool CAUSAL, bool VARLEN>
+static hipError_t launch_fwd_e(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int BH, int N, float scale, int exp_mode, const int* cu, int nseq,
+                               int max_len, hipStream_t stream) {
+  if (exp_mode == EXP_POLY)
+    return launch_fwd_t<D, CAUSAL, EXP_POLY, VARLEN>(q, k, v, o, lse, BH, N, scale, cu, nseq, max_len, stream);
+  if (exp_mode == EXP_SPLIT)
+    return launch_fwd_t<D, CAUSAL, EXP_SPLIT, VARLEN>(q, k, v, o, lse, BH, N, scale, cu, nseq, max_len, stream);
+  return launch_fwd_t<D, CAUSAL, EXP_HW, VARLEN>(q, k, v, o, lse, BH, N, scale, cu, nseq, max_len, stream);
+}
+
+template <int D, bool VARLEN>
 static hipError_t launch_fwd_d(const void* q, const void* k, const void* v, void* o, float* lse,
                                int BH, int N, bool causal, float scale, int exp_mode,
-                               hipStream_t stream) {
-  if (causal) {
-    if (exp_mode == EXP_POLY) return launch_fwd_t<D, true, EXP_POLY>(q, k, v, o, lse, BH, N, scale, stream);
-    if (exp_mode == EXP_SPLIT) return launch_fwd_t<D, true, EXP_SPLIT>(q, k, v, o, lse, BH, N, scale, stream);
-    return launch_fwd_t<D, true, EXP_HW>(q, k, v, o, lse, BH, N, scale, stream);
-  }
-  if (exp_mode == EXP_POLY) return launch_fwd_t<D, false, EXP_POLY>(q, k, v, o, lse, BH, N, scale, stream);
-  if (exp_mode == EXP_SPLIT) return launch_fwd_t<D, false, EXP_SPLIT>(q, k, v, o, lse, BH, N, scale, stream);
-  return launch_fwd_t<D, false, EXP_HW>(q, k, v, o, lse, BH, N, scale, stream);
+                               const int* cu, int nseq, int max_len, hipStream_t stream) {
+  if (causal)
+    return launch_fwd_e<D, true, VARLEN>(q, k, v, o, lse, BH, N, scale, exp_mode, cu, nseq, max_len, stream);
+  return launch_fwd_e<D, false, VARLEN>(q, k, v, o, lse, BH, N, scale, exp_mode, cu, nseq, max_len, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, bool causal, float scale, int exp_mode,
                            hipStream_t stream) {
   const int BH = B * H;
-  if (d == 64) return launch_fwd_d<64>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, stream);
-  return launch_fwd_d<128>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, stream);
+  if (d == 64) return launch_fwd_d<64, false>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, nullptr, 1, N, stream);
+  return launch_fwd_d<128, false>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, nullptr, 1, N, stream);
+}
+
+hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int* cu_seqlens, int nseq, int max_seqlen,
+                                  int B, int H, int N, int d, bool causal, float scale,
+                                  int exp_mode, hipStream_t stream) {
+  const int BH = B * H;
+  if (d == 64)
+    return launch_fwd_d<64, true>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, cu_seqlens, nseq, max_seqlen, stream);
+  return launch_fwd_d<128, true>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, cu_seqlens, nseq, max_seqlen, stream);
 }
 
 }  // namespace fattn
