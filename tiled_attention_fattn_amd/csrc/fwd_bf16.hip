@@ -20,7 +20,11 @@
 //  * Software pipeline over 64-key tiles: the exponentials of tile j run
 //    beside the MFMAs of S(j+1), then PV(j) (FlashAttention-4 news page,
 //    "Cómo Together AI resolvió el problema": overlap the tensor units, the
-//    exponential units and memory).
+//    exponential units and memory). The loop body is written in program
+//    order as pieces of one MFMA each between scheduling fences: every piece
+//    issues the LDS operand read of the MFMA three pieces ahead, and each S
+//    piece also carries its share of the softmax of tile j, so neither an
+//    MFMA's operand latency nor the exponentials stall the MFMA pipe.
 //  * Online softmax in the exp2 domain with conditional rescaling
 //    (FlashAttention-4 gist, technical summary 2.B): the exponent offset
 //    moves only when a tile's probabilities would exceed 2^τ, detected from
@@ -51,9 +55,8 @@ constexpr int kFwdBM = kFwdQW * kFwdWaves;  // query rows per workgroup
 constexpr int kFwdBN = 64;                  // keys per K/V tile
 constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between rescales
 constexpr float kSumGuard = 256.0f;         // 2^kRescaleTau
+constexpr int kLead = 3;                    // LDS operand reads in flight ahead of the MFMAs
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100, SG_TRANS = 0x400 };
 
 // Running softmax state of one 32-query sub-tile (per lane: one query).
 template <int DT>
@@ -102,6 +105,22 @@ __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c_log2,
       p[2 * t + half] = __builtin_bit_cast(bf16x8, packed);
     }
   return la + lb;
+}
+
+// One element pair x (0..15) of softmax_exp: tile t = x/8, register half
+// (x/4)%2, pair e = x%4; same arithmetic, for interleaving with MFMAs.
+template <int EXPM>
+__device__ __forceinline__ void softmax_exp_pair(const f32x16 (&s)[2], float c_log2, float m_c,
+                                                 int x, i32x4 (&pk)[4], float& la, float& lb) {
+  const int t = x / 8, half = (x / 4) % 2, e = x % 4;
+  constexpr int M = EXPM == EXP_SPLIT ? EXP_HW : EXPM;
+  const float x0 = fmaf(s[t][half * 8 + 2 * e], c_log2, -m_c);
+  const float x1 = fmaf(s[t][half * 8 + 2 * e + 1], c_log2, -m_c);
+  const float p0 = (EXPM == EXP_SPLIT && e == 3) ? exp2_poly(x0) : exp2_sel<M>(x0);
+  const float p1 = (EXPM == EXP_SPLIT && e == 3) ? exp2_poly(x1) : exp2_sel<M>(x1);
+  la += p0;
+  lb += p1;
+  pk[2 * t + half][e] = (int)pack_bf16x2(p0, p1);
 }
 
 template <int D, bool CAUSAL, int EXPM, bool VARLEN>
@@ -272,9 +291,24 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     st.l_part += lt;
   };
 
-  // Iteration j: exp(S(j)) ∥ S(j+1) on the MFMA pipe, the guard, then PV(j).
-  // The last iteration (no tile j+1) is peeled so that each phase is one
-  // basic block the scheduler can interleave.
+  // Iteration j: exp(S(j)) ∥ S(j+1) on the MFMA pipe, the guard, then PV(j),
+  // laid out in program order as pieces of one MFMA each separated by
+  // scheduling fences. Each piece issues the LDS operand read of the MFMA
+  // kLead pieces ahead (the reads of the first PV MFMAs ride on the last S
+  // pieces), so no MFMA waits for its own operand, and the S pieces carry
+  // one element pair of the softmax of tile j each. The last iteration (no
+  // tile j+1) is peeled.
+  constexpr int NSP = 2 * KD;     // S pieces: key half t = i/KD, k-step kk = i%KD
+  static_assert(16 % NSP == 0, "softmax pairs must spread evenly over the S pieces");
+  constexpr int NPV = NS * DT;    // PV pieces: key step ks = i/DT, d tile dt = i%DT
+  auto kread = [&](const char* kt, int i) __device__ {
+    return *(const bf16x8*)(kt + (i / KD) * 32 * RB + koff[i % KD]);
+  };
+  auto vread = [&](const char* vt, int i, bf16x4 (&ta)[NPV][2]) __device__ {
+    const char* base = vt + 16 * (i / DT) * RB;
+    ta[i][0] = lds_read_tr16(base + voff[0][i % DT]);
+    ta[i][1] = lds_read_tr16(base + voff[1][i % DT]);
+  };
   auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
     constexpr int PAR = decltype(parity_tag)::value;  // j & 1, a compile-time slot index
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
@@ -285,41 +319,55 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       if (j + 2 < n_kv) gload(Kh, k_lds + PAR * TILE, j + 2);
       gload(Vh, v_lds + (PAR ^ 1) * TILE, j + 1);
     }
-    bf16x8 p[NS];
+    const char* kt = k_lds + (PAR ^ 1) * TILE;
+    const char* vt = v_lds + PAR * TILE;
+    i32x4 pk[4];
+    float la = 0.0f, lb = 0.0f;
     f32x16 ns[2];
-    float lt = softmax_exp<EXPM>(s, c_log2, st.m_c, p);
+    bf16x4 ta[NPV][2];
     if constexpr (HAS_NEXT) {
-      scores(k_lds + (PAR ^ 1) * TILE, ns);
+      bf16x8 ra[NSP];
 #pragma unroll
-      for (int i = 0; i < 2 * KD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU | SG_TRANS, 4, 0);
+      for (int i = 0; i < kLead; ++i) ra[i] = kread(kt, i);
+#pragma unroll
+      for (int i = 0; i < NSP; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int t = i / KD, kk = i % KD;
+        ns[t] = mfma32(ra[i], qr[kk], kk == 0 ? f32x16{} : ns[t]);
+        if (i + kLead < NSP) ra[i + kLead] = kread(kt, i + kLead);
+        else vread(vt, i + kLead - NSP, ta);
+        // 16 element pairs over the NSP pieces; each kept beside its MFMA
+        // instead of sinking to its use.
+#pragma unroll
+        for (int x = i * 16 / NSP; x < (i + 1) * 16 / NSP; ++x) {
+          softmax_exp_pair<EXPM>(s, c_log2, st.m_c, x, pk, la, lb);
+          asm volatile("" ::"v"(pk[x / 4][x % 4]), "v"(la), "v"(lb));
+        }
       }
-      // Keep the exponentials in this block (next to the S MFMAs) instead of
-      // letting them sink past the branches into the PV block.
-#pragma unroll
-      for (int ks = 0; ks < NS; ++ks) asm volatile("" ::"v"(p[ks]));
+      __builtin_amdgcn_sched_barrier(0);
       if (j + 1 >= first_masked) mask_tile<CAUSAL>(ns, (j + 1) * kFwdBN, L, qi, h);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLead; ++i) vread(vt, i, ta);
+#pragma unroll
+      for (int x = 0; x < 16; ++x) softmax_exp_pair<EXPM>(s, c_log2, st.m_c, x, pk, la, lb);
     }
+    bf16x8 p[NS];
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) p[ks] = __builtin_bit_cast(bf16x8, pk[ks]);
+    float lt = la + lb;
     guard(j, p, lt);
 
-    // PV(j): Vᵀ operands by transpose reads.
-    const char* vt = v_lds + PAR * TILE;
+    // PV(j): Vᵀ operands by transpose reads, kLead pieces ahead.
 #pragma unroll
-    for (int ks = 0; ks < NS; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x4 lo = lds_read_tr16(vt + 16 * ks * RB + voff[0][dt]);
-        const bf16x4 hi = lds_read_tr16(vt + 16 * ks * RB + voff[1][dt]);
-        st.o[dt] = mfma32(concat(lo, hi), p[ks], st.o[dt]);
-      }
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = i / DT, dt = i % DT;
+      st.o[dt] = mfma32(concat(ta[i][0], ta[i][1]), p[ks], st.o[dt]);
+      if (i + kLead < NPV) vread(vt, i + kLead, ta);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (HAS_NEXT) {
-#pragma unroll
-      for (int i = 0; i < NS * DT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      }
       s[0] = ns[0];
       s[1] = ns[1];
       wait_vmem();
