@@ -27,8 +27,14 @@ offsets cu_seqlens = [c_0, …, c_n] split the rows into segments
 segment (and, when causal, j ≤ i). Each segment is then an independent
 attention problem; rows outside every segment see no key.
 
-A row with no visible key (impossible for square causal attention, kept for
-completeness) has O = 0, LSE = −∞ and contributes no gradient.
+Block-sparse attention (the pages name it, like varlen, only as a variant
+the tiled design enables): a 0/1 block mask M over blocks of `block` query
+rows × `block` key rows (block = 128 for the kernels); reading: key j is
+visible to query i iff M[i // block, j // block] ≠ 0 (and the causal and
+segment conditions, when given, also hold).
+
+A row with no visible key (impossible for square causal attention, possible
+under a block mask) has O = 0, LSE = −∞ and contributes no gradient.
 
 All inputs are float64 arrays of shape [B, H, N, d]; they are the exact values
 of the bf16 inputs the GPU consumes.
@@ -46,11 +52,12 @@ def segment_ids(n, cu_seqlens):
     return ids
 
 
-def _scores(q, k, causal, scale, rows=None, seg=None):
-    """S = scale·q·kᵀ for one head with the causal and segment masks applied.
+def _scores(q, k, causal, scale, rows=None, seg=None, bmask=None, block=128):
+    """S = scale·q·kᵀ for one head with the causal, segment and block masks.
 
     rows: the global row index of each query row (default 0..n_q−1); seg: the
-    segment id of every key row (None: one segment holding all rows).
+    segment id of every key row (None: one segment holding all rows); bmask:
+    the head's block mask [⌈N/block⌉, ⌈N/block⌉] (None: every block visible).
     """
     s = scale * (q @ k.T)
     n_q, n_k = s.shape
@@ -61,7 +68,19 @@ def _scores(q, k, causal, scale, rows=None, seg=None):
     if seg is not None:
         sq = seg[r][:, None]
         s = np.where((seg[None, :] == sq) & (sq >= 0), s, -np.inf)
+    if bmask is not None:
+        vis = np.asarray(bmask)[r[:, None] // block, np.arange(n_k)[None, :] // block] != 0
+        s = np.where(vis, s, -np.inf)
     return s
+
+
+def _head_mask(block_mask, b, h, H):
+    """The block mask of head (b, h): one [nb, nb] mask for all heads, or
+    [B·H, nb, nb] with one per head."""
+    if block_mask is None:
+        return None
+    m = np.asarray(block_mask)
+    return m if m.ndim == 2 else m[b * H + h]
 
 
 def softmax_rows(s):
@@ -80,11 +99,13 @@ def softmax_rows(s):
     return p, lse
 
 
-def attention_forward(q, k, v, causal, scale, cu_seqlens=None):
-    """O = softmax(scale·Q·Kᵀ [causal] [segments]) · V and LSE, per (b, h), in float64.
+def attention_forward(q, k, v, causal, scale, cu_seqlens=None, block_mask=None, block=128):
+    """O = softmax(scale·Q·Kᵀ [causal] [segments] [block mask]) · V and LSE,
+    per (b, h), in float64.
 
     q, k, v: [B, H, N, d] float64; cu_seqlens: optional segment offsets (the
-    same for every (b, h)). Returns (O [B,H,N,d], LSE [B,H,N]).
+    same for every (b, h)); block_mask: optional 0/1 block mask, [nb, nb] for
+    all heads or [B·H, nb, nb], nb = ⌈N/block⌉. Returns (O [B,H,N,d], LSE [B,H,N]).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -95,13 +116,15 @@ def attention_forward(q, k, v, causal, scale, cu_seqlens=None):
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            s = _scores(q[b, h], k[b, h], causal, scale, seg=seg)
+            s = _scores(q[b, h], k[b, h], causal, scale, seg=seg,
+                        bmask=_head_mask(block_mask, b, h, H), block=block)
             p, lse[b, h] = softmax_rows(s)
             o[b, h] = p @ v[b, h]
     return o, lse
 
 
-def attention_forward_rows(q, k, v, causal, scale, b, h, rows, cu_seqlens=None):
+def attention_forward_rows(q, k, v, causal, scale, b, h, rows, cu_seqlens=None, block_mask=None,
+                           block=128):
     """Forward for selected query rows of one head (b, h); same definition.
 
     Used to check outputs at full problem sizes on sampled rows. Returns
@@ -112,12 +135,13 @@ def attention_forward_rows(q, k, v, causal, scale, b, h, rows, cu_seqlens=None):
     kh = np.asarray(k[b, h], dtype=np.float64)
     vh = np.asarray(v[b, h], dtype=np.float64)
     seg = None if cu_seqlens is None else segment_ids(kh.shape[0], cu_seqlens)
-    s = _scores(qh, kh, causal, scale, rows=rows, seg=seg)
+    s = _scores(qh, kh, causal, scale, rows=rows, seg=seg,
+                bmask=_head_mask(block_mask, b, h, np.asarray(q).shape[1]), block=block)
     p, lse = softmax_rows(s)
     return p @ vh, lse
 
 
-def attention_backward(q, k, v, do, causal, scale, cu_seqlens=None):
+def attention_backward(q, k, v, do, causal, scale, cu_seqlens=None, block_mask=None, block=128):
     """Gradients of ⟨O, dO⟩ with respect to Q, K, V, in float64.
 
     P is formed again from the definition (not from any saved statistic).
@@ -135,7 +159,8 @@ def attention_backward(q, k, v, do, causal, scale, cu_seqlens=None):
     seg = None if cu_seqlens is None else segment_ids(N, cu_seqlens)
     for b in range(B):
         for h in range(H):
-            s = _scores(q[b, h], k[b, h], causal, scale, seg=seg)
+            s = _scores(q[b, h], k[b, h], causal, scale, seg=seg,
+                        bmask=_head_mask(block_mask, b, h, H), block=block)
             p, _ = softmax_rows(s)
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T

@@ -11,11 +11,14 @@ computation from the vectorised oracle.
 import math
 
 
-def brute_forward(q, k, v, causal, scale, cu_seqlens=None):
+def brute_forward(q, k, v, causal, scale, cu_seqlens=None, block_mask=None, block=128):
     """q, k, v: nested lists [N][d] (one head). Returns (O [N][d], LSE [N]).
 
     cu_seqlens: optional segment offsets; key j then counts for query i only
-    if some segment [c_s, c_{s+1}) holds both.
+    if some segment [c_s, c_{s+1}) holds both. block_mask: optional nested
+    list [nb][nb] of 0/1; key j counts for query i only if the entry of
+    their blocks (block rows each) is 1. A query that sees no key gets
+    O = 0 and LSE = −∞.
     """
     n = len(q)
     d = len(q[0])
@@ -26,6 +29,9 @@ def brute_forward(q, k, v, causal, scale, cu_seqlens=None):
         weights = []
         for j in range(n):
             if causal and j > i:
+                weights.append(0.0)
+                continue
+            if block_mask is not None and block_mask[i // block][j // block] == 0:
                 weights.append(0.0)
                 continue
             if cu_seqlens is not None:
@@ -43,6 +49,9 @@ def brute_forward(q, k, v, causal, scale, cu_seqlens=None):
         total = 0.0
         for w in weights:
             total += w
+        if total == 0.0:
+            lse[i] = -math.inf
+            continue
         lse[i] = math.log(total)
         for c in range(dv):
             acc = 0.0

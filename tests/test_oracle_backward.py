@@ -154,3 +154,33 @@ def test_varlen_finite_differences():
             lm = loss(args["q"], args["k"], args["v"])
             num[idx] = (lp - lm) / (2 * h)
         np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_block_mask_finite_differences_and_empty_rows():
+    # Central differences through the block-masked forward; rows of a block
+    # row that sees no key get zero dQ and contribute nothing to dK, dV.
+    block = 3
+    m = np.array([[1, 0, 1], [0, 0, 0], [1, 1, 0]], dtype=np.uint8)
+    rng = np.random.default_rng(79)
+    q, k, v, do = (rng.standard_normal((1, 1, 8, 3)) for _ in range(4))
+    for causal in (False, True):
+        dq, dk, dv, _ = attention_backward(q, k, v, do, causal, 0.7, block_mask=m, block=block)
+        assert np.all(dq[0, 0, 3:6] == 0)
+
+        def loss(qq, kk, vv):
+            return float(np.sum(attention_forward(qq, kk, vv, causal, 0.7, block_mask=m,
+                                                  block=block)[0] * do))
+        h = 1e-6
+        for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args = {"q": q, "k": k, "v": v}
+                args[name] = xp
+                lp = loss(args["q"], args["k"], args["v"])
+                args[name] = xm
+                lm = loss(args["q"], args["k"], args["v"])
+                num[idx] = (lp - lm) / (2 * h)
+            np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)

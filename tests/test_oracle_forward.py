@@ -203,3 +203,60 @@ def test_varlen_rows_variant_and_uncovered_rows():
     np.testing.assert_allclose(rl, lse[0, 1][rows], rtol=0, atol=1e-14)
     # rows 20..23 lie in no segment: they see no key
     assert np.all(o[:, :, 20:] == 0) and np.all(np.isneginf(lse[:, :, 20:]))
+
+
+# Block-sparse masks (blocks of `block` rows × `block` keys).
+def _bmask(nb, seed, density=0.5):
+    return (np.random.default_rng(seed).random((nb, nb)) < density).astype(np.uint8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seed", [61, 62, 63])
+def test_block_mask_matches_brute_force(seed, causal):
+    n, d, block = 14, 3, 4
+    q, k, v = (_rand((1, 1, n, d), seed + s) for s in (0, 1, 2))
+    m = _bmask(4, seed)
+    m[0, 0] = 0  # a block row that may see nothing
+    o, lse = attention_forward(q, k, v, causal, 0.8, block_mask=m, block=block)
+    bo, bl = brute_forward(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), causal, 0.8,
+                           block_mask=m.tolist(), block=block)
+    np.testing.assert_allclose(o[0, 0], np.array(bo), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], np.array(bl), rtol=0, atol=1e-13)
+
+
+def test_block_mask_special_cases():
+    # all ones = plain; block-diagonal = packed segments of one block each;
+    # lower-triangular blocks under the causal mask = causal; rows of a block
+    # row with no visible block see nothing (O = 0, LSE = −∞); per-head masks.
+    n, block = 40, 8
+    q, k, v = (_rand((1, 3, n, 5), s) for s in (71, 72, 73))
+    nb = 5
+    ones = np.ones((nb, nb), np.uint8)
+    for causal in (False, True):
+        a = attention_forward(q, k, v, causal, 0.5, block_mask=ones, block=block)
+        b = attention_forward(q, k, v, causal, 0.5)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    diag = np.eye(nb, dtype=np.uint8)
+    a = attention_forward(q, k, v, False, 0.5, block_mask=diag, block=block)
+    b = attention_forward(q, k, v, False, 0.5, cu_seqlens=list(range(0, n + 1, block)))
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(a[1], b[1], rtol=0, atol=1e-14)
+    tril = np.tril(ones)
+    a = attention_forward(q, k, v, True, 0.5, block_mask=tril, block=block)
+    b = attention_forward(q, k, v, True, 0.5)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-14)
+    m = ones.copy()
+    m[2] = 0
+    o, lse = attention_forward(q, k, v, False, 0.5, block_mask=m, block=block)
+    assert np.all(o[:, :, 16:24] == 0) and np.all(np.isneginf(lse[:, :, 16:24]))
+    per_head = np.stack([ones, diag, tril])
+    o3, l3 = attention_forward(q, k, v, False, 0.5, block_mask=per_head, block=block)
+    for h, mh in enumerate((ones, diag, tril)):
+        oh, lh = attention_forward(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], False, 0.5,
+                                   block_mask=mh, block=block)
+        assert np.array_equal(o3[:, h:h + 1], oh) and np.array_equal(l3[:, h:h + 1], lh)
+    rows = np.array([0, 15, 16, 23, 39])
+    ro, rl = attention_forward_rows(q, k, v, False, 0.5, 0, 1, rows, block_mask=per_head,
+                                    block=block)
+    np.testing.assert_allclose(ro, o3[0, 1][rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(rl, l3[0, 1][rows], rtol=0, atol=1e-14)
