@@ -138,6 +138,25 @@ fattn_status fattn_bwd_varlen(const void* q, const void* k, const void* v,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Block-sparse bf16 forward.
+ *   block_mask  device uint8, one entry per block of 128 queries × 128 keys:
+ *               [nb][nb] shared by every (b, h) (per_head = 0) or
+ *               [B·H][nb][nb] (per_head = 1), nb = ceil(N/128), row-major
+ *               (query block, key block). Non-zero: the keys of the key block
+ *               are visible to the queries of the query block (subject also
+ *               to the causal mask); zero: they are not, and their K/V tiles
+ *               are never loaded.
+ * A query that sees no key gets O = 0 and LSE = −∞ (the convention of the
+ * plain definition for an empty row). Everything else as fattn_fwd. The mask
+ * lives in device memory and is read as given (the caller sizes it).
+ * Supports N <= 32768 (ENOTSUP beyond). There is no block-sparse backward.
+ */
+fattn_status fattn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, const uint8_t* block_mask, int per_head,
+                                   int B, int H, int N, int d, int causal, float scale,
+                                   int exp_mode, void* stream);
+
+/*
  * Forward with fp8 (OCP e4m3fn) operands and bf16 in/out
  * (FlashAttention-3 page, innovation 3).
  *   q, k, v     [B,H,N,d] bf16 inputs; o [B,H,N,d] bf16 output.

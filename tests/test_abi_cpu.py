@@ -166,3 +166,23 @@ def test_bwd_varlen_checks():
     assert call(P, need, nseq=-1) == EINVAL
     assert call(P, need, maxl=N + 1) == EINVAL
     assert call(P, need, dq=MIS) == EINVAL
+
+
+def test_fwd_blocksparse_checks():
+    lib = fa.lib()
+
+    def call(**kw):
+        a = dict(q=P, mask=P, per_head=0, N=300, d=128, causal=0, scale=0.1, exp=0)
+        a.update(kw)
+        return lib.fattn_fwd_blocksparse(a["q"], P, P, P, P, a["mask"], a["per_head"], 1, 2, a["N"],
+                                         a["d"], a["causal"], ctypes.c_float(a["scale"]), a["exp"],
+                                         NUL)
+    assert call(mask=NUL) == EINVAL
+    assert call(per_head=2) == EINVAL
+    assert call(q=MIS) == EINVAL
+    assert call(d=32) == ENOTSUP
+    assert call(N=40000) == ENOTSUP
+    assert call(causal=5) == EINVAL
+    assert call(exp=9) == EINVAL
+    assert call(scale=-2.0) == EINVAL
+    assert fa.lib().fattn_last_error()

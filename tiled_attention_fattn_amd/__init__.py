@@ -10,6 +10,7 @@ an exception is raised.
     o, lse = fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0)
     o, lse = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False)
     dq, dk, dv = bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False)
+    o, lse = fwd_blocksparse(q, k, v, block_mask, causal=False)
 
 Tensors are contiguous CUDA (HIP) bfloat16 [B, H, N, d], d ∈ {64, 128};
 ``scale`` defaults to 1/√d.
@@ -19,7 +20,7 @@ import os
 
 from ._lib import FattnError, lib, lib_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
            "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
            "EXP_AUTO", "EXP_HW", "EXP_POLY", "EXP_SPLIT"]
 
@@ -116,6 +117,37 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, exp_mo
                                      _ptr(cu_seqlens), nseq, int(max_seqlen), B, H, N, d,
                                      int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
                                      _stream(q)))
+    return o, lse_t
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, exp_mode="auto", out=None,
+                    lse=None):
+    """Block-sparse forward: block_mask is a uint8 tensor on the device of q,
+    [nb, nb] for every head or [B*H, nb, nb], nb = ceil(N/128); entry (i, j)
+    non-zero makes key block j visible to query block i. Returns (O, LSE)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16)
+    B, H, N, d = _shape(q)
+    if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
+        raise ValueError("q, k, v must have the same shape")
+    nb = (N + 127) // 128
+    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8 \
+            or not block_mask.is_contiguous() or block_mask.device != q.device \
+            or tuple(block_mask.shape) not in ((nb, nb), (B * H, nb, nb)):
+        raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape ({nb}, {nb}) "
+                         f"or ({B * H}, {nb}, {nb}) on the device of q")
+    per_head = int(block_mask.dim() == 3)
+    scale = float(d ** -0.5 if scale is None else scale)
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(o, "out", torch.bfloat16)
+    _check(lse_t, "lse", torch.float32)
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
+                                          _ptr(block_mask), per_head, B, H, N, d,
+                                          int(bool(causal)), ctypes.c_float(scale),
+                                          _EXP[exp_mode], _stream(q)))
     return o, lse_t
 
 

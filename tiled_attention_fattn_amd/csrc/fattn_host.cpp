@@ -160,6 +160,29 @@ fattn_status fattn_fwd_varlen(const void* q, const void* k, const void* v, void*
                     "fattn_fwd_varlen launch");
 }
 
+fattn_status fattn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, const uint8_t* block_mask, int per_head, int B,
+                                   int H, int N, int d, int causal, float scale, int exp_mode,
+                                   void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  FATTN_TRY(check_ptr(lse, "lse"));
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  if (block_mask == nullptr) return fail(FATTN_EINVAL, "block_mask is NULL");
+  if (per_head != 0 && per_head != 1)
+    return fail(FATTN_EINVAL, "per_head must be 0 or 1 (got %d)", per_head);
+  if (N > 32768) return fail(FATTN_ENOTSUP, "block-sparse forward supports N <= 32768 (got %d)", N);
+  FATTN_TRY(check_exp_mode(exp_mode));
+  FATTN_TRY(check_device());
+  const int mode = exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode;
+  return hip_status(fattn::launch_fwd_bf16_blocksparse(q, k, v, o, lse, block_mask,
+                                                       per_head != 0, B, H, N, d, causal != 0,
+                                                       scale, mode, (hipStream_t)stream),
+                    "fattn_fwd_blocksparse launch");
+}
+
 size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
@@ -313,6 +336,6 @@ const char* fattn_strerror(int status) {
 
 const char* fattn_last_error(void) { return g_last_error; }
 
-int fattn_version(void) { return 300; }
+int fattn_version(void) { return 400; }
 
 }  // extern "C"

@@ -19,6 +19,13 @@ hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, v
                                   int B, int H, int N, int d, bool causal, float scale,
                                   int exp_mode, hipStream_t stream);
 
+// Block-sparse forward: block_mask uint8 [⌈N/128⌉][⌈N/128⌉] (one for all
+// heads) or [B*H][⌈N/128⌉][⌈N/128⌉] (per_head); non-zero = visible.
+hipError_t launch_fwd_bf16_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const uint8_t* block_mask, bool per_head,
+                                       int B, int H, int N, int d, bool causal, float scale,
+                                       int exp_mode, hipStream_t stream);
+
 // Backward: `dvec` and `lse2` fp32 [B,H,Npad] live in the caller's workspace
 // (Npad = N rounded up to kBwdRowPad).
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

@@ -56,6 +56,8 @@ constexpr int kFwdBN = 64;                  // keys per K/V tile
 constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between rescales
 constexpr float kSumGuard = 256.0f;         // 2^kRescaleTau
 constexpr int kLead = 3;                    // LDS operand reads in flight ahead of the MFMAs
+constexpr int kMaskBlock = 128;             // block-mask granularity (queries and keys)
+constexpr int kMaskWords = 4;               // 64-block words of a mask row: N <= 32768
 
 
 // Running softmax state of one 32-query sub-tile (per lane: one query).
@@ -123,12 +125,14 @@ __device__ __forceinline__ void softmax_exp_pair(const f32x16 (&s)[2], float c_l
   pk[2 * t + half][e] = (int)pack_bf16x2(p0, p1);
 }
 
-template <int D, bool CAUSAL, int EXPM, bool VARLEN>
+template <int D, bool CAUSAL, int EXPM, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
                      int N, int BH, int n_qtiles, float c_log2, const int* __restrict__ cu,
-                     int nseq) {
+                     int nseq, const uint8_t* __restrict__ bmask, long mask_stride) {
+  static_assert(!(VARLEN && SPARSE), "block masks apply to whole sequences");
+  static_assert(!SPARSE || kFwdBM == kMaskBlock, "one query tile per mask block row");
   constexpr int KD = D / 16;          // MFMA k-steps over the head dimension
   constexpr int RB = D * 2;           // bytes per K/V row
   constexpr int TILE = kFwdBN * RB;
@@ -241,15 +245,61 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     return half_max(mx) * c_log2;
   };
 
-  // Prologue: K0, K1, V0 in flight; S(0); running max from tile 0.
-  gload(Kh, k_lds, 0);
-  if (n_kv > 1) gload(Kh, k_lds + TILE, 1);
-  gload(Vh, v_lds, 0);
+  // Key tiles in processing order: all of [0, n_kv), or under a block mask
+  // only those whose 128-key block is visible to this 128-query block (the
+  // workgroup's row of the mask; a tile of 64 keys lies in block j/2). The
+  // row is read once into four 64-bit ballots (up to 256 blocks), so the
+  // walk over it is scalar work that waits on no memory.
+  uint64_t mb[kMaskWords] = {};
+  if constexpr (SPARSE) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const uint8_t* mrow = bmask + bh * mask_stride + (long)qt * nb;
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) {
+      const int b = w * 64 + lane;
+      mb[w] = __ballot(b < nb && mrow[b] != 0);
+    }
+  }
+  auto next_tile = [&](int j) __device__ {
+    if constexpr (SPARSE) {
+      if (j >= n_kv) return n_kv;
+      const int b = j >> 1;
+#pragma unroll
+      for (int w = 0; w < kMaskWords; ++w) {
+        if (w < (b >> 6)) continue;
+        uint64_t bits = mb[w];
+        if (w == (b >> 6)) bits &= ~0ull << (b & 63);
+        if (bits != 0) {
+          const int nbk = w * 64 + __builtin_ctzll(bits);
+          return min(nbk == b ? j : 2 * nbk, n_kv);
+        }
+      }
+      return n_kv;
+    }
+    return j;
+  };
+  const int c0 = next_tile(0), c1 = next_tile(c0 + 1);
+  if (c0 >= n_kv) {  // no visible key for any row of the block: O = 0, LSE = −∞
+    if (qi < L) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(i32x2*)(O + head + (size_t)qi * D + 32 * dt + 8 * g + 4 * h) = i32x2{};
+      if (h == 0) LSE[(size_t)bh * N + row0 + qi] = -INFINITY;
+    }
+    return;
+  }
+
+  // Prologue: K(c0), K(c1), V(c0) in flight; S(c0); running max from it.
+  gload(Kh, k_lds, c0);
+  if (c1 < n_kv) gload(Kh, k_lds + TILE, c1);
+  gload(Vh, v_lds, c0);
   wait_vmem();
   __syncthreads();
   f32x16 s[2];
   scores(k_lds, s);
-  if (first_masked == 0) mask_tile<CAUSAL>(s, 0, L, qi, h);
+  if (c0 >= first_masked) mask_tile<CAUSAL>(s, c0 * kFwdBN, L, qi, h);
   st.m_c = tile_max(s);
 
   // Conditional rescale (FlashAttention-4 gist, technical summary 2.B). The
@@ -309,15 +359,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     ta[i][0] = lds_read_tr16(base + voff[0][i % DT]);
     ta[i][1] = lds_read_tr16(base + voff[1][i % DT]);
   };
-  auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
-    constexpr int PAR = decltype(parity_tag)::value;  // j & 1, a compile-time slot index
+  // Tiles j (this iteration), jn and jn2 (the next two in processing order;
+  // j + 1 and j + 2 without a block mask); PAR is the position's parity.
+  auto iteration = [&](int j, int jn, int jn2, auto parity_tag, auto has_next_tag) __device__ {
+    constexpr int PAR = decltype(parity_tag)::value;  // a compile-time slot index
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    // Loads for later iterations: K(j+2) into the K slot that held K(j)
-    // (consumed by S(j) one iteration ago), V(j+1) into the V slot that held
-    // V(j−1) (consumed by PV(j−1) one iteration ago).
+    // Loads for later iterations: K(jn2) into the K slot that held K(j)
+    // (consumed by S(j) one iteration ago), V(jn) into the V slot that held
+    // the previous tile's V (consumed by its PV one iteration ago).
     if constexpr (HAS_NEXT) {
-      if (j + 2 < n_kv) gload(Kh, k_lds + PAR * TILE, j + 2);
-      gload(Vh, v_lds + (PAR ^ 1) * TILE, j + 1);
+      if (jn2 < n_kv) gload(Kh, k_lds + PAR * TILE, jn2);
+      gload(Vh, v_lds + (PAR ^ 1) * TILE, jn);
     }
     const char* kt = k_lds + (PAR ^ 1) * TILE;
     const char* vt = v_lds + PAR * TILE;
@@ -345,7 +397,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 >= first_masked) mask_tile<CAUSAL>(ns, (j + 1) * kFwdBN, L, qi, h);
+      if (jn >= first_masked) mask_tile<CAUSAL>(ns, jn * kFwdBN, L, qi, h);
     } else {
 #pragma unroll
       for (int i = 0; i < kLead; ++i) vread(vt, i, ta);
@@ -376,16 +428,50 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int j = 0;
-  for (; j + 2 < n_kv; j += 2) {
-    iteration(j, I0{}, std::true_type{});
-    iteration(j + 1, I1{}, std::true_type{});
-  }
-  if (j + 1 < n_kv) {
-    iteration(j, I0{}, std::true_type{});
-    iteration(j + 1, I1{}, std::false_type{});
+  if constexpr (!SPARSE) {
+    int j = 0;
+    for (; j + 2 < n_kv; j += 2) {
+      iteration(j, j + 1, j + 2, I0{}, std::true_type{});
+      iteration(j + 1, j + 2, j + 3, I1{}, std::true_type{});
+    }
+    if (j + 1 < n_kv) {
+      iteration(j, j + 1, j + 2, I0{}, std::true_type{});
+      iteration(j + 1, n_kv, n_kv, I1{}, std::false_type{});
+    } else {
+      iteration(j, n_kv, n_kv, I0{}, std::false_type{});
+    }
   } else {
-    iteration(j, I0{}, std::false_type{});
+    // The same schedule over the visible tiles only (n_act of them; slots
+    // alternate by position): a, b, cc are the tiles at positions p, p+1, p+2.
+    const int nbk = (n_kv + 1) >> 1;  // mask blocks holding tiles < n_kv
+    int cnt = 0;
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) {
+      const int lim = nbk - 64 * w;
+      uint64_t bits = lim <= 0 ? 0 : (lim >= 64 ? mb[w] : mb[w] & ((1ull << lim) - 1));
+      cnt += __builtin_popcountll(bits);
+    }
+    const int last = nbk - 1;
+    const bool last_on = (mb[last >> 6] >> (last & 63)) & 1;
+    const int n_act = 2 * cnt - ((n_kv & 1) && last_on ? 1 : 0);
+    int a = c0, b = c1, cc = next_tile(c1 + 1);
+    int p = 0;
+    for (; p + 2 < n_act; p += 2) {
+      iteration(a, b, cc, I0{}, std::true_type{});
+      a = b;
+      b = cc;
+      cc = next_tile(cc + 1);
+      iteration(a, b, cc, I1{}, std::true_type{});
+      a = b;
+      b = cc;
+      cc = next_tile(cc + 1);
+    }
+    if (p + 1 < n_act) {
+      iteration(a, b, cc, I0{}, std::true_type{});
+      iteration(b, n_kv, n_kv, I1{}, std::false_type{});
+    } else {
+      iteration(a, n_kv, n_kv, I0{}, std::false_type{});
+    }
   }
 
   // Epilogue: O = Oᵀ/l (lane holds d = 32dt + 8(r/4) + 4h + r%4 of its query).
@@ -406,54 +492,80 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL, int EXPM, bool VARLEN>
+// Launch variants: dense, packed segments (varlen) or block mask.
+enum { FWD_DENSE = 0, FWD_VARLEN = 1, FWD_SPARSE = 2 };
+struct FwdAux {
+  const int* cu = nullptr;  // varlen: segment offsets
+  int nseq = 1;
+  int max_len = 0;          // varlen: longest segment the grid covers
+  const uint8_t* bmask = nullptr;  // block mask rows of 128 queries
+  long mask_stride = 0;     // elements between the masks of consecutive heads (0: shared)
+};
+
+template <int D, bool CAUSAL, int EXPM, int MODE>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int BH, int N, float scale, const int* cu, int nseq, int max_len,
-                               hipStream_t stream) {
-  const int n_qtiles = ((VARLEN ? max_len : N) + kFwdBM - 1) / kFwdBM;
-  const dim3 grid(n_qtiles * BH * (VARLEN ? nseq : 1)), block(64 * kFwdWaves);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXPM, VARLEN>), grid, block, 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, BH, n_qtiles,
-                     scale * kLog2e, cu, nseq);
+                               int BH, int N, float scale, const FwdAux& x, hipStream_t stream) {
+  const int n_qtiles = ((MODE == FWD_VARLEN ? x.max_len : N) + kFwdBM - 1) / kFwdBM;
+  const dim3 grid(n_qtiles * BH * (MODE == FWD_VARLEN ? x.nseq : 1)), block(64 * kFwdWaves);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXPM, MODE == FWD_VARLEN, MODE == FWD_SPARSE>),
+                     grid, block, 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                     (bf16*)o, lse, N, BH, n_qtiles, scale * kLog2e, x.cu, x.nseq, x.bmask,
+                     x.mask_stride);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, int MODE>
 static hipError_t launch_fwd_e(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int BH, int N, float scale, int exp_mode, const int* cu, int nseq,
-                               int max_len, hipStream_t stream) {
+                               int BH, int N, float scale, int exp_mode, const FwdAux& x,
+                               hipStream_t stream) {
   if (exp_mode == EXP_POLY)
-    return launch_fwd_t<D, CAUSAL, EXP_POLY, VARLEN>(q, k, v, o, lse, BH, N, scale, cu, nseq, max_len, stream);
+    return launch_fwd_t<D, CAUSAL, EXP_POLY, MODE>(q, k, v, o, lse, BH, N, scale, x, stream);
   if (exp_mode == EXP_SPLIT)
-    return launch_fwd_t<D, CAUSAL, EXP_SPLIT, VARLEN>(q, k, v, o, lse, BH, N, scale, cu, nseq, max_len, stream);
-  return launch_fwd_t<D, CAUSAL, EXP_HW, VARLEN>(q, k, v, o, lse, BH, N, scale, cu, nseq, max_len, stream);
+    return launch_fwd_t<D, CAUSAL, EXP_SPLIT, MODE>(q, k, v, o, lse, BH, N, scale, x, stream);
+  return launch_fwd_t<D, CAUSAL, EXP_HW, MODE>(q, k, v, o, lse, BH, N, scale, x, stream);
 }
 
-template <int D, bool VARLEN>
-static hipError_t launch_fwd_d(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int BH, int N, bool causal, float scale, int exp_mode,
-                               const int* cu, int nseq, int max_len, hipStream_t stream) {
-  if (causal)
-    return launch_fwd_e<D, true, VARLEN>(q, k, v, o, lse, BH, N, scale, exp_mode, cu, nseq, max_len, stream);
-  return launch_fwd_e<D, false, VARLEN>(q, k, v, o, lse, BH, N, scale, exp_mode, cu, nseq, max_len, stream);
+template <int MODE>
+static hipError_t launch_fwd_m(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int BH, int N, int d, bool causal, float scale, int exp_mode,
+                               const FwdAux& x, hipStream_t stream) {
+  if (d == 64) {
+    return causal ? launch_fwd_e<64, true, MODE>(q, k, v, o, lse, BH, N, scale, exp_mode, x, stream)
+                  : launch_fwd_e<64, false, MODE>(q, k, v, o, lse, BH, N, scale, exp_mode, x, stream);
+  }
+  return causal ? launch_fwd_e<128, true, MODE>(q, k, v, o, lse, BH, N, scale, exp_mode, x, stream)
+                : launch_fwd_e<128, false, MODE>(q, k, v, o, lse, BH, N, scale, exp_mode, x, stream);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, bool causal, float scale, int exp_mode,
                            hipStream_t stream) {
-  const int BH = B * H;
-  if (d == 64) return launch_fwd_d<64, false>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, nullptr, 1, N, stream);
-  return launch_fwd_d<128, false>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, nullptr, 1, N, stream);
+  return launch_fwd_m<FWD_DENSE>(q, k, v, o, lse, B * H, N, d, causal, scale, exp_mode, FwdAux{},
+                                 stream);
 }
 
 hipError_t launch_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
                                   float* lse, const int* cu_seqlens, int nseq, int max_seqlen,
                                   int B, int H, int N, int d, bool causal, float scale,
                                   int exp_mode, hipStream_t stream) {
-  const int BH = B * H;
-  if (d == 64)
-    return launch_fwd_d<64, true>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, cu_seqlens, nseq, max_seqlen, stream);
-  return launch_fwd_d<128, true>(q, k, v, o, lse, BH, N, causal, scale, exp_mode, cu_seqlens, nseq, max_seqlen, stream);
+  FwdAux x;
+  x.cu = cu_seqlens;
+  x.nseq = nseq;
+  x.max_len = max_seqlen;
+  return launch_fwd_m<FWD_VARLEN>(q, k, v, o, lse, B * H, N, d, causal, scale, exp_mode, x,
+                                  stream);
+}
+
+hipError_t launch_fwd_bf16_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const uint8_t* block_mask, bool per_head,
+                                       int B, int H, int N, int d, bool causal, float scale,
+                                       int exp_mode, hipStream_t stream) {
+  FwdAux x;
+  x.bmask = block_mask;
+  const long nb = (N + kMaskBlock - 1) / kMaskBlock;
+  x.mask_stride = per_head ? nb * nb : 0;
+  return launch_fwd_m<FWD_SPARSE>(q, k, v, o, lse, B * H, N, d, causal, scale, exp_mode, x,
+                                  stream);
 }
 
 }  // namespace fattn
