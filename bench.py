@@ -270,6 +270,34 @@ def sweep(args):
     print(f"[sweep] varlen done ({len(lengths)} segments, max {maxl})", file=sys.stderr,
           flush=True)
 
+    # Block masks over 128x128 blocks: B = 2, H = 16, N = 8192, d = 128, seeded
+    # random masks with the diagonal block always visible, at several densities.
+    B, H, N, d = 2, 16, 8192, 128
+    g = torch.Generator(device="cuda").manual_seed(78)
+    q, k, v, do = (torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16)
+                   for _ in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    nb = N // 128
+    scale = d ** -0.5
+    for dens in (1.0, 0.5, 0.25, 0.1):
+        m = (np.random.default_rng(3).random((nb, nb)) < dens).astype(np.uint8)
+        m[np.arange(nb), np.arange(nb)] = 1
+        mt = torch.as_tensor(m, device="cuda")
+        vis = float(m.sum()) * 128 * 128 * B * H  # visible (query, key) pairs
+        ms_f = timed(lambda: fa.fwd_blocksparse(q, k, v, mt, scale=scale, out=o, lse=lse))
+        ms_b = timed(lambda: fa.bwd_blocksparse(q, k, v, o, lse, do, mt, scale=scale,
+                                                workspace=ws, out=grads))
+        for part, ms, fl in (("fwd_blocksparse", ms_f, 4 * d * vis),
+                             ("bwd_blocksparse", ms_b, 10 * d * vis)):
+            tf = fl / (ms * 1e-3) / 1e12
+            points.append({"part": part, "causal": False, "B": B, "H": H, "N": N, "d": d,
+                           "density": round(float(m.mean()), 4), "ms": round(ms, 4),
+                           "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16, 4)})
+    print("[sweep] block masks done", file=sys.stderr, flush=True)
+
     print(json.dumps({"sweep": "tokens per point B*H*N = %d, B = 1" % SWEEP_TOKENS,
                       "data": "synthetic: seeded N(0,1) rounded to bf16", "reps": reps,
                       "warmup": warm, "points": points}), flush=True)

@@ -149,12 +149,21 @@ fattn_status fattn_bwd_varlen(const void* q, const void* k, const void* v,
  * A query that sees no key gets O = 0 and LSE = −∞ (the convention of the
  * plain definition for an empty row). Everything else as fattn_fwd. The mask
  * lives in device memory and is read as given (the caller sizes it).
- * Supports N <= 32768 (ENOTSUP beyond). There is no block-sparse backward.
+ * Supports N <= 32768 (ENOTSUP beyond).
+ * fattn_bwd_blocksparse: the backward of fattn_fwd_blocksparse from its O and
+ * LSE, same mask, same workspace as fattn_bwd; key blocks that no query sees
+ * get dK = dV = 0, queries that see no key get dQ = 0.
  */
 fattn_status fattn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
                                    float* lse, const uint8_t* block_mask, int per_head,
                                    int B, int H, int N, int d, int causal, float scale,
                                    int exp_mode, void* stream);
+fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
+                                   const void* o, const float* lse, const void* dout,
+                                   void* dq, void* dk, void* dv,
+                                   const uint8_t* block_mask, int per_head, int B, int H,
+                                   int N, int d, int causal, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * Forward with fp8 (OCP e4m3fn) operands and bf16 in/out

@@ -186,3 +186,21 @@ def test_fwd_blocksparse_checks():
     assert call(exp=9) == EINVAL
     assert call(scale=-2.0) == EINVAL
     assert fa.lib().fattn_last_error()
+
+
+def test_bwd_blocksparse_checks():
+    lib = fa.lib()
+    B, H, N, d = 1, 2, 300, 128
+    need = lib.fattn_bwd_workspace_bytes(B, H, N, d)
+
+    def call(ws, nbytes, **kw):
+        a = dict(mask=P, per_head=0, N=N, dk=P)
+        a.update(kw)
+        return lib.fattn_bwd_blocksparse(P, P, P, P, P, P, P, a["dk"], P, a["mask"], a["per_head"],
+                                         B, H, a["N"], d, 0, ctypes.c_float(0.1), ws, nbytes, NUL)
+    assert call(P, need - 1) == EWORKSPACE
+    assert call(NUL, need) == EWORKSPACE
+    assert call(P, need, mask=NUL) == EINVAL
+    assert call(P, need, per_head=-1) == EINVAL
+    assert call(P, need, dk=MIS) == EINVAL
+    assert call(P, lib.fattn_bwd_workspace_bytes(B, H, 40000, d), N=40000) == ENOTSUP

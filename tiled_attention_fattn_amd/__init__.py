@@ -11,6 +11,7 @@ an exception is raised.
     o, lse = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False)
     dq, dk, dv = bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False)
     o, lse = fwd_blocksparse(q, k, v, block_mask, causal=False)
+    dq, dk, dv = bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=False)
 
 Tensors are contiguous CUDA (HIP) bfloat16 [B, H, N, d], d ∈ {64, 128};
 ``scale`` defaults to 1/√d.
@@ -20,7 +21,7 @@ import os
 
 from ._lib import FattnError, lib, lib_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "bwd_blocksparse", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
            "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
            "EXP_AUTO", "EXP_HW", "EXP_POLY", "EXP_SPLIT"]
 
@@ -120,6 +121,18 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, exp_mo
     return o, lse_t
 
 
+def _bmask(block_mask, q):
+    torch = _torch()
+    B, H, N, _ = _shape(q)
+    nb = (N + 127) // 128
+    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8 \
+            or not block_mask.is_contiguous() or block_mask.device != q.device \
+            or tuple(block_mask.shape) not in ((nb, nb), (B * H, nb, nb)):
+        raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape ({nb}, {nb}) "
+                         f"or ({B * H}, {nb}, {nb}) on the device of q")
+    return int(block_mask.dim() == 3)
+
+
 def fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, exp_mode="auto", out=None,
                     lse=None):
     """Block-sparse forward: block_mask is a uint8 tensor on the device of q,
@@ -131,13 +144,7 @@ def fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, exp_mode="aut
     B, H, N, d = _shape(q)
     if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
         raise ValueError("q, k, v must have the same shape")
-    nb = (N + 127) // 128
-    if not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8 \
-            or not block_mask.is_contiguous() or block_mask.device != q.device \
-            or tuple(block_mask.shape) not in ((nb, nb), (B * H, nb, nb)):
-        raise ValueError(f"block_mask must be a contiguous uint8 tensor of shape ({nb}, {nb}) "
-                         f"or ({B * H}, {nb}, {nb}) on the device of q")
-    per_head = int(block_mask.dim() == 3)
+    per_head = _bmask(block_mask, q)
     scale = float(d ** -0.5 if scale is None else scale)
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -215,6 +222,30 @@ def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, scale=
                                      int(max_seqlen), B, H, N, d, int(bool(causal)),
                                      ctypes.c_float(scale), _ptr(ws), ctypes.c_size_t(ws.numel()),
                                      _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=False, scale=None, workspace=None,
+                    out=None):
+    """Backward of fwd_blocksparse from its O and LSE. Returns (dQ, dK, dV) bf16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, n, torch.bfloat16)
+    _check(lse, "lse", torch.float32)
+    B, H, N, d = _shape(q)
+    per_head = _bmask(block_mask, q)
+    scale = float(d ** -0.5 if scale is None else scale)
+    if out is None:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    else:
+        dq, dk, dv = out
+    need = bwd_workspace_bytes(B, H, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(block_mask), per_head,
+                                          B, H, N, d, int(bool(causal)), ctypes.c_float(scale),
+                                          _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(q)))
     return dq, dk, dv
 
 

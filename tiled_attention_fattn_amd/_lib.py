@@ -13,6 +13,8 @@ PROTOTYPES = {
     "fattn_fwd": (c_int, [c_void_p] * 5 + [c_int] * 5 + [c_float, c_int, c_void_p]),
     "fattn_fwd_varlen": (c_int, [c_void_p] * 6 + [c_int] * 7 + [c_float, c_int, c_void_p]),
     "fattn_fwd_blocksparse": (c_int, [c_void_p] * 6 + [c_int] * 6 + [c_float, c_int, c_void_p]),
+    "fattn_bwd_blocksparse": (c_int, [c_void_p] * 10 + [c_int] * 6
+                              + [c_float, c_void_p, c_size_t, c_void_p]),
     "fattn_bwd_workspace_bytes": (c_size_t, [c_int] * 4),
     "fattn_bwd_varlen": (c_int, [c_void_p] * 10 + [c_int] * 7
                          + [c_float, c_void_p, c_size_t, c_void_p]),

@@ -12,6 +12,10 @@
 // padded rows carry lse2 = +∞ and D = 0, so their P (and every contribution
 // they make) is exactly 0 without any mask.
 //
+// Block masks (SPARSE): kernel 2 walks only the query tiles whose block row
+// sees its key block (the mask column), kernel 3 only the key tiles of the
+// blocks its query block sees (the mask row).
+//
 // Packed variable-length sequences (VARLEN): kernels 2 and 3 run over
 // (head, segment, tile) and treat each segment as a sequence of its own
 // (rows offset to the segment start, length = the segment's). Rows past the
@@ -90,14 +94,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O
 // ---------------------------------------------------------------------------
 // Kernel 2: dK, dV, key-stationary.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ lse2, const float* __restrict__ dvec,
                      bf16* __restrict__ dK, bf16* __restrict__ dV,
                      int N, int Npad, int BH, int n_kvtiles, float c_log2, float scale,
-                     const int* __restrict__ cu, int nseq) {
+                     const int* __restrict__ cu, int nseq, const uint8_t* __restrict__ bmask,
+                     long mask_stride) {
+  static_assert(!SPARSE || (kBwdBN == kMaskBlockRows && 2 * kBwdBM == kMaskBlockRows),
+                "one key block per mask column, two query tiles per mask row");
   constexpr int KD = D / 16, DT = D / 32;
   constexpr int RB = D * 2;                         // bytes per Q / dO row
   constexpr int QT_BYTES = kBwdBM * RB;             // one Q or dO tile
@@ -234,12 +241,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // the MFMAs:
   //   A: S, dP of half 0 (16 MFMA)  B: S, dP of half 1 ∥ P, dS of half 0
   //   C: dVᵀ, dKᵀ of half 0 ∥ P, dS of half 1   D: dVᵀ, dKᵀ of half 1
-  auto iteration = [&](int it, auto parity_tag, auto masked_tag) __device__ {
+  // itn: the next query tile in processing order (it + 1 without a block mask).
+  auto iteration = [&](int it, int itn, auto parity_tag, auto masked_tag) __device__ {
     constexpr int PAR = decltype(parity_tag)::value;  // stage of tile it
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr int NR = 4 * KD;  // S/dP operand reads: half i/(2KD), kk (i/2)%KD, Q or dO by i%2
     const int qs = it * kBwdBM;
-    if (it + 1 < n_qt) gload(it + 1, PAR ^ 1);
+    if (itn < n_qt) gload(itn, PAR ^ 1);
     const char* qb = q_lds + PAR * 2 * QT_BYTES;
     const char* db = qb + QT_BYTES;
     const float* lse_s = (const float*)(st_lds + PAR * 512);
@@ -316,26 +324,53 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     __syncthreads();
   };
 
-  gload(i0, 0);
-  wait_vmem();
-  __syncthreads();
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int it = i0;
-  // Masked (diagonal) tiles first, then the rest; parity follows it − i0.
-  for (; it < first_unmasked; ++it) {
-    if (((it - i0) & 1) == 0) iteration(it, I0{}, std::true_type{});
-    else iteration(it, I1{}, std::true_type{});
+  if constexpr (!SPARSE) {
+    gload(i0, 0);
+    wait_vmem();
+    __syncthreads();
+    int it = i0;
+    // Masked (diagonal) tiles first, then the rest; parity follows it − i0.
+    for (; it < first_unmasked; ++it) {
+      if (((it - i0) & 1) == 0) iteration(it, it + 1, I0{}, std::true_type{});
+      else iteration(it, it + 1, I1{}, std::true_type{});
+    }
+    if (((it - i0) & 1) == 1 && it < n_qt) {
+      iteration(it, it + 1, I1{}, std::false_type{});
+      ++it;
+    }
+    for (; it + 1 < n_qt; it += 2) {
+      iteration(it, it + 1, I0{}, std::false_type{});
+      iteration(it + 1, it + 2, I1{}, std::false_type{});
+    }
+    if (it < n_qt) iteration(it, it + 1, I0{}, std::false_type{});
+  } else {
+    // Only the query tiles whose block row sees this key block (its column
+    // of the mask); stages alternate by position. A key block no query sees
+    // keeps dK = dV = 0.
+    uint64_t mb[kMaskWords];
+    const int nb = (N + kMaskBlockRows - 1) / kMaskBlockRows;
+    load_mask_bits(bmask + bh * mask_stride + jt, nb, nb, lane, mb);
+    int a = next_mask_tile(mb, i0, n_qt);
+    if (a < n_qt) {
+      gload(a, 0);
+      wait_vmem();
+      __syncthreads();
+      int b = next_mask_tile(mb, a + 1, n_qt);
+      for (int pos = 0; a < n_qt; ++pos) {
+        if (pos & 1) {
+          if (a < first_unmasked) iteration(a, b, I1{}, std::true_type{});
+          else iteration(a, b, I1{}, std::false_type{});
+        } else {
+          if (a < first_unmasked) iteration(a, b, I0{}, std::true_type{});
+          else iteration(a, b, I0{}, std::false_type{});
+        }
+        a = b;
+        b = next_mask_tile(mb, b + 1, n_qt);
+      }
+    }
   }
-  if (((it - i0) & 1) == 1 && it < n_qt) {
-    iteration(it, I1{}, std::false_type{});
-    ++it;
-  }
-  for (; it + 1 < n_qt; it += 2) {
-    iteration(it, I0{}, std::false_type{});
-    iteration(it + 1, I1{}, std::false_type{});
-  }
-  if (it < n_qt) iteration(it, I0{}, std::false_type{});
 
   // Epilogue: lane holds dKᵀ/dVᵀ[d = 32dt + 8g + 4h + 0..3][key].
   if (key < L) {
@@ -366,13 +401,16 @@ constexpr int kDqWaves = 4;
 constexpr int kDqBM = 32 * kDqWaves;  // queries per workgroup
 constexpr int kDqBN = 64;             // keys per tile
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ lse2, const float* __restrict__ dvec,
                    bf16* __restrict__ dQ, int N, int Npad, int BH, int n_qtiles, float c_log2,
-                   float scale, const int* __restrict__ cu, int nseq) {
+                   float scale, const int* __restrict__ cu, int nseq,
+                   const uint8_t* __restrict__ bmask, long mask_stride) {
+  static_assert(!SPARSE || (kDqBM == kMaskBlockRows && 2 * kDqBN == kMaskBlockRows),
+                "one query block per mask row, two key tiles per mask column");
   constexpr int KD = D / 16, RB = D * 2, TILE = kDqBN * RB, DT = D / 32;
   constexpr int LOADS = TILE / 1024 / kDqWaves;  // 1 KB wave loads per tensor per tile
   // LDS: K slots 0, 1 then V slots 0, 1, row-major with the 64-bank swizzle.
@@ -456,10 +494,11 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
 
-  auto iteration = [&](int j, auto parity_tag, auto masked_tag) __device__ {
+  // jn: the next key tile in processing order (j + 1 without a block mask).
+  auto iteration = [&](int j, int jn, auto parity_tag, auto masked_tag) __device__ {
     constexpr int PAR = decltype(parity_tag)::value;
     constexpr bool MASKED = decltype(masked_tag)::value;
-    if (j + 1 < n_kv) gload(j + 1, PAR ^ 1);
+    if (jn < n_kv) gload(jn, PAR ^ 1);
     const char* kt = k_lds + PAR * TILE;
     const char* vt = v_lds + PAR * TILE;
     const int key0 = j * kDqBN;
@@ -527,19 +566,46 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     __syncthreads();
   };
 
-  gload(0, 0);
-  wait_vmem();
-  __syncthreads();
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int j = 0;
-  for (; j + 1 < first_masked; j += 2) {
-    iteration(j, I0{}, std::false_type{});
-    iteration(j + 1, I1{}, std::false_type{});
-  }
-  for (; j < n_kv; ++j) {
-    if (j & 1) iteration(j, I1{}, std::integral_constant<bool, true>{});
-    else iteration(j, I0{}, std::integral_constant<bool, true>{});
+  if constexpr (!SPARSE) {
+    gload(0, 0);
+    wait_vmem();
+    __syncthreads();
+    int j = 0;
+    for (; j + 1 < first_masked; j += 2) {
+      iteration(j, j + 1, I0{}, std::false_type{});
+      iteration(j + 1, j + 2, I1{}, std::false_type{});
+    }
+    for (; j < n_kv; ++j) {
+      if (j & 1) iteration(j, j + 1, I1{}, std::integral_constant<bool, true>{});
+      else iteration(j, j + 1, I0{}, std::integral_constant<bool, true>{});
+    }
+  } else {
+    // Only the key tiles of the blocks this query block sees (its row of the
+    // mask); slots alternate by position. A block row that sees nothing
+    // keeps dQ = 0.
+    uint64_t mb[kMaskWords];
+    const int nb = (N + kMaskBlockRows - 1) / kMaskBlockRows;
+    load_mask_bits(bmask + bh * mask_stride + (long)qt * nb, 1, nb, lane, mb);
+    int a = next_mask_tile(mb, 0, n_kv);
+    if (a < n_kv) {
+      gload(a, 0);
+      wait_vmem();
+      __syncthreads();
+      int b = next_mask_tile(mb, a + 1, n_kv);
+      for (int pos = 0; a < n_kv; ++pos) {
+        if (pos & 1) {
+          if (a >= first_masked) iteration(a, b, I1{}, std::true_type{});
+          else iteration(a, b, I1{}, std::false_type{});
+        } else {
+          if (a >= first_masked) iteration(a, b, I0{}, std::true_type{});
+          else iteration(a, b, I0{}, std::false_type{});
+        }
+        a = b;
+        b = next_mask_tile(mb, b + 1, n_kv);
+      }
+    }
   }
 
   // Epilogue: dQ = scale·dQᵀ (lane holds d = 32dt + 8(r/4) + 4h + r%4).
@@ -557,15 +623,26 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+// Launch variants: dense, packed segments (varlen) or block mask.
+enum { BWD_DENSE = 0, BWD_VARLEN = 1, BWD_SPARSE = 2 };
+struct BwdAux {
+  const int* cu = nullptr;
+  int nseq = 1;
+  int max_len = 0;
+  const uint8_t* bmask = nullptr;
+  long mask_stride = 0;
+};
+
+template <int D, bool CAUSAL, int MODE>
 static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                float* dvec, float* lse2, int BH, int N, float scale,
-                               const int* cu, int nseq, int max_len, hipStream_t stream) {
+                               const BwdAux& x, hipStream_t stream) {
+  constexpr bool VARLEN = MODE == BWD_VARLEN, SPARSE = MODE == BWD_SPARSE;
   const int Npad = (N + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad;
   const long rows_pad = (long)BH * Npad;
-  const int len = VARLEN ? max_len : N;  // longest sequence the grid covers
-  const int units = BH * (VARLEN ? nseq : 1);
+  const int len = VARLEN ? x.max_len : N;  // longest sequence the grid covers
+  const int units = BH * (VARLEN ? x.nseq : 1);
   {
     const long threads = rows_pad * (D / 8);
     const dim3 grid((unsigned)((threads + 255) / 256));
@@ -577,44 +654,44 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
   {
     const int n_kvtiles = (len + kBwdBN - 1) / kBwdBN;
     const dim3 grid(n_kvtiles * units);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, SPARSE>), grid, dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                        (const float*)lse2, (const float*)dvec, (bf16*)dk, (bf16*)dv, N,
-                       Npad, BH, n_kvtiles, scale * kLog2e, scale, cu, nseq);
+                       Npad, BH, n_kvtiles, scale * kLog2e, scale, x.cu, x.nseq, x.bmask,
+                       x.mask_stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     const int n_qtiles = (len + kDqBM - 1) / kDqBM;
     const dim3 grid(n_qtiles * units);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN, SPARSE>), grid, dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                        (const float*)lse2, (const float*)dvec, (bf16*)dq, N, Npad, BH, n_qtiles,
-                       scale * kLog2e, scale, cu, nseq);
+                       scale * kLog2e, scale, x.cu, x.nseq, x.bmask, x.mask_stride);
   }
   return hipGetLastError();
 }
 
-template <bool VARLEN>
-static hipError_t launch_bwd_v(const void* q, const void* k, const void* v, const void* o,
+template <int MODE>
+static hipError_t launch_bwd_m(const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                float* dvec, float* lse2, int BH, int N, int d, bool causal,
-                               float scale, const int* cu, int nseq, int max_len,
-                               hipStream_t stream) {
+                               float scale, const BwdAux& x, hipStream_t stream) {
   if (d == 64) {
-    return causal ? launch_bwd_t<64, true, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream)
-                  : launch_bwd_t<64, false, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream);
+    return causal ? launch_bwd_t<64, true, MODE>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, x, stream)
+                  : launch_bwd_t<64, false, MODE>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, x, stream);
   }
-  return causal ? launch_bwd_t<128, true, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream)
-                : launch_bwd_t<128, false, VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, cu, nseq, max_len, stream);
+  return causal ? launch_bwd_t<128, true, MODE>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, x, stream)
+                : launch_bwd_t<128, false, MODE>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, BH, N, scale, x, stream);
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* dvec, float* lse2, int B, int H, int N, int d, bool causal,
                            float scale, hipStream_t stream) {
-  return launch_bwd_v<false>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B * H, N, d, causal,
-                             scale, nullptr, 1, N, stream);
+  return launch_bwd_m<BWD_DENSE>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B * H, N, d,
+                                 causal, scale, BwdAux{}, stream);
 }
 
 hipError_t launch_bwd_bf16_varlen(const void* q, const void* k, const void* v, const void* o,
@@ -622,8 +699,26 @@ hipError_t launch_bwd_bf16_varlen(const void* q, const void* k, const void* v, c
                                   void* dv, float* dvec, float* lse2, const int* cu_seqlens,
                                   int nseq, int max_seqlen, int B, int H, int N, int d,
                                   bool causal, float scale, hipStream_t stream) {
-  return launch_bwd_v<true>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B * H, N, d, causal,
-                            scale, cu_seqlens, nseq, max_seqlen, stream);
+  BwdAux x;
+  x.cu = cu_seqlens;
+  x.nseq = nseq;
+  x.max_len = max_seqlen;
+  return launch_bwd_m<BWD_VARLEN>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B * H, N, d,
+                                  causal, scale, x, stream);
+}
+
+hipError_t launch_bwd_bf16_blocksparse(const void* q, const void* k, const void* v,
+                                       const void* o, const float* lse, const void* dout,
+                                       void* dq, void* dk, void* dv, float* dvec, float* lse2,
+                                       const uint8_t* block_mask, bool per_head, int B, int H,
+                                       int N, int d, bool causal, float scale,
+                                       hipStream_t stream) {
+  BwdAux x;
+  x.bmask = block_mask;
+  const long nb = (N + kMaskBlockRows - 1) / kMaskBlockRows;
+  x.mask_stride = per_head ? nb * nb : 0;
+  return launch_bwd_m<BWD_SPARSE>(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B * H, N, d,
+                                  causal, scale, x, stream);
 }
 
 }  // namespace fattn

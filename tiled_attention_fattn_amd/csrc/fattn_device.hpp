@@ -146,6 +146,47 @@ __device__ __forceinline__ void stats_to_lds(const float* src, char* dst, int la
 #endif
 }
 
+// Block masks (block-sparse attention): one bit per 128-row mask block,
+// kMaskWords 64-bit ballots per row or column of the mask (N <= 32768).
+constexpr int kMaskBlockRows = 128;
+constexpr int kMaskWords = 4;
+
+// Bits of the mask blocks base[b * stride] for b < nb (a mask row: stride
+// 1; a mask column: stride nb), identical in every lane.
+__device__ __forceinline__ void load_mask_bits(const uint8_t* base, long stride, int nb, int lane,
+                                               uint64_t (&mb)[kMaskWords]) {
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) {
+    const int b = w * 64 + lane;
+    mb[w] = __ballot(b < nb && base[b * stride] != 0);
+  }
+}
+
+// First 64-row tile index >= j whose mask block (tile / 2) is set, or n if
+// there is none below n.
+__device__ __forceinline__ int next_mask_tile(const uint64_t (&mb)[kMaskWords], int j, int n) {
+  if (j >= n) return n;
+  const int b = j >> 1;
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) {
+    if (w < (b >> 6)) continue;
+    uint64_t bits = mb[w];
+    if (w == (b >> 6)) bits &= ~0ull << (b & 63);
+    if (bits != 0) {
+      const int nbk = w * 64 + __builtin_ctzll(bits);
+      return min(nbk == b ? j : 2 * nbk, n);
+    }
+  }
+  return n;
+}
+
+// Number of tiles in [j0, n) whose mask block is set.
+__device__ __forceinline__ int count_mask_tiles(const uint64_t (&mb)[kMaskWords], int j0, int n) {
+  int cnt = 0;
+  for (int j = next_mask_tile(mb, j0, n); j < n; j = next_mask_tile(mb, j + 1, n)) ++cnt;
+  return cnt;
+}
+
 // Wait until this wave's outstanding global loads (including those that
 // write straight into LDS) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

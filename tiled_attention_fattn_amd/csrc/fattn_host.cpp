@@ -248,6 +248,41 @@ fattn_status fattn_bwd_varlen(const void* q, const void* k, const void* v, const
                     "fattn_bwd_varlen launch");
 }
 
+fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                                   const float* lse, const void* dout, void* dq, void* dk,
+                                   void* dv, const uint8_t* block_mask, int per_head, int B,
+                                   int H, int N, int d, int causal, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  FATTN_TRY(check_ptr(lse, "lse"));
+  FATTN_TRY(check_ptr(dout, "dout"));
+  FATTN_TRY(check_ptr(dq, "dq"));
+  FATTN_TRY(check_ptr(dk, "dk"));
+  FATTN_TRY(check_ptr(dv, "dv"));
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  if (block_mask == nullptr) return fail(FATTN_EINVAL, "block_mask is NULL");
+  if (per_head != 0 && per_head != 1)
+    return fail(FATTN_EINVAL, "per_head must be 0 or 1 (got %d)", per_head);
+  if (N > 32768) return fail(FATTN_ENOTSUP, "block-sparse backward supports N <= 32768 (got %d)", N);
+  if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
+  if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
+  const size_t need = fattn_bwd_workspace_bytes(B, H, N, d);
+  if (workspace_bytes < need)
+    return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, need);
+  FATTN_TRY(check_device());
+  const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
+  float* dvec = (float*)workspace;
+  float* lse2 = (float*)((char*)dvec + round_up(n * sizeof(float), 256));
+  return hip_status(fattn::launch_bwd_bf16_blocksparse(q, k, v, o, lse, dout, dq, dk, dv, dvec,
+                                                       lse2, block_mask, per_head != 0, B, H, N,
+                                                       d, causal != 0, scale,
+                                                       (hipStream_t)stream),
+                    "fattn_bwd_blocksparse launch");
+}
+
 size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   return fp8_layout(B, H, N, d).total;

@@ -39,6 +39,13 @@ hipError_t launch_bwd_bf16_varlen(const void* q, const void* k, const void* v, c
                                   int nseq, int max_seqlen, int B, int H, int N, int d,
                                   bool causal, float scale, hipStream_t stream);
 
+hipError_t launch_bwd_bf16_blocksparse(const void* q, const void* k, const void* v,
+                                       const void* o, const float* lse, const void* dout,
+                                       void* dq, void* dk, void* dv, float* dvec, float* lse2,
+                                       const uint8_t* block_mask, bool per_head, int B, int H,
+                                       int N, int d, bool causal, float scale,
+                                       hipStream_t stream);
+
 constexpr int kBwdRowPad = 64;
 
 // fp8 forward: q8/q8lo/k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32

@@ -56,8 +56,7 @@ constexpr int kFwdBN = 64;                  // keys per K/V tile
 constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between rescales
 constexpr float kSumGuard = 256.0f;         // 2^kRescaleTau
 constexpr int kLead = 3;                    // LDS operand reads in flight ahead of the MFMAs
-constexpr int kMaskBlock = 128;             // block-mask granularity (queries and keys)
-constexpr int kMaskWords = 4;               // 64-block words of a mask row: N <= 32768
+constexpr int kMaskBlock = kMaskBlockRows;  // block-mask granularity (queries and keys)
 
 
 // Running softmax state of one 32-query sub-tile (per lane: one query).
@@ -253,29 +252,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   uint64_t mb[kMaskWords] = {};
   if constexpr (SPARSE) {
     const int nb = (N + kMaskBlock - 1) / kMaskBlock;
-    const uint8_t* mrow = bmask + bh * mask_stride + (long)qt * nb;
-#pragma unroll
-    for (int w = 0; w < kMaskWords; ++w) {
-      const int b = w * 64 + lane;
-      mb[w] = __ballot(b < nb && mrow[b] != 0);
-    }
+    load_mask_bits(bmask + bh * mask_stride + (long)qt * nb, 1, nb, lane, mb);
   }
   auto next_tile = [&](int j) __device__ {
-    if constexpr (SPARSE) {
-      if (j >= n_kv) return n_kv;
-      const int b = j >> 1;
-#pragma unroll
-      for (int w = 0; w < kMaskWords; ++w) {
-        if (w < (b >> 6)) continue;
-        uint64_t bits = mb[w];
-        if (w == (b >> 6)) bits &= ~0ull << (b & 63);
-        if (bits != 0) {
-          const int nbk = w * 64 + __builtin_ctzll(bits);
-          return min(nbk == b ? j : 2 * nbk, n_kv);
-        }
-      }
-      return n_kv;
-    }
+    if constexpr (SPARSE) return next_mask_tile(mb, j, n_kv);
     return j;
   };
   const int c0 = next_tile(0), c1 = next_tile(c0 + 1);
@@ -443,17 +423,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   } else {
     // The same schedule over the visible tiles only (n_act of them; slots
     // alternate by position): a, b, cc are the tiles at positions p, p+1, p+2.
-    const int nbk = (n_kv + 1) >> 1;  // mask blocks holding tiles < n_kv
-    int cnt = 0;
-#pragma unroll
-    for (int w = 0; w < kMaskWords; ++w) {
-      const int lim = nbk - 64 * w;
-      uint64_t bits = lim <= 0 ? 0 : (lim >= 64 ? mb[w] : mb[w] & ((1ull << lim) - 1));
-      cnt += __builtin_popcountll(bits);
-    }
-    const int last = nbk - 1;
-    const bool last_on = (mb[last >> 6] >> (last & 63)) & 1;
-    const int n_act = 2 * cnt - ((n_kv & 1) && last_on ? 1 : 0);
+    const int n_act = count_mask_tiles(mb, 0, n_kv);
     int a = c0, b = c1, cc = next_tile(c1 + 1);
     int p = 0;
     for (; p + 2 < n_act; p += 2) {
