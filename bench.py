@@ -64,10 +64,15 @@ def copy_calibration(nbytes, reps):
 
 
 def source_hash(part):
+    """Hash of the kernel sources of a bench part, ignoring comments and blank
+    lines (a comment edit does not change the compiled kernels)."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[part]:
-        with open(os.path.join(HERE, "tiled_attention_fattn_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(HERE, "tiled_attention_fattn_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

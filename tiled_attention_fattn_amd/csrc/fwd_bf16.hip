@@ -42,6 +42,9 @@
 //    segment, query tile) and each workgroup works on its segment as on a
 //    sequence of its own (base rows offset to the segment start, length =
 //    the segment's), so no tile ever mixes two segments.
+//  * Block masks (SPARSE): each workgroup is one 128-query block; it reads
+//    its row of the 128×128-block mask once (as 64-bit ballots) and runs the
+//    same schedule over the visible 64-key tiles only.
 #include <type_traits>
 
 #include "fattn_device.hpp"
