@@ -107,6 +107,12 @@ __device__ __forceinline__ i32x4 make_rsrc_sgpr(const void* base, int bytes) {
   return r;
 }
 
+// LDS byte address of a generic pointer into LDS. A generic address in the
+// shared aperture carries the LDS address in its low 32 bits, so truncation
+// is the cast (without the null test of an address-space cast, which would
+// keep the 64-bit pointer alive in vector registers).
+__device__ __forceinline__ int lds_addr(const char* p) { return (int)(uint32_t)(uintptr_t)p; }
+
 // Moves LOADS × 1 KB of a tile into LDS with buffer loads: wave load i takes
 // 16 bytes per lane from byte offset off[i] of the buffer [base, base + bytes)
 // (zero past the end) to LDS at dst + (first + i)·1 KB + lane·16.
@@ -122,8 +128,7 @@ __device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, char*
   const i32x4 rsrc = make_rsrc_sgpr(base, bytes);
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    const int m0v = __builtin_amdgcn_readfirstlane(
-        (int)(uint32_t)(uintptr_t)(FATTN_LDS char*)(dst + (first + i) * 1024));
+    const int m0v = __builtin_amdgcn_readfirstlane(lds_addr(dst + (first + i) * 1024));
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(m0v), "v"(off[i]), "s"(rsrc)
@@ -138,7 +143,7 @@ __device__ __forceinline__ void stats_to_lds(const float* src, char* dst, int la
                                              int bytes = 256) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const i32x4 rsrc = make_rsrc_sgpr(src, bytes);
-  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(FATTN_LDS char*)dst);
+  const int m0v = __builtin_amdgcn_readfirstlane(lds_addr(dst));
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(m0v), "v"(lane * 4), "s"(rsrc)

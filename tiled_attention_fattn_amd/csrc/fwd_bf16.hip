@@ -275,6 +275,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 
   // Prologue: K(c0), K(c1), V(c0) in flight; S(c0); running max from it.
+  // The second barrier lets the first iteration refill K slot 0 only once
+  // every wave has read K(c0) from it.
   gload(Kh, k_lds, c0);
   if (c1 < n_kv) gload(Kh, k_lds + TILE, c1);
   gload(Vh, v_lds, c0);
@@ -284,6 +286,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   scores(k_lds, s);
   if (c0 >= first_masked) mask_tile<CAUSAL>(s, c0 * kFwdBN, L, qi, h);
   st.m_c = tile_max(s);
+  __syncthreads();
 
   // Conditional rescale (FlashAttention-4 gist, technical summary 2.B). The
   // offset m_c stays put while every P̃ of a tile is at most 2^τ. A lane

@@ -483,6 +483,8 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   if (first_masked == 0) mask(s, 0);
   // The exponent offset starts at tile 0's row max; P̃ ≤ 2^τ afterwards.
   float m_c = tile_max(s);
+  // The first iteration refills K slot 0: every wave must have read K(0).
+  __syncthreads();
 
   auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
     constexpr int PAR = decltype(parity_tag)::value;
