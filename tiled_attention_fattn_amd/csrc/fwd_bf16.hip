@@ -334,11 +334,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // pieces), so no MFMA waits for its own operand, and the S pieces carry
   // one element pair of the softmax of tile j each. The last iteration (no
   // tile j+1) is peeled.
-  constexpr int NSP = 2 * KD;     // S pieces: key half t = i/KD, k-step kk = i%KD
+  constexpr int NSP = 2 * KD;     // S pieces: key half t = i%2, k-step kk = i/2
   static_assert(16 % NSP == 0, "softmax pairs must spread evenly over the S pieces");
   constexpr int NPV = NS * DT;    // PV pieces: key step ks = i/DT, d tile dt = i%DT
   auto kread = [&](const char* kt, int i) __device__ {
-    return *(const bf16x8*)(kt + (i / KD) * 32 * RB + koff[i % KD]);
+    return *(const bf16x8*)(kt + (i % 2) * 32 * RB + koff[i / 2]);
   };
   auto vread = [&](const char* vt, int i, bf16x4 (&ta)[NPV][2]) __device__ {
     const char* base = vt + 16 * (i / DT) * RB;
@@ -370,7 +370,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
       for (int i = 0; i < NSP; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        const int t = i / KD, kk = i % KD;
+        // The two key halves alternate, so no MFMA waits for the one before.
+        const int t = i % 2, kk = i / 2;
         ns[t] = mfma32(ra[i], qr[kk], kk == 0 ? f32x16{} : ns[t]);
         if (i + kLead < NSP) ra[i + kLead] = kread(kt, i + kLead);
         else vread(vt, i + kLead - NSP, ta);
@@ -396,7 +397,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     float lt = la + lb;
     guard(j, p, lt);
 
-    // PV(j): Vᵀ operands by transpose reads, kLead pieces ahead.
+    // PV(j): Vᵀ operands by transpose reads, kLead pieces ahead. The PV
+    // pieces run at the lower wave priority: when the other wave of the SIMD
+    // is in its S/softmax phase, that phase (VALU-heavy, with the loads) is
+    // issued first and the PV MFMAs fill the matrix pipe around it.
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 0; i < NPV; ++i) {
       __builtin_amdgcn_sched_barrier(0);
@@ -405,6 +410,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       if (i + kLead < NPV) vread(vt, i + kLead, ta);
     }
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (HAS_NEXT) {
       s[0] = ns[0];
       s[1] = ns[1];
