@@ -1,8 +1,9 @@
 """GPU parity of the bf16 forward (libfattn fattn_fwd) against the float64 oracle.
 
 Small shapes are compared element by element with the full oracle; they span
-several 128-row query tiles and 64-key tiles, ragged tails, N = 1 and both
-head dimensions. The two throughput workloads (causal B=8 H=16 N=2048 and
+several 128-row query tiles and 64-key tiles, ragged tails, N = 1, both head
+dimensions, and a ragged N above 4096 where the non-causal d=128 launch uses
+256-query workgroups. The two throughput workloads (causal B=8 H=16 N=2048 and
 non-causal B=2 H=16 N=8192, d=128) run at full size in the launch
 configuration the bench times and are compared on sampled heads and rows.
 """
@@ -41,6 +42,7 @@ SMALL = [
     (17, (1, 1, 513, 128), False),
     (18, (1, 2, 1024, 128), True),
     (19, (2, 1, 129, 64), False),
+    (20, (1, 1, 4100, 128), False),  # 256-query workgroups (non-causal, d=128, N >= 4096), ragged
 ]
 
 

@@ -6,9 +6,10 @@
 // one head; K and V stream through LDS in 64-key tiles; the scores and the
 // probabilities never leave the compute unit.
 //
-// Layout inside a workgroup (4 waves of 64 lanes, 32 queries per wave, two
-// workgroups per compute unit so that each SIMD holds two waves whose VALU
-// and MFMA phases interleave):
+// Layout inside a workgroup (32 queries per wave; 8 waves for plain
+// non-causal attention, one workgroup per compute unit, or 4 waves and two
+// workgroups per compute unit otherwise; either way each SIMD holds two
+// waves whose VALU and MFMA phases interleave):
 //  * Sᵀ = K·Qᵀ on 32x32x16 bf16 MFMA: the accumulator column is the query,
 //    so each lane owns one query row and the row reductions are in-lane plus
 //    one exchange between the two lane halves. K comes from LDS, Q stays in
@@ -52,9 +53,15 @@
 
 namespace fattn {
 
-constexpr int kFwdWaves = 4;
 constexpr int kFwdQW = 32;                  // queries per wave
-constexpr int kFwdBM = kFwdQW * kFwdWaves;  // query rows per workgroup
+// Waves per workgroup (WAVES): 4 (128 queries, two workgroups per compute
+// unit), or 8 (256 queries sharing every K/V tile, one workgroup per compute
+// unit), which halves the bytes the tile loads write into LDS per MFMA. The
+// launch picks 8 only for plain non-causal attention with d = 128 and
+// N >= 4096: under the causal mask the diagonal work grows with the query
+// block, and for d = 64 or shorter sequences the halved workgroup count
+// costs more than it saves (measured).
+constexpr int kFwdWideMinN = 4096;
 constexpr int kFwdBN = 64;                  // keys per K/V tile
 constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between rescales
 constexpr float kSumGuard = 256.0f;         // 2^kRescaleTau
@@ -127,13 +134,17 @@ __device__ __forceinline__ void softmax_exp_pair(const f32x16 (&s)[2], float c_l
   pk[2 * t + half][e] = (int)pack_bf16x2(p0, p1);
 }
 
-template <int D, bool CAUSAL, int EXPM, bool VARLEN, bool SPARSE>
-__global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int EXPM, bool VARLEN, bool SPARSE, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
                      int N, int BH, int n_qtiles, float c_log2, const int* __restrict__ cu,
                      int nseq, const uint8_t* __restrict__ bmask, long mask_stride) {
   static_assert(!(VARLEN && SPARSE), "block masks apply to whole sequences");
+  static_assert(WAVES == 4 || (WAVES == 8 && !CAUSAL && !VARLEN && !SPARSE),
+                "eight waves only for plain non-causal attention");
+  constexpr int kFwdWaves = WAVES;
+  constexpr int kFwdBM = kFwdQW * kFwdWaves;  // query rows per workgroup
   static_assert(!SPARSE || kFwdBM == kMaskBlock, "one query tile per mask block row");
   constexpr int KD = D / 16;          // MFMA k-steps over the head dimension
   constexpr int RB = D * 2;           // bytes per K/V row
@@ -484,16 +495,27 @@ struct FwdAux {
   long mask_stride = 0;     // elements between the masks of consecutive heads (0: shared)
 };
 
+template <int D, bool CAUSAL, int EXPM, int MODE, int WAVES>
+static hipError_t launch_fwd_w(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int BH, int N, float scale, const FwdAux& x, hipStream_t stream) {
+  constexpr int bm = kFwdQW * WAVES;
+  const int n_qtiles = ((MODE == FWD_VARLEN ? x.max_len : N) + bm - 1) / bm;
+  const dim3 grid(n_qtiles * BH * (MODE == FWD_VARLEN ? x.nseq : 1)), block(64 * WAVES);
+  hipLaunchKernelGGL(
+      (fwd_bf16_kernel<D, CAUSAL, EXPM, MODE == FWD_VARLEN, MODE == FWD_SPARSE, WAVES>), grid,
+      block, 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, BH,
+      n_qtiles, scale * kLog2e, x.cu, x.nseq, x.bmask, x.mask_stride);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, int EXPM, int MODE>
 static hipError_t launch_fwd_t(const void* q, const void* k, const void* v, void* o, float* lse,
                                int BH, int N, float scale, const FwdAux& x, hipStream_t stream) {
-  const int n_qtiles = ((MODE == FWD_VARLEN ? x.max_len : N) + kFwdBM - 1) / kFwdBM;
-  const dim3 grid(n_qtiles * BH * (MODE == FWD_VARLEN ? x.nseq : 1)), block(64 * kFwdWaves);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, EXPM, MODE == FWD_VARLEN, MODE == FWD_SPARSE>),
-                     grid, block, 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                     (bf16*)o, lse, N, BH, n_qtiles, scale * kLog2e, x.cu, x.nseq, x.bmask,
-                     x.mask_stride);
-  return hipGetLastError();
+  if constexpr (D == 128 && !CAUSAL && MODE == FWD_DENSE) {
+    if (N >= kFwdWideMinN)
+      return launch_fwd_w<D, CAUSAL, EXPM, MODE, 8>(q, k, v, o, lse, BH, N, scale, x, stream);
+  }
+  return launch_fwd_w<D, CAUSAL, EXPM, MODE, 4>(q, k, v, o, lse, BH, N, scale, x, stream);
 }
 
 template <int D, bool CAUSAL, int MODE>
