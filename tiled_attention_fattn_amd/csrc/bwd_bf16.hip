@@ -3,29 +3,29 @@
 // Gradient of ⟨O, dO⟩ for O = softmax(scale·Q·Kᵀ [causal])·V, recomputing P
 // from the forward's log-sum-exp (the pages name the dS and dQ terms:
 // FlashAttention-4 gist, technical summary 2.C):
-//   D  = rowsum(dO ∘ O), lse2 = LSE·log2(e)            (kernel 1)
+//   D  = rowsum(dO ∘ O), lse2 = LSE·log2(e)            (dQ kernel, run first)
 //   P  = exp(scale·Q·Kᵀ − LSE),  dP = dO·Vᵀ,  dS = P ∘ (dP − D)
-//   dV = Pᵀ·dO,  dK = scale·dSᵀ·Q                       (kernel 2, per key block)
-//   dQ = scale·dS·K                                      (kernel 3, per query block)
+//   dQ = scale·dS·K                                      (dQ kernel, per query block)
+//   dV = Pᵀ·dO,  dK = scale·dSᵀ·Q                       (dK/dV kernel, per key block)
 //
 // The statistics are padded to Npad = N rounded up to 64 rows per head;
 // padded rows carry lse2 = +∞ and D = 0, so their P (and every contribution
 // they make) is exactly 0 without any mask.
 //
-// Block masks (SPARSE): kernel 2 walks only the query tiles whose block row
-// sees its key block (the mask column), kernel 3 only the key tiles of the
-// blocks its query block sees (the mask row).
+// Block masks (SPARSE): the dK/dV kernel walks only the query tiles whose
+// block row sees its key block (the mask column), the dQ kernel only the key
+// tiles of the blocks its query block sees (the mask row).
 //
-// Packed variable-length sequences (VARLEN): kernels 2 and 3 run over
+// Packed variable-length sequences (VARLEN): both kernels run over
 // (head, segment, tile) and treat each segment as a sequence of its own
 // (rows offset to the segment start, length = the segment's). Rows past the
 // segment end read as zero from every buffer load (Q, dO, K, V and the
 // statistics alike), so they contribute nothing: their Q and dO are zero and
 // so is every product they enter.
 //
-// dQ is a sum over keys and dK, dV are sums over queries. Kernel 2 owns a
-// block of keys and walks the query tiles, so dK and dV accumulate in
-// registers; kernel 3 owns a block of queries and walks the key tiles (it
+// dQ is a sum over keys and dK, dV are sums over queries. The dK/dV kernel
+// owns a block of keys and walks the query tiles, so dK and dV accumulate in
+// registers; the dQ kernel owns a block of queries and walks the key tiles (it
 // recomputes S and dP, two extra products), so dQ accumulates in registers
 // too. Nothing is reduced through global atomics: on gfx950 the fp32 atomic
 // traffic of a fused kernel (one add per dQ element per key block and query
@@ -33,11 +33,11 @@
 // gradients are bitwise reproducible.
 //
 // Operand orientation (32x32x16 bf16 MFMA, accumulator column = lane%32):
-//  kernel 2 (column = key):
+//  dK/dV kernel (column = key):
 //   S, dP   : A = Q / dO rows from LDS, B = K / V rows held in registers.
 //   dVᵀ, dKᵀ: A = dOᵀ / Qᵀ by the LDS transpose read, B = P / dS straight from
 //             the S / dP accumulator registers (the forward's P·V trick).
-//  kernel 3 (column = query):
+//  dQ kernel (column = query):
 //   Sᵀ, dPᵀ : A = K / V rows from LDS, B = Q / dO rows held in registers.
 //   dQᵀ     : A = Kᵀ by the LDS transpose read, B = dSᵀ from the accumulators.
 // Tiles stream through LDS by buffer loads straight into LDS (no staging
@@ -58,41 +58,8 @@ enum : int { BG_VALU = 0x002, BG_MFMA = 0x008, BG_DS_READ = 0x100, BG_DS_WRITE =
              BG_TRANS = 0x400 };
 
 // ---------------------------------------------------------------------------
-// Kernel 1: D_i = Σ_c dO_ic·O_ic, lse2_i = LSE_i·log2(e) (padded rows: D = 0,
-// lse2 = +∞). One 16-byte chunk of a (padded) row per thread.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ O,
-                                                     const bf16* __restrict__ dO,
-                                                     const float* __restrict__ LSE,
-                                                     float* __restrict__ dvec,
-                                                     float* __restrict__ lse2, int N, int Npad,
-                                                     long rows_pad) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long prow = t / LPR;  // padded row index (bh·Npad + n)
-  const int part = (int)(t % LPR);
-  const long bh = prow / Npad;
-  const int n = (int)(prow - bh * Npad);
-  const bool real = prow < rows_pad && n < N;
-  float acc = 0.0f;
-  if (real) {
-    const long row = bh * N + n;
-    const bf16x8 o = *(const bf16x8*)(O + row * D + part * 8);
-    const bf16x8 g = *(const bf16x8*)(dO + row * D + part * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
-  }
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
-  if (prow < rows_pad && part == 0) {
-    dvec[prow] = real ? acc : 0.0f;
-    lse2[prow] = real ? LSE[bh * N + n] * kLog2e : INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 2: dK, dV, key-stationary.
+// dK/dV kernel, key-stationary (launched after the dQ kernel, which writes
+// the row statistics it reads).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -392,7 +359,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: dQ, query-stationary. A workgroup owns 128 queries of one head
+// dQ kernel, query-stationary. A workgroup owns 128 queries of one head
 // (32 per wave, one per lane column) and walks the 64-key tiles up to its
 // diagonal: Sᵀ = K·Qᵀ and dPᵀ = V·dOᵀ with Q, dO in registers, then
 // dS = P ∘ (dP − D) packed as the B operand of dQᵀ += Kᵀ·dSᵀ.
@@ -405,7 +372,8 @@ template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                   const float* __restrict__ lse2, const float* __restrict__ dvec,
+                   const bf16* __restrict__ O, const float* __restrict__ LSE,
+                   float* __restrict__ lse2, float* __restrict__ dvec,
                    bf16* __restrict__ dQ, int N, int Npad, int BH, int n_qtiles, float c_log2,
                    float scale, const int* __restrict__ cu, int nseq,
                    const uint8_t* __restrict__ bmask, long mask_stride) {
@@ -447,8 +415,6 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* dOh = dO + head;
   const int qi = q_start + 32 * wave + c;  // this lane's query
   const bool qv = qi < L;
-  const float l2 = qv ? lse2[(size_t)bh * Npad + row0 + qi] : INFINITY;
-  const float dq_d = qv ? dvec[(size_t)bh * Npad + row0 + qi] : 0.0f;
 
   // Qᵀ and dOᵀ operands: lane holds row qi, elements 16kk + 8h + 0..7.
   bf16x8 qr[KD], dor[KD];
@@ -456,6 +422,38 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   for (int kk = 0; kk < KD; ++kk) {
     qr[kk] = qv ? *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
     dor[kk] = qv ? *(const bf16x8*)(dOh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
+  }
+
+  // Row statistics of this lane's query, for this kernel and for the dK/dV
+  // kernel that runs after it: D = rowsum(dO∘O) and lse2 = LSE·log2(e).
+  // D is summed in one fixed order: an FMA chain over each 16-byte chunk
+  // of the row, then pairs of chunks combined as a butterfly over the chunk
+  // index (bits 3, 2, 1 of chunk 2kk + h are bits of kk, in-lane; bit 0 is
+  // the lane half). Rows in [L, Npad) of the last tile get D = 0 and
+  // lse2 = +∞, so that their P, and every contribution they make, is 0.
+  float dq_d = 0.0f;
+  {
+    const bf16* Oh = O + head;
+    float part[KD];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) {
+      const bf16x8 o = qv ? *(const bf16x8*)(Oh + (size_t)qi * D + kk * 16 + 8 * h) : bf16x8{};
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)dor[kk][e], acc);
+      part[kk] = acc;
+    }
+#pragma unroll
+    for (int m = KD / 2; m >= 1; m >>= 1)
+#pragma unroll
+      for (int kk = 0; kk < m; ++kk) part[kk] = part[kk] + part[kk + m];
+    dq_d = half_sum(part[0]);
+  }
+  const float l2 = qv ? LSE[(size_t)bh * N + row0 + qi] * kLog2e : INFINITY;
+  if (!qv) dq_d = 0.0f;
+  if (h == 0 && (VARLEN ? qv : row0 + qi < Npad)) {
+    lse2[(size_t)bh * Npad + row0 + qi] = l2;
+    dvec[(size_t)bh * Npad + row0 + qi] = dq_d;
   }
 
   // Per-lane LDS offsets: K / V rows (A operands of Sᵀ, dPᵀ) and the Kᵀ
@@ -640,14 +638,16 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                                const BwdAux& x, hipStream_t stream) {
   constexpr bool VARLEN = MODE == BWD_VARLEN, SPARSE = MODE == BWD_SPARSE;
   const int Npad = (N + kBwdRowPad - 1) / kBwdRowPad * kBwdRowPad;
-  const long rows_pad = (long)BH * Npad;
   const int len = VARLEN ? x.max_len : N;  // longest sequence the grid covers
   const int units = BH * (VARLEN ? x.nseq : 1);
   {
-    const long threads = rows_pad * (D / 8);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), grid, dim3(256), 0, stream, (const bf16*)o,
-                       (const bf16*)dout, lse, dvec, lse2, N, Npad, rows_pad);
+    // dQ, and the row statistics D and lse2 that the dK/dV kernel reads.
+    const int n_qtiles = (len + kDqBM - 1) / kDqBM;
+    const dim3 grid(n_qtiles * units);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN, SPARSE>), grid, dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                       (const bf16*)o, lse, lse2, dvec, (bf16*)dq, N, Npad, BH, n_qtiles,
+                       scale * kLog2e, scale, x.cu, x.nseq, x.bmask, x.mask_stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -659,16 +659,6 @@ static hipError_t launch_bwd_t(const void* q, const void* k, const void* v, cons
                        (const float*)lse2, (const float*)dvec, (bf16*)dk, (bf16*)dv, N,
                        Npad, BH, n_kvtiles, scale * kLog2e, scale, x.cu, x.nseq, x.bmask,
                        x.mask_stride);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int n_qtiles = (len + kDqBM - 1) / kDqBM;
-    const dim3 grid(n_qtiles * units);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN, SPARSE>), grid, dim3(256), 0, stream,
-                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                       (const float*)lse2, (const float*)dvec, (bf16*)dq, N, Npad, BH, n_qtiles,
-                       scale * kLog2e, scale, x.cu, x.nseq, x.bmask, x.mask_stride);
   }
   return hipGetLastError();
 }
