@@ -163,13 +163,26 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // Workgroup → (head[, segment], query tile). Consecutive workgroup ids go
   // to different XCDs; the remap gives each XCD a contiguous run of logical
   // tiles so the tiles of one head share that XCD's L2. Causal: heaviest
-  // tiles first.
-  const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
-  int logical = blockIdx.x;
-  if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int unit = logical / n_qtiles;
-  int qt = logical - unit * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  // tiles first. Packed sequences under the causal mask: tile-major from the
+  // last tile down, so the heaviest tiles (a query tile's work grows with its
+  // index in every segment) are issued first across all segments; ids run
+  // round-robin over the XCDs, so an XCD keeps the same (head, segment)
+  // units from tile to tile. (Without the mask a tile costs its segment's
+  // length whatever its index, and tile-major order would leave the first
+  // tiles of the longest segments to the end.)
+  int unit, qt;
+  if constexpr (VARLEN && CAUSAL) {
+    const int units = BH * nseq;
+    qt = n_qtiles - 1 - (int)(blockIdx.x / units);
+    unit = blockIdx.x - (n_qtiles - 1 - qt) * units;
+  } else {
+    const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
+    int logical = blockIdx.x;
+    if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    unit = logical / n_qtiles;
+    qt = logical - unit * n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;
+  }
   const int bh = VARLEN ? unit / nseq : unit;
   // Rows [row0, row0 + L) of the head: the whole head, or one segment (its
   // offsets clamped to [0, N] so that no offset can address outside the head).
