@@ -3,7 +3,7 @@
 offsets.
 
 Small packings mix segment lengths of 1, a few rows, exact tile multiples and
-ragged tails, both head dimensions, causal and not; they are compared element
+ragged tails, both head dimensions, causal and not, up to 70 segments; they are compared element
 by element with the full oracle. Each segment must also come out bit for bit
 as the plain kernels compute it on that segment alone (the same tiles and the
 same accumulation order). A larger packing (B=1, H=8, N=16384, lengths drawn
@@ -28,6 +28,10 @@ CASES = [
     (82, 1, 64, [200, 1, 1, 333, 128], False),
     (83, 3, 64, [5, 250, 64, 64, 17], True),
     (84, 1, 128, [513], True),
+    # 64 segments (the most the forward's longest-first order ranks), 70 (more:
+    # segment order kept), both with many equal lengths
+    (85, 1, 64, [(i * 13) % 29 + 1 for i in range(64)], False),
+    (86, 1, 128, [(i * 37) % 41 + 1 for i in range(70)], False),
 ]
 
 

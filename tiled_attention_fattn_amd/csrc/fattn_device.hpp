@@ -192,6 +192,26 @@ __device__ __forceinline__ int count_mask_tiles(const uint64_t (&mb)[kMaskWords]
   return cnt;
 }
 
+// Packed segments (rows [cu[s], cu[s+1]) clamped to [0, N]) ranked by
+// decreasing length, ties by index: the segment of rank r (r < nseq), the
+// same in every lane. Lane i ranks segment i by counting the longer ones;
+// with more than 64 segments the order is left as it is (segment r).
+__device__ __forceinline__ int segment_of_rank(const int* cu, int nseq, int N, int r, int lane) {
+  if (nseq > 64) return r;
+  int len = -1;
+  if (lane < nseq) {
+    const int a = min(max(cu[lane], 0), N);
+    len = min(max(cu[lane + 1], a), N) - a;
+  }
+  int rank = 0;
+  for (int j = 0; j < nseq; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  const uint64_t hit = __ballot(lane < nseq && rank == r);
+  return hit ? (int)__builtin_ctzll(hit) : r;
+}
+
 // Wait until this wave's outstanding global loads (including those that
 // write straight into LDS) have completed: s_waitcnt vmcnt(0).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -170,11 +170,21 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // units from tile to tile. (Without the mask a tile costs its segment's
   // length whatever its index, and tile-major order would leave the first
   // tiles of the longest segments to the end.)
+  // Without the mask, packed segments are issued longest first (every tile
+  // of a segment costs its length): the workgroup's rank r picks the r-th
+  // longest segment, heads interleaved within a rank.
   int unit, qt;
   if constexpr (VARLEN && CAUSAL) {
     const int units = BH * nseq;
     qt = n_qtiles - 1 - (int)(blockIdx.x / units);
     unit = blockIdx.x - (n_qtiles - 1 - qt) * units;
+  } else if constexpr (VARLEN) {
+    const int per_rank = BH * n_qtiles;
+    const int r = (int)(blockIdx.x / per_rank);
+    const int rem = blockIdx.x - r * per_rank;
+    qt = rem / BH;
+    const int b = rem - qt * BH;
+    unit = b * nseq + segment_of_rank(cu, nseq, N, r, lane);
   } else {
     const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
     int logical = blockIdx.x;
