@@ -85,14 +85,23 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
 
-  // Workgroup → (head, key tile): heads contiguous per XCD (they share Q, dO
-  // in that XCD's L2), key tiles of a head in increasing order (heaviest first
-  // under the causal mask).
-  const int total = n_kvtiles * BH * (VARLEN ? nseq : 1);
-  int logical = blockIdx.x;
-  if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int unit = logical / n_kvtiles;
-  const int jt = logical - unit * n_kvtiles;
+  // Workgroup → (head[, segment], key tile). Causal: tile-major from the
+  // first key tile up (early key tiles see the most queries), heaviest first
+  // over the whole grid, ids round-robin over the XCDs so an XCD keeps the
+  // same units from tile to tile. Otherwise heads contiguous per XCD (they
+  // share Q, dO in that XCD's L2), key tiles of a head in increasing order.
+  int unit, jt;
+  if constexpr (CAUSAL) {
+    const int units = BH * (VARLEN ? nseq : 1);
+    jt = (int)(blockIdx.x / units);
+    unit = blockIdx.x - jt * units;
+  } else {
+    const int total = n_kvtiles * BH * (VARLEN ? nseq : 1);
+    int logical = blockIdx.x;
+    if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    unit = logical / n_kvtiles;
+    jt = logical - unit * n_kvtiles;
+  }
   const int bh = VARLEN ? unit / nseq : unit;
   int row0 = 0, L = N;  // rows of the sequence or segment (offsets clamped to [0, N])
   if constexpr (VARLEN) {
@@ -390,14 +399,22 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
 
-  // Workgroup → (head[, segment], query tile), XCD-aware; causal: heaviest
-  // tiles first.
-  const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
-  int logical = blockIdx.x;
-  if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int unit = logical / n_qtiles;
-  int qt = logical - unit * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  // Workgroup → (head[, segment], query tile). Causal: tile-major from the
+  // last query tile down, heaviest first over the whole grid (as in the
+  // forward). Otherwise XCD-aware: each XCD gets a contiguous run of tiles.
+  int unit, qt;
+  if constexpr (CAUSAL) {
+    const int units = BH * (VARLEN ? nseq : 1);
+    const int step = (int)(blockIdx.x / units);
+    unit = blockIdx.x - step * units;
+    qt = n_qtiles - 1 - step;
+  } else {
+    const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
+    int logical = blockIdx.x;
+    if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    unit = logical / n_qtiles;
+    qt = logical - unit * n_qtiles;
+  }
   const int bh = VARLEN ? unit / nseq : unit;
   int row0 = 0, L = N;  // rows of the sequence or segment (offsets clamped to [0, N])
   if constexpr (VARLEN) {

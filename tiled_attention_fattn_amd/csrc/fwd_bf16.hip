@@ -160,24 +160,23 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int h = lane >> 5, c = lane & 31;
 
-  // Workgroup → (head[, segment], query tile). Consecutive workgroup ids go
-  // to different XCDs; the remap gives each XCD a contiguous run of logical
-  // tiles so the tiles of one head share that XCD's L2. Causal: heaviest
-  // tiles first. Packed sequences under the causal mask: tile-major from the
-  // last tile down, so the heaviest tiles (a query tile's work grows with its
-  // index in every segment) are issued first across all segments; ids run
-  // round-robin over the XCDs, so an XCD keeps the same (head, segment)
-  // units from tile to tile. (Without the mask a tile costs its segment's
-  // length whatever its index, and tile-major order would leave the first
-  // tiles of the longest segments to the end.)
-  // Without the mask, packed segments are issued longest first (every tile
-  // of a segment costs its length): the workgroup's rank r picks the r-th
-  // longest segment, heads interleaved within a rank.
+  // Workgroup → (head[, segment], query tile).
+  //  * Causal: tile-major from the last query tile down, so the heaviest
+  //    tiles (a tile's work grows with its index) of every head and segment
+  //    are issued before any lighter one, longest-processing-time first over
+  //    the whole grid; consecutive ids run round-robin over the XCDs, so an
+  //    XCD keeps the same (head, segment) units from tile to tile.
+  //  * Packed segments without the mask: longest segment first (every tile
+  //    of a segment costs its length): the workgroup's rank r picks the r-th
+  //    longest segment, heads interleaved within a rank.
+  //  * Otherwise the remap gives each XCD a contiguous run of tiles so the
+  //    tiles of one head share that XCD's L2.
   int unit, qt;
-  if constexpr (VARLEN && CAUSAL) {
-    const int units = BH * nseq;
-    qt = n_qtiles - 1 - (int)(blockIdx.x / units);
-    unit = blockIdx.x - (n_qtiles - 1 - qt) * units;
+  if constexpr (CAUSAL) {
+    const int units = BH * (VARLEN ? nseq : 1);
+    const int step = (int)(blockIdx.x / units);
+    unit = blockIdx.x - step * units;
+    qt = n_qtiles - 1 - step;
   } else if constexpr (VARLEN) {
     const int per_rank = BH * n_qtiles;
     const int r = (int)(blockIdx.x / per_rank);
@@ -186,12 +185,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int b = rem - qt * BH;
     unit = b * nseq + segment_of_rank(cu, nseq, N, r, lane);
   } else {
-    const int total = n_qtiles * BH * (VARLEN ? nseq : 1);
+    const int total = n_qtiles * BH;
     int logical = blockIdx.x;
     if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
     unit = logical / n_qtiles;
     qt = logical - unit * n_qtiles;
-    if (CAUSAL) qt = n_qtiles - 1 - qt;
   }
   const int bh = VARLEN ? unit / nseq : unit;
   // Rows [row0, row0 + L) of the head: the whole head, or one segment (its

@@ -354,12 +354,22 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
 
-  const int total = n_qtiles * BH;
-  int logical = blockIdx.x;
-  if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-  const int bh = logical / n_qtiles;
-  int qt = logical - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  // Workgroup → (head, query tile). Causal: tile-major from the last query
+  // tile down, heaviest first over the whole grid (ids round-robin over the
+  // XCDs). Otherwise each XCD gets a contiguous run of tiles (one head's
+  // tiles share its L2).
+  int bh, qt;
+  if constexpr (CAUSAL) {
+    const int step = (int)(blockIdx.x / BH);
+    bh = blockIdx.x - step * BH;
+    qt = n_qtiles - 1 - step;
+  } else {
+    const int total = n_qtiles * BH;
+    int logical = blockIdx.x;
+    if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+    bh = logical / n_qtiles;
+    qt = logical - bh * n_qtiles;
+  }
 
   const float sq = scales[bh], sk = scales[BH + bh], sv = scales[2 * BH + bh];
   const float c_log2 = sq * sk * scale_log2;
