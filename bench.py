@@ -185,15 +185,18 @@ def sweep(args):
     points = []
 
     def timed(fn):
+        # Median of per-call event timings: one slow call (a rare stall of the
+        # box) must not move a point the way it moves a mean.
         for _ in range(warm):
             fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record()
             fn()
-        b.record()
+            b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
     # Bring the shader clock up before the first point (a few calls are not
     # enough for the first configuration measured).
