@@ -62,6 +62,8 @@ constexpr int kFwdQW = 32;                  // queries per wave
 // block, and for d = 64 or shorter sequences the halved workgroup count
 // costs more than it saves (measured).
 constexpr int kFwdWideMinN = 4096;
+// d = 64 needs 168 vector registers per lane, so three waves fit on each SIMD
+// (three 4-wave workgroups per compute unit, 96 KB of LDS); d = 128 needs 256.
 constexpr int kFwdBN = 64;                  // keys per K/V tile
 constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between rescales
 constexpr float kSumGuard = 256.0f;         // 2^kRescaleTau
@@ -135,7 +137,8 @@ __device__ __forceinline__ void softmax_exp_pair(const f32x16 (&s)[2], float c_l
 }
 
 template <int D, bool CAUSAL, int EXPM, bool VARLEN, bool SPARSE, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
                      int N, int BH, int n_qtiles, float c_log2, const int* __restrict__ cu,
