@@ -62,7 +62,11 @@ enum : int { BG_VALU = 0x002, BG_MFMA = 0x008, BG_DS_READ = 0x100, BG_DS_WRITE =
 // the row statistics it reads).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// d = 128 needs the whole register file (504 of 512 per lane: K, V and the
+// dK, dV accumulators of its 32 keys), one wave per SIMD; d = 64 fits in 256,
+// two waves per SIMD.
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ lse2, const float* __restrict__ dvec,
@@ -378,7 +382,9 @@ constexpr int kDqBM = 32 * kDqWaves;  // queries per workgroup
 constexpr int kDqBN = 64;             // keys per tile
 
 template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Two waves per SIMD at d = 128 (up to 256 registers), three at d = 64 (168).
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const bf16* __restrict__ O, const float* __restrict__ LSE,
