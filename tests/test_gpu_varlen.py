@@ -32,6 +32,10 @@ CASES = [
     # segment order kept), both with many equal lengths
     (85, 1, 64, [(i * 13) % 29 + 1 for i in range(64)], False),
     (86, 1, 128, [(i * 37) % 41 + 1 for i in range(70)], False),
+    # one segment of 4100 rows: the plain forward it is compared with bit for
+    # bit runs 256-query workgroups (non-causal, d=128, N >= 4096), the packed
+    # one 128-query workgroups
+    (87, 1, 128, [4100], False),
 ]
 
 
