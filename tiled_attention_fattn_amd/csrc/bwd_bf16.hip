@@ -91,8 +91,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   // Workgroup → (head[, segment], key tile). Causal: tile-major from the
   // first key tile up (early key tiles see the most queries), heaviest first
-  // over the whole grid, ids round-robin over the XCDs so an XCD keeps the
-  // same units from tile to tile. Otherwise heads contiguous per XCD (they
+  // over the whole grid, ids round-robin over the XCDs (with a multiple of 8
+  // units an XCD keeps the same units from tile to tile). Otherwise heads contiguous per XCD (they
   // share Q, dO in that XCD's L2), key tiles of a head in increasing order.
   int unit, jt;
   if constexpr (CAUSAL) {

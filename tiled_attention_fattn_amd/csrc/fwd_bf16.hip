@@ -167,8 +167,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   //  * Causal: tile-major from the last query tile down, so the heaviest
   //    tiles (a tile's work grows with its index) of every head and segment
   //    are issued before any lighter one, longest-processing-time first over
-  //    the whole grid; consecutive ids run round-robin over the XCDs, so an
-  //    XCD keeps the same (head, segment) units from tile to tile.
+  //    the whole grid; consecutive ids run round-robin over the XCDs, so
+  //    (with a multiple of 8 units) an XCD keeps the same (head, segment)
+  //    units from tile to tile.
   //  * Packed segments without the mask: longest segment first (every tile
   //    of a segment costs its length): the workgroup's rank r picks the r-th
   //    longest segment, heads interleaved within a rank.
