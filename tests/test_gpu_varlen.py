@@ -102,15 +102,17 @@ def test_bwd_varlen_matches_oracle(seed, H, d, lengths, causal):
             assert torch.equal(got[:, :, a:b], g), f"{name} segment [{a}, {b}) differs from bwd"
 
 
-def test_varlen_single_segment_equals_plain_and_empty_segments():
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_single_segment_equals_plain_and_empty_segments(causal):
     import tiled_attention_fattn_amd as fa
     inp, t, cu, cu_t, N = _setup(90, 2, 128, [300], names=("q", "k", "v", "do"))
-    o1, l1 = fa.fwd(t["q"], t["k"], t["v"], causal=True)
-    # empty segments at the start, middle and end change nothing
+    o1, l1 = fa.fwd(t["q"], t["k"], t["v"], causal=causal)
+    # empty segments at the start, middle and end change nothing (without the
+    # mask the forward ranks segments by length: the empty ones tie at 0)
     cu2 = torch.as_tensor(np.array([0, 0, 300, 300], dtype=np.int32), device="cuda")
-    o2, l2 = fa.fwd_varlen(t["q"], t["k"], t["v"], cu2, 300, causal=True)
-    g1 = fa.bwd(t["q"], t["k"], t["v"], o1, l1, t["do"], causal=True)
-    g2 = fa.bwd_varlen(t["q"], t["k"], t["v"], o2, l2, t["do"], cu2, 300, causal=True)
+    o2, l2 = fa.fwd_varlen(t["q"], t["k"], t["v"], cu2, 300, causal=causal)
+    g1 = fa.bwd(t["q"], t["k"], t["v"], o1, l1, t["do"], causal=causal)
+    g2 = fa.bwd_varlen(t["q"], t["k"], t["v"], o2, l2, t["do"], cu2, 300, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
