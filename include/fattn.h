@@ -187,7 +187,7 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  *               the order in which the kernel's P operand holds keys),
  *               then fp32 scales [3][B·H]
  *               (Q', K', V per head: amax/448, or 1 for an all-zero head),
- *               then an fp32 [3][B·H][⌈N/256⌉] scratch of per-chunk amax.
+ *               then an fp32 [3][B·H][⌈N/128⌉] scratch of per-chunk amax.
  * Each operand is quantised per (b,h): code = e4m3(x·448/amax), the exact
  * ratio rounded to nearest even. Q' keeps a second e4m3 term for its
  * quantisation residual, Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that
