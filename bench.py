@@ -26,9 +26,9 @@ PEAK_FP8 = 5000.0       # TFLOP/s, MI355X dense fp8 MFMA
 PARTS = ["fwd", "bwd", "fp8"]
 PART_WORKLOAD = {"fwd": 3, "bwd": 4, "fp8": 5}
 KERNEL_SOURCES = {
-    "fwd": ["fwd_bf16.hip", "fattn_device.hpp"],
-    "bwd": ["bwd_bf16.hip", "fattn_device.hpp"],
-    "fp8": ["fwd_fp8.hip", "fattn_device.hpp"],
+    "fwd": ["fwd_bf16.hip", "fattn_device.hpp", "fattn_launch.h"],
+    "bwd": ["bwd_bf16.hip", "fattn_device.hpp", "fattn_launch.h"],
+    "fp8": ["fwd_fp8.hip", "fattn_device.hpp", "fattn_launch.h"],
 }
 
 
