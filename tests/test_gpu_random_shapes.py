@@ -6,14 +6,15 @@ line up with them), ragged sequence lengths up to 900 in both head
 dimensions, causal and not, compared element by element with the float64
 oracle; plus two single-head sequences just above 4096 rows with d = 128,
 where the non-causal launch switches to 256-query workgroups (forward only,
-full oracle).
+full oracle); and the fp8 forward on seeded random shapes, with and without
+the rotation, against exact attention on the unquantised inputs.
 """
 import numpy as np
 import pytest
 
 from oracle.attention import attention_backward, attention_forward
-from tests.parity import assert_bf16_close, assert_lse_close, to_np
-from tiled_attention_fattn_amd.inputs import gen_workload, to_device_bf16
+from tests.parity import FP8_REL_RMS, assert_bf16_close, assert_lse_close, rel_rms, to_np
+from tiled_attention_fattn_amd.inputs import WORKLOADS, gen_workload, to_device_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -65,3 +66,39 @@ def test_random_long_single_head_fwd(k, N, causal):
     ref_o, ref_lse = attention_forward(inp["q"][0], inp["k"][0], inp["v"][0], causal, scale)
     assert_bf16_close(to_np(o), ref_o, f"O {shape} causal={causal}")
     assert_lse_close(to_np(lse), ref_lse, f"LSE {shape} causal={causal}")
+
+
+def _fp8_shapes():
+    rng = np.random.default_rng(20261203)
+    cases = []
+    for i in range(6):
+        B = int(rng.integers(1, 3))
+        H = int(rng.choice([1, 3, 5]))
+        N = int(rng.integers(1, 700))
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        cases.append((230 + i, (B, H, N, d), causal))
+    return cases
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+@pytest.mark.parametrize("k,shape,causal", _fp8_shapes())
+def test_random_shape_fp8(k, shape, causal, rotate):
+    import tiled_attention_fattn_amd as fa
+    w = WORKLOADS[5]
+    inp = gen_workload(k, shape=shape, outlier_frac=w["outlier_frac"],
+                       outlier_factor=w["outlier_factor"])
+    q, kk, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    B, H, N, d = shape
+    scale = d ** -0.5
+    ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    print(f"[random fp8] seed={k} shape={shape} causal={causal} rotate={rotate}", flush=True)
+    o, _ = fa.fwd_fp8(q, kk, v, causal=causal, scale=scale, rotate=rotate, seed=k, workspace=ws)
+    torch.cuda.synchronize()
+    ref_o, _ = attention_forward(inp["q"][0], inp["k"][0], inp["v"][0], causal, scale)
+    got = to_np(o)
+    assert np.all(np.isfinite(got))
+    rr = rel_rms(got, ref_o)
+    # Without the rotation the outliers of Q and K make the error larger; the
+    # stated bound applies to the rotated path.
+    assert rr <= (FP8_REL_RMS if rotate else 0.15), f"fp8 O rel-RMS {rr:.3e} (rotate={rotate})"
