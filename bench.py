@@ -64,10 +64,13 @@ def copy_calibration(nbytes, reps):
 
 
 def source_hash(part):
-    """Hash of the kernel sources of a bench part, ignoring comments and blank
-    lines (a comment edit does not change the compiled kernels)."""
+    """Hash of the kernel sources of a bench part and of the compile flags,
+    ignoring comments and blank lines (a comment edit does not change the
+    compiled kernels, a code-generation flag can)."""
     import re
+    from tiled_attention_fattn_amd.build import FLAGS
     h = hashlib.sha256()
+    h.update(" ".join(f for f in FLAGS if not f.startswith("/")).encode())
     for f in KERNEL_SOURCES[part]:
         with open(os.path.join(HERE, "tiled_attention_fattn_amd", "csrc", f)) as fh:
             text = fh.read()

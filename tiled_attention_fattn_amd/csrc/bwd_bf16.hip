@@ -80,10 +80,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   constexpr int RB = D * 2;                         // bytes per Q / dO row
   constexpr int QT_BYTES = kBwdBM * RB;             // one Q or dO tile
   constexpr int LD_LOADS = QT_BYTES / 1024 / kBwdWaves;  // 1 KB wave loads per tile per wave
-  // LDS: Q0 | dO0 | Q1 | dO1 | stats[2 stages][lse2 64 | D 64]
-  __shared__ __attribute__((aligned(16))) char lds[4 * QT_BYTES + 4 * kBwdBM * 4];
-  char* const q_lds = lds;                         // stage s: Q at s·2·QT, dO at s·2·QT + QT
-  char* const st_lds = lds + 4 * QT_BYTES;         // stage s: lse2 at s·512, D at s·512 + 256
+  // LDS: stats[2 stages][lse2 64 | D 64] | Q0 | dO0 | Q1 | dO1. The statistics
+  // come first so that their reads reach them through the 16-bit immediate
+  // offset of the DS instructions (behind 64 KB of tiles every read needed an
+  // address computed by a VALU op); 1 KB keeps the tiles' bank pattern.
+  __shared__ __attribute__((aligned(16))) char lds[4 * kBwdBM * 4 + 4 * QT_BYTES];
+  char* const st_lds = lds;                        // stage s: lse2 at s·512, D at s·512 + 256
+  char* const q_lds = lds + 4 * kBwdBM * 4;        // stage s: Q at s·2·QT, dO at s·2·QT + QT
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
