@@ -93,9 +93,9 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o,
  *   dq, dk, dv  [B,H,N,d] bf16 outputs.
  *   workspace   device memory of at least fattn_bwd_workspace_bytes(B,H,N,d)
  *               bytes, 256-byte aligned; contents on entry are ignored.
- *               Layout (Npad = N rounded up to 64): fp32 D = rowsum(dO∘O)
+ *               Layout (Npad = N rounded up to 64): fp32 −D, D = rowsum(dO∘O),
  *               [B,H,Npad] at offset 0, then fp32 LSE·log2(e) [B,H,Npad]
- *               (padded rows: D = 0, +∞), each piece 256-byte aligned; with
+ *               (padded rows: 0, +∞), each piece 256-byte aligned; with
                packed sequences (fattn_bwd_varlen) only the rows of the
                segments are written.
  * dK and dV are accumulated by the workgroup that owns their key block and dQ

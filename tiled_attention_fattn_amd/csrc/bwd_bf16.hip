@@ -3,13 +3,14 @@
 // Gradient of ⟨O, dO⟩ for O = softmax(scale·Q·Kᵀ [causal])·V, recomputing P
 // from the forward's log-sum-exp (the pages name the dS and dQ terms:
 // FlashAttention-4 gist, technical summary 2.C):
-//   D  = rowsum(dO ∘ O), lse2 = LSE·log2(e)            (dQ kernel, run first)
+//   D  = rowsum(dO ∘ O), lse2 = LSE·log2(e)            (dQ kernel, run first;
+//                                                        it stores −D for the dK/dV kernel)
 //   P  = exp(scale·Q·Kᵀ − LSE),  dP = dO·Vᵀ,  dS = P ∘ (dP − D)
 //   dQ = scale·dS·K                                      (dQ kernel, per query block)
 //   dV = Pᵀ·dO,  dK = scale·dSᵀ·Q                       (dK/dV kernel, per key block)
 //
 // The statistics are padded to Npad = N rounded up to 64 rows per head;
-// padded rows carry lse2 = +∞ and D = 0, so their P (and every contribution
+// padded rows carry lse2 = +∞ and −D = 0, so their P (and every contribution
 // they make) is exactly 0 without any mask.
 //
 // Block masks (SPARSE): the dK/dV kernel walks only the query tiles whose
@@ -80,12 +81,12 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   constexpr int RB = D * 2;                         // bytes per Q / dO row
   constexpr int QT_BYTES = kBwdBM * RB;             // one Q or dO tile
   constexpr int LD_LOADS = QT_BYTES / 1024 / kBwdWaves;  // 1 KB wave loads per tile per wave
-  // LDS: stats[2 stages][lse2 64 | D 64] | Q0 | dO0 | Q1 | dO1. The statistics
+  // LDS: stats[2 stages][lse2 64 | −D 64] | Q0 | dO0 | Q1 | dO1. The statistics
   // come first so that their reads reach them through the 16-bit immediate
   // offset of the DS instructions (behind 64 KB of tiles every read needed an
   // address computed by a VALU op); 1 KB keeps the tiles' bank pattern.
   __shared__ __attribute__((aligned(16))) char lds[4 * kBwdBM * 4 + 4 * QT_BYTES];
-  char* const st_lds = lds;                        // stage s: lse2 at s·512, D at s·512 + 256
+  char* const st_lds = lds;                        // stage s: lse2 at s·512, −D at s·512 + 256
   char* const q_lds = lds + 4 * kBwdBM * 4;        // stage s: Q at s·2·QT, dO at s·2·QT + QT
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -168,7 +169,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     buffer_to_lds<LD_LOADS>(Qh + (size_t)qs * D, (L - qs) * RB, qb, ld_off, wave * LD_LOADS);
     buffer_to_lds<LD_LOADS>(dOh + (size_t)qs * D, (L - qs) * RB, qb + QT_BYTES, ld_off,
                             wave * LD_LOADS);
-    // lse2 (wave 0) and D (wave 1): 64 floats = one 4-byte element per lane
+    // lse2 (wave 0) and −D (wave 1): 64 floats = one 4-byte element per lane
     // (a segment's rows only: rows past its end read as zero).
     if (wave < 2)
       stats_to_lds((wave == 0 ? lse_h : d_h) + qs, st_lds + stage * 512 + wave * 256, lane,
@@ -198,13 +199,19 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       hs.d4[g] = *(const f32x4*)(d_s + 32 * hh + 8 * g + 4 * h);
     }
   };
+  auto neg_d = [](const HalfState& hs) __device__ {
+    f32x16 c;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) c[x] = hs.d4[x / 4][x % 4];
+    return c;
+  };
   auto pds_step = [&](const f32x16& sv, const f32x16& dpv, int hh, int qs, bool masked,
                       HalfState& hs, int x) __device__ {
     const int g = x / 4, e = x % 4, r = x;
     const int qrow = 32 * hh + 8 * g + 4 * h;
     float p = exp2_hw(fmaf(sv[r], c_log2, -hs.l4[g][e]));
     if (CAUSAL && masked && key > qs + qrow + e) p = 0.0f;
-    const float ds = p * (dpv[r] - hs.d4[g][e]);
+    const float ds = p * dpv[r];  // dpv = dP − D (the chain starts at −D)
     hs.pv[e & 1] = p;
     hs.dsv[e & 1] = ds;
     if (e & 1) {
@@ -243,15 +250,17 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     f32x16 sd[2][2];  // [half][S, dP]
     bf16x8 ra[NR];
     HalfState hs0, hs1;
+    load_stats(lse_s, d_s, 0, hs0);
 #pragma unroll
     for (int i = 0; i < kLeadB; ++i) ra[i] = sread(i);
-    load_stats(lse_s, d_s, 0, hs0);
     load_stats(lse_s, d_s, 1, hs1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int hh = i / (2 * KD), kk = (i / 2) % KD, w = i % 2;
-      sd[hh][w] = mfma32(ra[i], w ? vreg[kk] : kreg[kk], kk == 0 ? f32x16{} : sd[hh][w]);
+      // The dP chain starts from −D of its rows, so it ends at dP − D.
+      const f32x16 c0 = w ? neg_d(hh ? hs1 : hs0) : f32x16{};
+      sd[hh][w] = mfma32(ra[i], w ? vreg[kk] : kreg[kk], kk == 0 ? c0 : sd[hh][w]);
       if (i + kLeadB < NR) ra[i + kLeadB] = sread(i + kLeadB);
       if (hh == 1) {
         // 16 element steps of half 0 over the 2KD pieces of phase B.
@@ -479,7 +488,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   if (!qv) dq_d = 0.0f;
   if (h == 0 && (VARLEN ? qv : row0 + qi < Npad)) {
     lse2[(size_t)bh * Npad + row0 + qi] = l2;
-    dvec[(size_t)bh * Npad + row0 + qi] = dq_d;
+    dvec[(size_t)bh * Npad + row0 + qi] = -dq_d;
   }
 
   // Per-lane LDS offsets: K / V rows (A operands of Sᵀ, dPᵀ) and the Kᵀ
