@@ -2,6 +2,7 @@
 
 One step = one pass of the whole hot path over resident synthetic inputs:
   * bf16 forward, non-causal, B=2 H=16 N=8192 d=128   (fattn_fwd)
+  * bf16 forward, causal,     B=8 H=16 N=2048 d=128   (fattn_fwd; causal tile skipping)
   * bf16 backward, causal,   B=4 H=16 N=4096 d=128   (fattn_bwd)
   * fp8 forward with Hadamard rotation, non-causal, B=4 H=16 N=4096 d=128
     (fattn_fwd_fp8)
@@ -23,10 +24,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16 = 2500.0      # TFLOP/s, MI355X dense bf16 MFMA
 PEAK_FP8 = 5000.0       # TFLOP/s, MI355X dense fp8 MFMA
 
-PARTS = ["fwd", "bwd", "fp8"]
-PART_WORKLOAD = {"fwd": 3, "bwd": 4, "fp8": 5}
+PARTS = ["fwd", "fwd_causal", "bwd", "fp8"]
+PART_WORKLOAD = {"fwd": 3, "fwd_causal": 2, "bwd": 4, "fp8": 5}
 KERNEL_SOURCES = {
     "fwd": ["fwd_bf16.hip", "fattn_device.hpp", "fattn_launch.h"],
+    "fwd_causal": ["fwd_bf16.hip", "fattn_device.hpp", "fattn_launch.h"],
     "bwd": ["bwd_bf16.hip", "fattn_device.hpp", "fattn_launch.h"],
     "fp8": ["fwd_fp8.hip", "fattn_device.hpp", "fattn_launch.h"],
 }
@@ -42,6 +44,11 @@ def parse():
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--no-exp-variants", action="store_true",
                     help="skip the separate hw/poly/split exp2 timing of the forward")
+    ap.add_argument("--exp-mode", default="auto", choices=["auto", "hw", "poly", "split"],
+                    help="exp2 variant of the timed forward and fp8 calls (default: auto)")
+    ap.add_argument("--fp8-error-rows", type=int, default=64,
+                    help="rows per head of the fp8 output compared with the oracle, with and "
+                         "without the rotation, in the cpu_baseline leg (0: skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the sequence-length / head-dimension sweep: N = 4096 to "
                          "32768 at a fixed B*H*N = 262144 tokens, d = 64 and 128")
@@ -91,6 +98,10 @@ def committed_traffic(part):
     return rec.get("bytes_per_launch")
 
 
+def part_peak(part):
+    return PEAK_FP8 if part == "fp8" else PEAK_BF16
+
+
 def part_flops(part):
     from tiled_attention_fattn_amd.inputs import WORKLOADS, flops_bwd, flops_fwd
     w = WORKLOADS[PART_WORKLOAD[part]]
@@ -98,8 +109,8 @@ def part_flops(part):
     return flops_bwd(*args) if part == "bwd" else flops_fwd(*args)
 
 
-def setup_part(part, torch, fa):
-    """Resident inputs/outputs for one part; returns a zero-arg launch closure."""
+def setup_part(part, torch, fa, exp_mode="auto"):
+    """Resident inputs/outputs for one part; returns a launch closure."""
     from tiled_attention_fattn_amd.inputs import WORKLOADS, gen_workload, to_device_bf16
     k = PART_WORKLOAD[part]
     w = WORKLOADS[k]
@@ -109,11 +120,11 @@ def setup_part(part, torch, fa):
     t = {n: to_device_bf16(inp[n][1]) for n in names}
     del inp
     scale = d ** -0.5
-    if part == "fwd":
+    if w["kind"] == "fwd":
         o = torch.empty_like(t["q"])
         lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-        return lambda mode="auto": fa.fwd(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
-                                          exp_mode=mode, out=o, lse=lse)
+        return lambda mode=exp_mode: fa.fwd(t["q"], t["k"], t["v"], causal=w["causal"],
+                                            scale=scale, exp_mode=mode, out=o, lse=lse)
     if part == "bwd":
         o, lse = fa.fwd(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale)
         grads = tuple(torch.empty_like(t["q"]) for _ in range(3))
@@ -124,13 +135,64 @@ def setup_part(part, torch, fa):
     o2 = torch.empty_like(t["q"])
     ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
 
-    def run(mode="full", exp_mode="auto"):
+    def run(mode="full", em=exp_mode):
         if mode == "attend":  # the attention step alone on the operands of the last full call
             return fa.fwd_fp8_attend(ws, B, H, N, d, causal=w["causal"], scale=scale,
-                                     want_lse=False, out=o2, exp_mode=exp_mode)
+                                     want_lse=False, out=o2, exp_mode=em)
+        if mode == "outputs":  # O with and without the rotation (outside the timed region)
+            outs = {}
+            for rot in (True, False):
+                outs[rot] = fa.fwd_fp8(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
+                                       rotate=rot, seed=k, want_lse=False, workspace=ws,
+                                       exp_mode=em)[0]
+            return outs
         return fa.fwd_fp8(t["q"], t["k"], t["v"], causal=w["causal"], scale=scale,
-                          rotate=w["rotate"], seed=k, want_lse=False, workspace=ws, out=o)
+                          rotate=w["rotate"], seed=k, want_lse=False, workspace=ws, out=o,
+                          exp_mode=em)
     return run
+
+
+def fp8_error_sample(run, rows_per_head):
+    """Sampled rows of the fp8 output with and without the rotation, copied to
+    the host for the oracle leg: (rows, {rotate: float64 [B, H, rows, d]})."""
+    import torch
+    w = WORKLOADS_CACHE()[PART_WORKLOAD["fp8"]]
+    outs = run("outputs")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    N = w["N"]
+    rows = np.unique(np.concatenate([[0, N - 1], rng.choice(N, rows_per_head, replace=False)]))
+    idx = torch.as_tensor(rows, device=outs[True].device)
+    got = {rot: o[:, :, idx].float().cpu().numpy().astype(np.float64) for rot, o in outs.items()}
+    return rows, got
+
+
+def WORKLOADS_CACHE():
+    from tiled_attention_fattn_amd.inputs import WORKLOADS
+    return WORKLOADS
+
+
+def fp8_error_vs_oracle(rows, got):
+    """Relative RMS of the fp8 output against the float64 oracle's exact
+    attention on the unrotated bf16 inputs, on the sampled rows of every head,
+    with and without the rotation (the checker's side: oracle code only)."""
+    from oracle.attention import attention_forward_rows
+    from tiled_attention_fattn_amd.inputs import gen_workload
+    k = PART_WORKLOAD["fp8"]
+    w = WORKLOADS_CACHE()[k]
+    x = gen_workload(k, names=("q", "k", "v"))
+    scale = w["d"] ** -0.5
+    ref = np.empty_like(got[True])
+    for b in range(w["B"]):
+        for h in range(w["H"]):
+            ref[b, h] = attention_forward_rows(x["q"][0], x["k"][0], x["v"][0], w["causal"],
+                                               scale, b, h, rows)[0]
+    den = np.linalg.norm(ref)
+    err = {rot: float(np.linalg.norm(g - ref) / den) for rot, g in got.items()}
+    return {"rel_rms_rotate": round(err[True], 5), "rel_rms_no_rotate": round(err[False], 5),
+            "ratio_no_rotate_over_rotate": round(err[False] / err[True], 3), "bound": 6e-2,
+            "sample": f"{len(rows)} rows of each of the {w['B'] * w['H']} heads of "
+                      f"{w['name']}, against float64 exact attention (oracle)"}
 
 
 def cpu_baseline(parts, heads):
@@ -153,7 +215,7 @@ def cpu_baseline(parts, heads):
         x = gen_workload(k, names=names, shape=shape)
         scale = w["d"] ** -0.5
         t0 = time.perf_counter()
-        if part == "fwd":
+        if w["kind"] == "fwd":
             attention_forward(x["q"][0], x["k"][0], x["v"][0], w["causal"], scale)
         elif part == "bwd":
             attention_backward(x["q"][0], x["k"][0], x["v"][0], x["do"][0], w["causal"], scale)
@@ -332,7 +394,7 @@ def main():
     parts = [p for p in args.parts.split(",") if p]
     torch.cuda.set_device(0)
     clocks_before = gpu_clocks()
-    launch = {p: setup_part(p, torch, fa) for p in parts}
+    launch = {p: setup_part(p, torch, fa, args.exp_mode) for p in parts}
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -364,7 +426,7 @@ def main():
     info = {}
     for p in parts:
         tf = flops[p] / (part_ms[p] * 1e-3) / 1e12
-        peak = PEAK_FP8 if p == "fp8" else PEAK_BF16
+        peak = part_peak(p)
         info[p] = {"workload": fa_workload_name(p), "ms": round(part_ms[p], 4),
                    "ms_median": round(float(np.median(samples[p])), 4),
                    "ms_min": round(float(np.min(samples[p])), 4),
@@ -437,9 +499,17 @@ def main():
     if clocks_before or clocks:
         info["gpu_clock_mhz"] = {"before": clocks_before, "after": clocks}
 
+    # GPU outputs for the fp8 error check (after all timing).
+    fp8_sample = None
+    if "fp8" in parts and not args.no_cpu_baseline and args.fp8_error_rows > 0:
+        fp8_sample = fp8_error_sample(launch["fp8"], args.fp8_error_rows)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(parts, args.cpu_heads)
+        if fp8_sample is not None:
+            # The checker's leg: the oracle's exact attention on the sampled rows.
+            info["fp8"]["error_vs_oracle"] = fp8_error_vs_oracle(*fp8_sample)
 
     dtype = "bf16" if "fp8" not in parts else ("fp8" if parts == ["fp8"] else "bf16+fp8")
     line = {
@@ -456,15 +526,21 @@ def main():
 
 
 def gpu_clocks():
-    """Current shader clock (MHz) of GPU 0 from rocm-smi, or None."""
+    """Current shader clock (MHz) of GPU 0, or None.
+
+    Read in-process from the amdgpu driver's sysfs DPM table of that device
+    (the line marked '*' of pp_dpm_sclk under its PCI address): nothing is
+    spawned from this process once it has touched the GPU."""
     import re
-    import subprocess
+    import torch
     try:
-        out = subprocess.run(["rocm-smi", "-d", "0", "--showclocks"], capture_output=True,
-                             text=True, timeout=20).stdout
-    except Exception:  # noqa: BLE001 (no rocm-smi: report nothing)
+        p = torch.cuda.get_device_properties(0)
+        bdf = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        with open(f"/sys/bus/pci/devices/{bdf}/pp_dpm_sclk") as fh:
+            text = fh.read()
+    except Exception:  # noqa: BLE001 (no sysfs entry: report nothing)
         return None
-    m = re.search(r"sclk.*?\((\d+)Mhz\)", out)
+    m = re.search(r"(\d+)\s*Mhz\s*\*", text, re.IGNORECASE)
     return int(m.group(1)) if m else None
 
 

@@ -96,11 +96,17 @@ fattn_status fattn_fwd(const void* q, const void* k, const void* v, void* o,
  *               Layout (Npad = N rounded up to 64): fp32 −D, D = rowsum(dO∘O),
  *               [B,H,Npad] at offset 0, then fp32 LSE·log2(e) [B,H,Npad]
  *               (padded rows: 0, +∞), each piece 256-byte aligned; with
-               packed sequences (fattn_bwd_varlen) only the rows of the
-               segments are written.
- * dK and dV are accumulated by the workgroup that owns their key block and dQ
- * by the workgroup that owns its query block (which recomputes the scores):
- * no global atomics, so all three gradients are bitwise reproducible.
+ *               packed sequences (fattn_bwd_varlen) only the rows of the
+ *               segments are written.
+ * The gradients are the standard ones of the softmax attention (FlashAttention-4
+ * gist, technical summary 2.C, names dS = P∘(dP − D) and the dQ reduction):
+ * dV = Pᵀ·dO, dP = dO·Vᵀ, dS = P∘(dP − D), dQ = scale·dS·K, dK = scale·dSᵀ·Q,
+ * with P recomputed from the saved LSE. That summary reduces dQ with global
+ * atomics; here dK and dV are accumulated by the workgroup that owns their
+ * key block and dQ by the workgroup that owns its query block (which
+ * recomputes the scores): no global atomics, so all three gradients are
+ * bitwise reproducible. Errors: EINVAL/ENOTSUP as fattn_fwd; EWORKSPACE for a
+ * NULL, misaligned or too small workspace; EDEVICE, EHIP.
  */
 size_t fattn_bwd_workspace_bytes(int B, int H, int N, int d);
 fattn_status fattn_bwd(const void* q, const void* k, const void* v,
@@ -192,7 +198,10 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  * ratio rounded to nearest even. Q' keeps a second e4m3 term for its
  * quantisation residual, Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that
  * Q' ≈ scale_q·(Q8 + Q8lo/16); the scores use both terms (two fp8 MFMAs).
- * P is quantised to e4m3 after multiplication by 2^8.
+ * The softmax keeps its exponent offset within a factor 2 of the running row
+ * max (rescaling the partial output when the max grows by more), so every
+ * unnormalised probability P̃ is at most 2; P is quantised to e4m3 as
+ * P̃·2^7 ≤ 256.
  * Additionally requires B·H ≤ 65535 (ENOTSUP otherwise).
  */
 size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d);

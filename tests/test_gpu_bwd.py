@@ -18,14 +18,16 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def _run(k, shape, causal):
+def _run(k, shape, causal, poison=False):
     import tiled_attention_fattn_amd as fa
     inp = gen_workload(k, names=("q", "k", "v", "do"), shape=shape)
     q, kk, v, do = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v", "do"))
     scale = shape[-1] ** -0.5
     print(f"[bwd] seed={k} shape={shape} causal={causal}", flush=True)
     o, lse = fa.fwd(q, kk, v, causal=causal, scale=scale)
-    dq, dk, dv = fa.bwd(q, kk, v, o, lse, do, causal=causal, scale=scale)
+    # poison: outputs prefilled with NaN, so an element no workgroup writes shows
+    out = tuple(torch.full_like(q, float("nan")) for _ in range(3)) if poison else None
+    dq, dk, dv = fa.bwd(q, kk, v, o, lse, do, causal=causal, scale=scale, out=out)
     torch.cuda.synchronize()
     return inp, (dq, dk, dv), scale
 
@@ -54,7 +56,10 @@ def test_bwd_matches_oracle(k, shape, causal):
 def test_bwd_full_size_sampled_heads():
     w = WORKLOADS[4]
     shape = (w["B"], w["H"], w["N"], w["d"])
-    inp, grads, scale = _run(4, shape, w["causal"])
+    inp, grads, scale = _run(4, shape, w["causal"], poison=True)
+    # Every element of every gradient written (the whole grid of the bench's launch).
+    for name, g in zip(("dQ", "dK", "dV"), grads):
+        assert not torch.isnan(g).any().item(), f"{name}: elements left unwritten"
     for (b, h) in [(0, 0), (w["B"] - 1, w["H"] - 1), (2, 7)]:
         sl = (slice(b, b + 1), slice(h, h + 1))
         ref = attention_backward(inp["q"][0][sl], inp["k"][0][sl], inp["v"][0][sl],

@@ -16,7 +16,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle.attention import attention_forward, attention_forward_rows
+from oracle.attention import attention_forward
 from oracle.e4m3 import e4m3_decode
 from oracle.fp8_model import fp8_attention_model
 from tests.parity import FP8_REL_RMS, max_abs, rel_rms, to_np
@@ -134,36 +134,40 @@ def test_fp8_matches_exact_attention(shape, causal, rotate):
         assert np.all(_unpermute_v8t(v8t, None)[:, :, N:] == 0)
 
 
-def test_fp8_full_size_sampled_and_rotation_ratio():
+def test_fp8_whole_tensor_error_and_rotation_ratio():
+    # The fp8 workload at full size (B=4 H=16 N=4096 d=128, outliers), relative
+    # RMS over the whole O tensor (all 64 heads) against the float64 exact
+    # attention on the unrotated bf16 inputs, with and without the rotation.
+    # Outputs are prefilled with NaN: every element must be written.
+    import tiled_attention_fattn_amd as fa
     w = WORKLOADS[5]
     shape = (w["B"], w["H"], w["N"], w["d"])
     inp = _inputs(5, shape)
     scale = w["d"] ** -0.5
-    N = w["N"]
-    rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, N - 1], rng.integers(0, N, 59)]))
-    heads = [(0, 0), (w["B"] - 1, w["H"] - 1), (1, 9)]
-    refs = {bh: attention_forward_rows(inp["q"][0], inp["k"][0], inp["v"][0], False, scale,
-                                       bh[0], bh[1], rows) for bh in heads}
-    err = {}
+    q, k, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    B, H, N, d = shape
+    ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    got = {}
     for rotate in (True, False):
-        o, _, _ = _run(inp, False, rotate, seed=5)
-        o3 = o.view(-1, N, w["d"])
-        got = np.concatenate([to_np(o3[b * w["H"] + h][torch.as_tensor(rows, device=o.device)])
-                              for (b, h) in heads])
-        ref = np.concatenate([refs[bh][0] for bh in heads])
-        err[rotate] = rel_rms(got, ref)
-        bound = FP8_REL_RMS if rotate else 0.15
-        assert err[rotate] <= bound, f"rotate={rotate}: rel-RMS {err[rotate]:.3e}"
+        print(f"[fp8] whole tensor {w['name']} rotate={rotate}", flush=True)
+        o = torch.full_like(q, float("nan"))
+        fa.fwd_fp8(q, k, v, scale=scale, rotate=rotate, seed=5, want_lse=False, workspace=ws,
+                   out=o)
+        torch.cuda.synchronize()
+        assert not torch.isnan(o).any().item(), f"rotate={rotate}: elements left unwritten"
+        got[rotate] = to_np(o)
+    ref, _ = attention_forward(inp["q"][0], inp["k"][0], inp["v"][0], False, scale)
+    err = {rot: rel_rms(g, ref) for rot, g in got.items()}
     ratio = err[False] / err[True]
-    print(f"[fp8] rel-RMS with rotation {err[True]:.4e}, without {err[False]:.4e}, "
-          f"ratio {ratio:.3f}", flush=True)
+    print(f"[fp8] whole tensor rel-RMS with rotation {err[True]:.4e}, without "
+          f"{err[False]:.4e}, ratio {ratio:.3f}", flush=True)
     out = os.environ.get("FATTN_REPORT_DIR")
     if out:
         with open(os.path.join(out, "fp8_rotation_error.json"), "w") as fh:
             json.dump({"rel_rms_rotate": err[True], "rel_rms_no_rotate": err[False],
-                       "ratio": ratio, "workload": w["name"], "rows": len(rows),
-                       "heads": heads}, fh)
+                       "ratio": ratio, "workload": w["name"], "scope": "whole O tensor"}, fh)
+    assert err[True] <= FP8_REL_RMS, f"rotate=True: rel-RMS {err[True]:.3e}"
+    assert err[False] <= 0.2, f"rotate=False: rel-RMS {err[False]:.3e}"
 
 
 @pytest.mark.parametrize("causal", [False, True])

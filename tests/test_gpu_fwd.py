@@ -19,14 +19,17 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def _run(k, shape, causal, exp_mode, scale=None):
+def _run(k, shape, causal, exp_mode, scale=None, poison=False):
     import tiled_attention_fattn_amd as fa
     inp = gen_workload(k, shape=shape)
     q, kk, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
     d = shape[-1]
     scale = d ** -0.5 if scale is None else scale
     print(f"[fwd] seed={k} shape={shape} causal={causal} exp={exp_mode}", flush=True)
-    o, lse = fa.fwd(q, kk, v, causal=causal, scale=scale, exp_mode=exp_mode)
+    # poison: outputs prefilled with NaN, so an element no workgroup writes shows
+    o = torch.full_like(q, float("nan")) if poison else None
+    lse = torch.full(shape[:3], float("nan"), device=q.device) if poison else None
+    o, lse = fa.fwd(q, kk, v, causal=causal, scale=scale, exp_mode=exp_mode, out=o, lse=lse)
     torch.cuda.synchronize()
     return inp, o, lse, scale
 
@@ -60,7 +63,10 @@ def test_fwd_full_size_sampled(wk):
     w = WORKLOADS[wk]
     shape = (w["B"], w["H"], w["N"], w["d"])
     for exp_mode in (["hw", "poly", "split"] if wk == 3 else ["auto"]):
-        inp, o, lse, scale = _run(wk, shape, w["causal"], exp_mode)
+        inp, o, lse, scale = _run(wk, shape, w["causal"], exp_mode, poison=True)
+        # Every output element written (the whole grid of the bench's launch).
+        assert not torch.isnan(o).any().item(), f"O: elements left unwritten ({exp_mode})"
+        assert not torch.isnan(lse).any().item(), f"LSE: rows left unwritten ({exp_mode})"
         o_np = o.view(-1, w["N"], w["d"])
         lse_np = lse.view(-1, w["N"])
         rng = np.random.default_rng(wk)

@@ -65,13 +65,13 @@ def test_bwd_long_sequence_one_head(k, d):
 
 @pytest.mark.parametrize("outliers", [False, True])
 def test_fp8_long_sequence_sampled(outliers):
-    # Without outliers the output is held to the fp8 bound against exact
-    # attention. With the 0.1% x20 outliers of the fp8 workload, per-head e4m3
-    # operands alone already put the exact-arithmetic model about 6.4% from
-    # exact attention at this length (more rows, larger per-head amax), so
-    # there the kernel is compared with that model on the same rows: what is
-    # left is the kernel's own error (P in e4m3, fp32 accumulation), held to
-    # 4e-2 against the 2.5% the quantisation of P contributes on its own.
+    # N = 32768 on sampled rows, reported against exact attention and against
+    # the oracle's operand-quantised model on the same rows. Without outliers
+    # the output is held to the fp8 bound against exact attention. With the
+    # 0.1% x20 outliers of the fp8 workload the model alone (operands in
+    # e4m3, exact P) is about 5.4% from exact attention on these rows (a CPU
+    # oracle test pins that), so the kernel is held to the model at 4e-2 and
+    # its error against exact attention is reported.
     import tiled_attention_fattn_amd as fa
     from oracle.fp8_model import (dequantize, dequantize_split, quantize_per_head,
                                   quantize_per_head_split)
@@ -87,22 +87,22 @@ def test_fp8_long_sequence_sampled(outliers):
     torch.cuda.synchronize()
     rows = _rows(N, k)
     idx = torch.as_tensor(rows, device=o.device)
-    if outliers:
-        q8, q8lo, sq = quantize_per_head_split(rotate(inp["q"][0], k))
-        k8, sk = quantize_per_head(rotate(inp["k"][0], k))
-        v8, sv = quantize_per_head(inp["v"][0])
-        model = (dequantize_split(q8, q8lo, sq), dequantize(k8, sk), dequantize(v8, sv))
+    q8, q8lo, sq = quantize_per_head_split(rotate(inp["q"][0], k))
+    k8, sk = quantize_per_head(rotate(inp["k"][0], k))
+    v8, sv = quantize_per_head(inp["v"][0])
+    model = (dequantize_split(q8, q8lo, sq), dequantize(k8, sk), dequantize(v8, sv))
+    got, ref, mod = [], [], []
     for h in range(2):
-        got = to_np(o[0, h][idx])
-        assert np.all(np.isfinite(got))
-        ref_o, _ = attention_forward_rows(inp["q"][0], inp["k"][0], inp["v"][0], False, scale,
-                                          0, h, rows)
-        err = rel_rms(got, ref_o)
-        print(f"[long fp8] h={h} rel-RMS vs exact {err:.4e}", flush=True)
-        if not outliers:
-            assert err <= FP8_REL_RMS, f"fp8 N={N} h={h}: rel-RMS {err:.3e}"
-        else:
-            mod_o, _ = attention_forward_rows(*model, False, scale, 0, h, rows)
-            em = rel_rms(got, mod_o)
-            print(f"[long fp8] h={h} rel-RMS vs operand-quantised model {em:.4e}", flush=True)
-            assert em <= 4e-2, f"fp8 N={N} h={h}: rel-RMS vs model {em:.3e}"
+        got.append(to_np(o[0, h][idx]))
+        assert np.all(np.isfinite(got[-1]))
+        ref.append(attention_forward_rows(inp["q"][0], inp["k"][0], inp["v"][0], False, scale,
+                                          0, h, rows)[0])
+        mod.append(attention_forward_rows(*model, False, scale, 0, h, rows)[0])
+    got, ref, mod = np.stack(got), np.stack(ref), np.stack(mod)
+    err, em, model_err = rel_rms(got, ref), rel_rms(got, mod), rel_rms(mod, ref)
+    print(f"[long fp8] outliers={outliers} rel-RMS vs exact {err:.4e}, vs model {em:.4e}, "
+          f"model vs exact {model_err:.4e}", flush=True)
+    if not outliers:
+        assert err <= FP8_REL_RMS, f"fp8 N={N}: rel-RMS {err:.3e}"
+    else:
+        assert em <= 4e-2, f"fp8 N={N}: rel-RMS vs model {em:.3e}"

@@ -35,21 +35,87 @@ def _torch():
     return torch
 
 
-def _check(t, name, dtype=None):
+def _check(t, name, dtype=None, shape=None):
+    """Validate one tensor argument before anything reaches the C ABI, which
+    sees raw pointers only: a tensor of the wrong shape, dtype or layout would
+    otherwise become an out-of-bounds device access. Devices are checked
+    afterwards, once for all arguments (`_on_device`), so every shape, dtype
+    and layout check runs (and is tested) without a GPU."""
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
+def _on_device(ref, named, ref_name="q"):
+    """`ref` on a GPU and every (tensor, name) pair on its device (None
+    entries skipped)."""
+    if ref.device.type != "cuda":
+        raise ValueError(f"{ref_name} must be on a GPU device, got {ref.device}")
+    for t, n in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{n} must be on {ref.device} (the device of {ref_name}), "
+                             f"got {t.device}")
+
+
+def _check_qkv(q, k, v, extra=()):
+    """q, k, v (and the tensors in `extra`, (tensor, name) pairs) as bf16
+    [B, H, N, d] on q's device; returns (B, H, N, d)."""
+    torch = _torch()
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    B, H, N, d = _shape(q)
+    _check(q, "q", torch.bfloat16)
+    for t, n in ((k, "k"), (v, "v"), *extra):
+        _check(t, n, torch.bfloat16, (B, H, N, d))
+    return B, H, N, d
+
+
+def _outputs(q, out, lse, want_lse=True):
+    """The caller's (or new) O [B,H,N,d] bf16 and LSE [B,H,N] fp32 buffers."""
+    torch = _torch()
+    B, H, N, d = _shape(q)
+    o = torch.empty_like(q) if out is None else out
+    _check(o, "out", torch.bfloat16, (B, H, N, d))
+    if not want_lse:
+        return o, None
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lse_t, "lse", torch.float32, (B, H, N))
+    return o, lse_t
+
+
+def _grads(q, out):
+    """The caller's (or new) dQ, dK, dV buffers, bf16 of q's shape."""
+    torch = _torch()
+    if out is None:
+        return tuple(torch.empty_like(q) for _ in range(3))
+    if len(out) != 3:
+        raise ValueError("out must be a (dq, dk, dv) triple")
+    for t, n in zip(out, ("dq", "dk", "dv")):
+        _check(t, n, torch.bfloat16, tuple(q.shape))
+    return tuple(out)
+
+
+def _workspace(ws, need, q):
+    """The caller's (or a new) uint8 workspace of at least `need` bytes."""
+    torch = _torch()
+    if ws is None:
+        return torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(ws, "workspace", torch.uint8)
+    if ws.dim() != 1 or ws.numel() < need:
+        raise ValueError(f"workspace must be a 1-D uint8 tensor of at least {need} bytes, "
+                         f"got shape {tuple(ws.shape)}")
+    return ws
+
+
 def _shape(q):
     if q.dim() != 4:
-        raise ValueError("expected [B, H, N, d] tensors")
+        raise ValueError(f"expected a [B, H, N, d] tensor, got shape {tuple(q.shape)}")
     return tuple(int(x) for x in q.shape)
 
 
@@ -67,23 +133,19 @@ def _call(status):
         raise FattnError(status)
 
 
+def _scale(scale, d):
+    return float(d ** -0.5 if scale is None else scale)
+
+
 def fwd(q, k, v, causal=False, scale=None, exp_mode="auto", out=None, lse=None):
     """Forward. Returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N])."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16)
-    B, H, N, d = _shape(q)
-    if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
-        raise ValueError("q, k, v must have the same shape")
-    scale = float(d ** -0.5 if scale is None else scale)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(o, "out", torch.bfloat16)
-    _check(lse_t, "lse", torch.float32)
-    with torch.cuda.device(q.device):
+    B, H, N, d = _check_qkv(q, k, v)
+    o, lse_t = _outputs(q, out, lse)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "out"), (lse_t, "lse")))
+    with _torch().cuda.device(q.device):
         _call(lib().fattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
-                              int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
-                              _stream(q)))
+                              int(bool(causal)), ctypes.c_float(_scale(scale, d)),
+                              _EXP[exp_mode], _stream(q)))
     return o, lse_t
 
 
@@ -101,23 +163,15 @@ def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, exp_mo
                out=None, lse=None):
     """Forward over packed variable-length sequences: rows [cu[s], cu[s+1]) of
     every head are segment s. Returns (O, LSE) like fwd."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16)
-    B, H, N, d = _shape(q)
-    if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
-        raise ValueError("q, k, v must have the same shape")
+    B, H, N, d = _check_qkv(q, k, v)
     nseq = _cu(cu_seqlens, q)
-    scale = float(d ** -0.5 if scale is None else scale)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(o, "out", torch.bfloat16)
-    _check(lse_t, "lse", torch.float32)
-    with torch.cuda.device(q.device):
+    o, lse_t = _outputs(q, out, lse)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "out"), (lse_t, "lse")))
+    with _torch().cuda.device(q.device):
         _call(lib().fattn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
                                      _ptr(cu_seqlens), nseq, int(max_seqlen), B, H, N, d,
-                                     int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
-                                     _stream(q)))
+                                     int(bool(causal)), ctypes.c_float(_scale(scale, d)),
+                                     _EXP[exp_mode], _stream(q)))
     return o, lse_t
 
 
@@ -138,39 +192,15 @@ def fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, exp_mode="aut
     """Block-sparse forward: block_mask is a uint8 tensor on the device of q,
     [nb, nb] for every head or [B*H, nb, nb], nb = ceil(N/128); entry (i, j)
     non-zero makes key block j visible to query block i. Returns (O, LSE)."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16)
-    B, H, N, d = _shape(q)
-    if _shape(k) != (B, H, N, d) or _shape(v) != (B, H, N, d):
-        raise ValueError("q, k, v must have the same shape")
+    B, H, N, d = _check_qkv(q, k, v)
     per_head = _bmask(block_mask, q)
-    scale = float(d ** -0.5 if scale is None else scale)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(o, "out", torch.bfloat16)
-    _check(lse_t, "lse", torch.float32)
-    with torch.cuda.device(q.device):
+    o, lse_t = _outputs(q, out, lse)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "out"), (lse_t, "lse")))
+    with _torch().cuda.device(q.device):
         _call(lib().fattn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
                                           _ptr(block_mask), per_head, B, H, N, d,
-                                          int(bool(causal)), ctypes.c_float(scale),
+                                          int(bool(causal)), ctypes.c_float(_scale(scale, d)),
                                           _EXP[exp_mode], _stream(q)))
-    return o, lse_t
-
-
-def fwd_fp8_attend(workspace, B, H, N, d, causal=False, scale=None, want_lse=True, out=None,
-                   device=None, exp_mode="auto"):
-    """The attention step of fwd_fp8 alone, on a workspace a previous fwd_fp8
-    call of the same (B, H, N, d) filled. Returns (O, LSE or None)."""
-    torch = _torch()
-    scale = float(d ** -0.5 if scale is None else scale)
-    dev = workspace.device if device is None else device
-    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=dev) if want_lse else None
-    with torch.cuda.device(dev):
-        _call(lib().fattn_fwd_fp8_attend(_ptr(o), _ptr(lse_t), B, H, N, d, int(bool(causal)),
-                                         ctypes.c_float(scale), _EXP[exp_mode], _ptr(workspace),
-                                         ctypes.c_size_t(workspace.numel()), _stream(o)))
     return o, lse_t
 
 
@@ -178,74 +208,59 @@ def bwd_workspace_bytes(B, H, N, d):
     return int(lib().fattn_bwd_workspace_bytes(B, H, N, d))
 
 
+def _bwd_args(q, k, v, o, lse, do, out):
+    """Validated backward operands: (B, H, N, d, (dq, dk, dv))."""
+    torch = _torch()
+    B, H, N, d = _check_qkv(q, k, v, extra=((o, "o"), (do, "do")))
+    _check(lse, "lse", torch.float32, (B, H, N))
+    return B, H, N, d, _grads(q, out)
+
+
 def bwd(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, out=None):
     """Backward from the forward's O and LSE. Returns (dQ, dK, dV) bf16."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, torch.bfloat16)
-    _check(lse, "lse", torch.float32)
-    B, H, N, d = _shape(q)
-    scale = float(d ** -0.5 if scale is None else scale)
-    if out is None:
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    else:
-        dq, dk, dv = out
-    need = bwd_workspace_bytes(B, H, N, d)
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    with torch.cuda.device(q.device):
+    B, H, N, d, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, out)
+    ws = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"), (dq, "dq"),
+                   (dk, "dk"), (dv, "dv"), (ws, "workspace")))
+    with _torch().cuda.device(q.device):
         _call(lib().fattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
                               _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
-                              ctypes.c_float(scale), _ptr(ws), ctypes.c_size_t(ws.numel()),
-                              _stream(q)))
+                              ctypes.c_float(_scale(scale, d)), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream(q)))
     return dq, dk, dv
 
 
 def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False, scale=None,
                workspace=None, out=None):
     """Backward of fwd_varlen from its O and LSE. Returns (dQ, dK, dV) bf16."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, torch.bfloat16)
-    _check(lse, "lse", torch.float32)
-    B, H, N, d = _shape(q)
+    B, H, N, d, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, out)
     nseq = _cu(cu_seqlens, q)
-    scale = float(d ** -0.5 if scale is None else scale)
-    if out is None:
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    else:
-        dq, dk, dv = out
-    need = bwd_workspace_bytes(B, H, N, d)
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    with torch.cuda.device(q.device):
+    ws = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"), (dq, "dq"),
+                   (dk, "dk"), (dv, "dv"), (ws, "workspace")))
+    with _torch().cuda.device(q.device):
         _call(lib().fattn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), nseq,
                                      int(max_seqlen), B, H, N, d, int(bool(causal)),
-                                     ctypes.c_float(scale), _ptr(ws), ctypes.c_size_t(ws.numel()),
-                                     _stream(q)))
+                                     ctypes.c_float(_scale(scale, d)), _ptr(ws),
+                                     ctypes.c_size_t(ws.numel()), _stream(q)))
     return dq, dk, dv
 
 
 def bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=False, scale=None, workspace=None,
                     out=None):
     """Backward of fwd_blocksparse from its O and LSE. Returns (dQ, dK, dV) bf16."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, n, torch.bfloat16)
-    _check(lse, "lse", torch.float32)
-    B, H, N, d = _shape(q)
+    B, H, N, d, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, out)
     per_head = _bmask(block_mask, q)
-    scale = float(d ** -0.5 if scale is None else scale)
-    if out is None:
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    else:
-        dq, dk, dv = out
-    need = bwd_workspace_bytes(B, H, N, d)
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    with torch.cuda.device(q.device):
+    ws = _workspace(workspace, bwd_workspace_bytes(B, H, N, d), q)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"), (dq, "dq"),
+                   (dk, "dk"), (dv, "dv"), (ws, "workspace")))
+    with _torch().cuda.device(q.device):
         _call(lib().fattn_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(block_mask), per_head,
-                                          B, H, N, d, int(bool(causal)), ctypes.c_float(scale),
-                                          _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(q)))
+                                          B, H, N, d, int(bool(causal)),
+                                          ctypes.c_float(_scale(scale, d)), _ptr(ws),
+                                          ctypes.c_size_t(ws.numel()), _stream(q)))
     return dq, dk, dv
 
 
@@ -277,19 +292,34 @@ def fp8_workspace_views(ws, B, H, N, d):
 def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=True,
             workspace=None, out=None, exp_mode="auto"):
     """fp8 (e4m3) forward with optional Hadamard rotation. Returns (O, LSE or None)."""
-    torch = _torch()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, n, torch.bfloat16)
-    B, H, N, d = _shape(q)
-    scale = float(d ** -0.5 if scale is None else scale)
-    o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if want_lse else None
-    need = fp8_workspace_bytes(B, H, N, d)
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    with torch.cuda.device(q.device):
+    B, H, N, d = _check_qkv(q, k, v)
+    o, lse_t = _outputs(q, out, None, want_lse)
+    ws = _workspace(workspace, fp8_workspace_bytes(B, H, N, d), q)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "out"), (ws, "workspace")))
+    with _torch().cuda.device(q.device):
         _call(lib().fattn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, H, N, d,
-                                  int(bool(causal)), ctypes.c_float(scale), _EXP[exp_mode],
-                                  int(bool(rotate)),
+                                  int(bool(causal)), ctypes.c_float(_scale(scale, d)),
+                                  _EXP[exp_mode], int(bool(rotate)),
                                   ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
                                   ctypes.c_size_t(ws.numel()), _stream(q)))
+    return o, lse_t
+
+
+def fwd_fp8_attend(workspace, B, H, N, d, causal=False, scale=None, want_lse=True, out=None,
+                   exp_mode="auto"):
+    """The attention step of fwd_fp8 alone, on a workspace a previous fwd_fp8
+    call of the same (B, H, N, d) filled (outputs on the workspace's device).
+    Returns (O, LSE or None)."""
+    torch = _torch()
+    B, H, N, d = (int(x) for x in (B, H, N, d))
+    _check(workspace, "workspace", torch.uint8)
+    ws = _workspace(workspace, fp8_workspace_bytes(B, H, N, d), workspace)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=ws.device) if out is None else out
+    _check(o, "out", torch.bfloat16, (B, H, N, d))
+    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=ws.device) if want_lse else None
+    _on_device(ws, ((o, "out"), (lse_t, "lse")), "workspace")
+    with torch.cuda.device(ws.device):
+        _call(lib().fattn_fwd_fp8_attend(_ptr(o), _ptr(lse_t), B, H, N, d, int(bool(causal)),
+                                         ctypes.c_float(_scale(scale, d)), _EXP[exp_mode],
+                                         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(o)))
     return o, lse_t

@@ -63,9 +63,9 @@ enum : int { BG_VALU = 0x002, BG_MFMA = 0x008, BG_DS_READ = 0x100, BG_DS_WRITE =
 // the row statistics it reads).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool VARLEN, bool SPARSE>
-// d = 128 needs the whole register file (504 of 512 per lane: K, V and the
-// dK, dV accumulators of its 32 keys), one wave per SIMD; d = 64 fits in 256,
-// two waves per SIMD.
+// d = 128 needs more than half the register file (434 of 512 per lane with
+// the causal mask, 333 without: K, V and the dK, dV accumulators of its 32
+// keys), so one wave per SIMD; d = 64 fits in 256, two waves per SIMD.
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,

@@ -53,7 +53,7 @@ fattn_status check_ptr(const void* p, const char* name) {
 std::mutex g_dev_mu;
 int g_dev_ok[64];  // 0 unknown, 1 gfx950, 2 other
 
-fattn_status check_device() {
+fattn_status check_device(int* dev_out = nullptr) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(FATTN_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -67,6 +67,7 @@ fattn_status check_device() {
     if (g_dev_ok[dev] == 2) return fail(FATTN_EDEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
   }
   if (g_dev_ok[dev] != 1) return fail(FATTN_EDEVICE, "device %d is not gfx950", dev);
+  if (dev_out) *dev_out = dev;
   return FATTN_OK;
 }
 

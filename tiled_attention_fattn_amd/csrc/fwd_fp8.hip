@@ -7,8 +7,9 @@
 // applied row by row with a fast Walsh–Hadamard transform in registers.
 //
 // Launches (one stream):
-//   1. fp8_amax   — amax of |Q·R|, |K·R| and |V| over each chunk of 256 rows
-//                   of each (b,h), one plain store per block (no atomics).
+//   1. fp8_amax   — amax of |Q·R|, |K·R| and |V| over each chunk of
+//                   kFp8AmaxRows (128) rows of each (b,h), one plain store
+//                   per block (no atomics).
 //   2. fp8_quant_qk — recompute Q·R, K·R; code = e4m3(t), t = x·448/amax
 //                   (one correctly rounded division), round to nearest even;
 //                   for Q' also the residual code e4m3(16·(t − decode(code)));
