@@ -116,6 +116,29 @@ fattn_status fattn_bwd(const void* q, const void* k, const void* v,
                        size_t workspace_bytes, void* stream);
 
 /*
+ * fattn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: work recorded under graph capture, tight serving loops,
+ * harnesses that forbid allocation. The row statistics live in a
+ * library-owned static device buffer of FATTN_NOALLOC_WORKSPACE_BYTES bytes
+ * per GPU (held from the first use on that GPU until the process ends, its
+ * device address looked up on the first call on each device); the call
+ * itself allocates nothing. Inputs, outputs and results as fattn_bwd.
+ * Limits: fattn_bwd_workspace_bytes(B,H,N,d) must not exceed
+ * FATTN_NOALLOC_WORKSPACE_BYTES (B·H·ceil(N/64)·64 <= 2^21 rows, e.g.
+ * B·H = 64 at N = 32768), else FATTN_EWORKSPACE and nothing is launched.
+ * Every call on one GPU shares that GPU's buffer: calls that overlap on one
+ * GPU (other streams, other threads) race and give wrong gradients; the
+ * buffer keeps the last call's contents (each call overwrites all it reads).
+ * Errors otherwise as fattn_bwd; EHIP if the buffer's address cannot be
+ * looked up.
+ */
+#define FATTN_NOALLOC_WORKSPACE_BYTES ((size_t)16 << 20)
+fattn_status fattn_bwd_noalloc(const void* q, const void* k, const void* v,
+                               const void* o, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, int B, int H, int N,
+                               int d, int causal, float scale, void* stream);
+
+/*
  * Packed variable-length sequences (varlen), bf16 forward and backward.
  *   cu_seqlens  device int32 [nseq + 1], non-decreasing offsets into the N rows
  *               of every head: rows [cu_seqlens[s], cu_seqlens[s+1]) form

@@ -204,3 +204,27 @@ def test_bwd_blocksparse_checks():
     assert call(P, need, per_head=-1) == EINVAL
     assert call(P, need, dk=MIS) == EINVAL
     assert call(P, lib.fattn_bwd_workspace_bytes(B, H, 40000, d), N=40000) == ENOTSUP
+
+
+def test_bwd_noalloc_checks():
+    # Rejections only (a call that passes every check would launch on fake
+    # pointers): sizes past the static workspace, and the fattn_bwd checks.
+    lib = fa.lib()
+    cap = 16 << 20
+    assert lib.fattn_bwd_workspace_bytes(1, 32, 65536, 64) == cap   # exactly at the limit
+
+    def call(**kw):
+        a = dict(q=P, dv=P, B=1, H=2, N=100, d=128, causal=1, scale=0.1)
+        a.update(kw)
+        return lib.fattn_bwd_noalloc(a["q"], P, P, P, P, P, P, P, a["dv"], a["B"], a["H"],
+                                     a["N"], a["d"], a["causal"], ctypes.c_float(a["scale"]), NUL)
+    assert call(B=1, H=32, N=65537, d=64) == EWORKSPACE     # one 64-row block past the limit
+    assert b"static workspace" in lib.fattn_last_error()
+    assert call(B=16, H=16, N=32768, d=64) == EWORKSPACE
+    assert call(q=NUL) == EINVAL
+    assert call(dv=MIS) == EINVAL
+    assert call(d=96) == ENOTSUP
+    assert call(N=0) == EINVAL
+    assert call(causal=2) == EINVAL
+    assert call(scale=0.0) == EINVAL
+    assert call(B=4096, H=64, N=8192, d=128) == ENOTSUP

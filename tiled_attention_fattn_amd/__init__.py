@@ -21,7 +21,7 @@ import os
 
 from ._lib import FattnError, lib, lib_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "bwd_blocksparse", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_WORKSPACE_BYTES", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "bwd_blocksparse", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
            "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
            "EXP_AUTO", "EXP_HW", "EXP_POLY", "EXP_SPLIT"]
 
@@ -227,6 +227,25 @@ def bwd(q, k, v, o, lse, do, causal=False, scale=None, workspace=None, out=None)
                               _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)),
                               ctypes.c_float(_scale(scale, d)), _ptr(ws),
                               ctypes.c_size_t(ws.numel()), _stream(q)))
+    return dq, dk, dv
+
+
+NOALLOC_WORKSPACE_BYTES = 16 << 20  # FATTN_NOALLOC_WORKSPACE_BYTES
+
+
+def bwd_noalloc(q, k, v, o, lse, do, causal=False, scale=None, out=None):
+    """Backward like bwd, through fattn_bwd_noalloc: the row statistics use the
+    library's static per-GPU buffer (no workspace argument, nothing allocated
+    by the library; with `out` given, nothing allocated at all). Calls that
+    overlap on one GPU race. Returns (dQ, dK, dV) bf16."""
+    B, H, N, d, (dq, dk, dv) = _bwd_args(q, k, v, o, lse, do, out)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do"), (dq, "dq"),
+                   (dk, "dk"), (dv, "dv")))
+    with _torch().cuda.device(q.device):
+        _call(lib().fattn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                                      int(bool(causal)), ctypes.c_float(_scale(scale, d)),
+                                      _stream(q)))
     return dq, dk, dv
 
 

@@ -19,6 +19,7 @@ PROTOTYPES = {
     "fattn_bwd_varlen": (c_int, [c_void_p] * 10 + [c_int] * 7
                          + [c_float, c_void_p, c_size_t, c_void_p]),
     "fattn_bwd": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float, c_void_p, c_size_t, c_void_p]),
+    "fattn_bwd_noalloc": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float, c_void_p]),
     "fattn_fwd_fp8_workspace_bytes": (c_size_t, [c_int] * 4),
     "fattn_fwd_fp8_workspace_layout": (c_int, [c_int] * 4 + [ctypes.POINTER(c_size_t)] * 5),
     "fattn_fwd_fp8": (c_int, [c_void_p] * 5 + [c_int] * 5

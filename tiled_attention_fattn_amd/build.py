@@ -25,7 +25,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfattn.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["fattn_host.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "fwd_fp8.hip"]
+SOURCES = ["fattn_host.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "fwd_fp8.hip", "static_ws.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

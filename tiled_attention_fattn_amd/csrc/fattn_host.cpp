@@ -284,6 +284,42 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v, 
                     "fattn_bwd_blocksparse launch");
 }
 
+fattn_status fattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int B, int H, int N, int d, int causal, float scale,
+                               void* stream) {
+  static_assert(FATTN_NOALLOC_WORKSPACE_BYTES == fattn::kStaticWorkspaceBytes,
+                "the header states the static workspace's capacity");
+  FATTN_TRY(check_ptr(q, "q"));
+  FATTN_TRY(check_ptr(k, "k"));
+  FATTN_TRY(check_ptr(v, "v"));
+  FATTN_TRY(check_ptr(o, "o"));
+  FATTN_TRY(check_ptr(lse, "lse"));
+  FATTN_TRY(check_ptr(dout, "dout"));
+  FATTN_TRY(check_ptr(dq, "dq"));
+  FATTN_TRY(check_ptr(dk, "dk"));
+  FATTN_TRY(check_ptr(dv, "dv"));
+  FATTN_TRY(check_shape(B, H, N, d, causal, scale));
+  const size_t need = fattn_bwd_workspace_bytes(B, H, N, d);
+  if (need > fattn::kStaticWorkspaceBytes)
+    return fail(FATTN_EWORKSPACE,
+                "B=%d H=%d N=%d needs %zu bytes of workspace; the library's static workspace "
+                "holds %zu (use fattn_bwd with a caller workspace)",
+                B, H, N, need, fattn::kStaticWorkspaceBytes);
+  int dev = 0;
+  FATTN_TRY(check_device(&dev));
+  void* ws = nullptr;
+  const hipError_t e = fattn::static_workspace(dev, &ws);
+  if (e != hipSuccess)
+    return fail(FATTN_EHIP, "static workspace of device %d: %s", dev, hipGetErrorString(e));
+  const size_t n = (size_t)B * H * round_up((size_t)N, fattn::kBwdRowPad);
+  float* dvec = (float*)ws;
+  float* lse2 = (float*)((char*)dvec + round_up(n * sizeof(float), 256));
+  return hip_status(fattn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, dvec, lse2, B, H, N,
+                                           d, causal != 0, scale, (hipStream_t)stream),
+                    "fattn_bwd_noalloc launch");
+}
+
 size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
   return fp8_layout(B, H, N, d).total;

@@ -63,6 +63,12 @@ hipError_t launch_fwd_fp8_attend(void* o, float* lse, const uint8_t* q8, const u
                                  int H, int N, int d, bool causal, float scale, int exp_mode,
                                  hipStream_t stream);
 
+// Library-owned backward workspace (static_ws.hip): its capacity, and its
+// device address on `device`, which must be the current device (looked up on
+// the first call for that device, then cached).
+constexpr size_t kStaticWorkspaceBytes = (size_t)16 << 20;
+hipError_t static_workspace(int device, void** ptr);
+
 constexpr int kFp8Npad = 64;
 constexpr int kFp8AmaxRows = 128;  // rows per amax chunk (measured: 128 beats 64 and 256)
 
