@@ -226,6 +226,14 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  * unnormalised probability P̃ is at most 2; P is quantised to e4m3 as
  * P̃·2^7 ≤ 256.
  * Additionally requires B·H ≤ 65535 (ENOTSUP otherwise).
+ * Validated range (GPU parity tests against float64 attention): d ∈ {64,
+ * 128}, N from 1 to 32768, causal and not. Error against exact attention,
+ * relative RMS of O: within 6e-2 for N(0,1) inputs up to N = 32768 and for
+ * inputs with 0.1% of the Q and K entries scaled by 20 at N = 4096 (every
+ * element of B=4, H=16). With such outliers the e4m3 operands alone already
+ * cost about 5.4% at N = 32768 (the quantised operands with exact P against
+ * exact attention), so there the output is held to 4e-2 of that operand
+ * model instead. Longer sequences run but are not validated.
  */
 size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d);
 fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d,

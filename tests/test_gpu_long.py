@@ -3,9 +3,10 @@
 The long-sequence points of the throughput sweep: the forward at N = 32768
 (and a ragged N = 32731) on sampled rows against the float64 oracle, the
 causal backward at N = 16384 against the full float64 gradients of one head,
-and the fp8 forward at N = 32768 on sampled rows against exact attention
-(without outliers) or against the operand-quantised model (with them).
-Inputs are the seeded N(0,1) draws rounded to bf16 (seed ids 60 and up).
+and the fp8 forward at N = 32768 (non-causal and causal) on sampled rows
+against exact attention (without outliers) or against the operand-quantised
+model (with them). Inputs are the seeded N(0,1) draws rounded to bf16 (seed
+ids 60 and up).
 """
 import numpy as np
 import pytest
@@ -63,8 +64,8 @@ def test_bwd_long_sequence_one_head(k, d):
         assert_bf16_close(to_np(got), r, f"{name} N={N} d={d}")
 
 
-@pytest.mark.parametrize("outliers", [False, True])
-def test_fp8_long_sequence_sampled(outliers):
+@pytest.mark.parametrize("outliers,causal", [(False, False), (True, False), (False, True)])
+def test_fp8_long_sequence_sampled(outliers, causal):
     # N = 32768 on sampled rows, reported against exact attention and against
     # the oracle's operand-quantised model on the same rows. Without outliers
     # the output is held to the fp8 bound against exact attention. With the
@@ -76,14 +77,15 @@ def test_fp8_long_sequence_sampled(outliers):
     from oracle.fp8_model import (dequantize, dequantize_split, quantize_per_head,
                                   quantize_per_head_split)
     from oracle.hadamard import rotate
-    N, d, k = 32768, 128, 66 + int(outliers)
+    N, d, k = 32768, 128, 66 + int(outliers) + 2 * int(causal)
     shape = (1, 2, N, d)
     kw = dict(outlier_frac=0.001, outlier_factor=20.0) if outliers else {}
     inp = gen_workload(k, shape=shape, names=("q", "k", "v"), **kw)
     q, kk, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
     scale = d ** -0.5
-    print(f"[long fp8] seed={k} shape={shape} outliers={outliers}", flush=True)
-    o, _ = fa.fwd_fp8(q, kk, v, scale=scale, rotate=True, seed=k, want_lse=False)
+    print(f"[long fp8] seed={k} shape={shape} outliers={outliers} causal={causal}", flush=True)
+    o, _ = fa.fwd_fp8(q, kk, v, causal=causal, scale=scale, rotate=True, seed=k,
+                      want_lse=False)
     torch.cuda.synchronize()
     rows = _rows(N, k)
     idx = torch.as_tensor(rows, device=o.device)
@@ -95,12 +97,12 @@ def test_fp8_long_sequence_sampled(outliers):
     for h in range(2):
         got.append(to_np(o[0, h][idx]))
         assert np.all(np.isfinite(got[-1]))
-        ref.append(attention_forward_rows(inp["q"][0], inp["k"][0], inp["v"][0], False, scale,
-                                          0, h, rows)[0])
-        mod.append(attention_forward_rows(*model, False, scale, 0, h, rows)[0])
+        ref.append(attention_forward_rows(inp["q"][0], inp["k"][0], inp["v"][0], causal,
+                                          scale, 0, h, rows)[0])
+        mod.append(attention_forward_rows(*model, causal, scale, 0, h, rows)[0])
     got, ref, mod = np.stack(got), np.stack(ref), np.stack(mod)
     err, em, model_err = rel_rms(got, ref), rel_rms(got, mod), rel_rms(mod, ref)
-    print(f"[long fp8] outliers={outliers} rel-RMS vs exact {err:.4e}, vs model {em:.4e}, "
+    print(f"[long fp8] outliers={outliers} causal={causal} rel-RMS vs exact {err:.4e}, vs model {em:.4e}, "
           f"model vs exact {model_err:.4e}", flush=True)
     if not outliers:
         assert err <= FP8_REL_RMS, f"fp8 N={N}: rel-RMS {err:.3e}"
