@@ -119,6 +119,9 @@ __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, i
 }
 
 // grid (row chunks, BH, 3 tensors): block max of |x| over kFp8AmaxRows rows.
+// The tensors are taken in the order V, K, Q (blockIdx.z = 0, 1, 2), so that
+// Q and K, which the quantisation kernel reads next, are the most recently
+// read lines in the last-level cache.
 template <int D>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ Q,
                                                       const bf16* __restrict__ K,
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ 
   constexpr int LPR = D / kEpl, RPB = 256 / LPR;
   __shared__ float sgn[D];
   __shared__ float wmax[4];
-  const int t = blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
+  const int t = 2 - (int)blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;  // tensor: 0 Q, 1 K, 2 V
   const bool rot = rotate && t < 2;
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
   __syncthreads();
