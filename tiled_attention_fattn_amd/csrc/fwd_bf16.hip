@@ -395,6 +395,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     const char* kt = k_lds + (PAR ^ 1) * TILE;
     const char* vt = v_lds + PAR * TILE;
+    // An empty asm statement on the exponent offset at every call site, so
+    // the exp2 arguments of this iteration are formed inside it: otherwise
+    // the compiler forms them once above the branch between the last two
+    // iterations and spills them, and each spill reload's wait on the
+    // vector-memory counter also waits for the tile loads issued above.
+    asm volatile("" : "+v"(st.m_c));
     i32x4 pk[4];
     float la = 0.0f, lb = 0.0f;
     f32x16 ns[2];
