@@ -29,8 +29,9 @@ brute       pure-Python triple loops (no BLAS) for tiny shapes.
 hadamard    Sylvester Hadamard matrix, fast Walsh–Hadamard transform,
             SplitMix64 sign vector, the random-sign rotation.
 e4m3        OCP FP8 E4M3FN decode/encode (round-to-nearest-even, saturating).
-fp8_model   diagnostic model of the fp8 forward: rotate, per-head amax scale,
-            quantise, dequantise, then the float64 attention.
+fp8_model   diagnostic model of the fp8 forward: rotate, amax scales (per row
+            for Q', per head for K' and V), quantise, dequantise, then the
+            float64 attention.
 
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against closed forms, invariants, brute force or library routines.
@@ -40,11 +41,11 @@ from .attention import (attention_forward, attention_backward,
                         attention_forward_rows, softmax_rows)
 from .hadamard import (sylvester, fwht, splitmix64, rotation_signs, rotate)
 from .e4m3 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_values)
-from .fp8_model import (quantize_per_head, fp8_attention_model)
+from .fp8_model import (quantize_per_head, quantize_per_row_split, fp8_attention_model)
 
 __all__ = [
     "attention_forward", "attention_backward", "attention_forward_rows",
     "softmax_rows", "sylvester", "fwht", "splitmix64", "rotation_signs",
     "rotate", "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_values",
-    "quantize_per_head", "fp8_attention_model",
+    "quantize_per_head", "quantize_per_row_split", "fp8_attention_model",
 ]

@@ -6,11 +6,16 @@ The page fixes neither the scaling granularity nor which other operands are
 fp8. Readings used here:
 
 * Q' = Q·R and K' = K·R (``oracle.hadamard.rotate``); V is not rotated.
-* Each of Q', K', V is quantised with one scale per (batch, head):
+* K' and V are quantised with one scale per (batch, head):
   scale = amax/448 (scale 1 for an all-zero head) and
   code = E4M3FN(x·448/amax), the exact ratio rounded once to nearest-even
   (saturating). x·448/amax is used rather than x/scale because a rounded scale
   would double-round at the exact e4m3 midpoints that bf16 inputs do hit.
+* Q' is quantised the same way with one scale per row (per query): its amax
+  is the row's own. A query row only ever meets the keys through its own
+  scores, so a per-row scale is as exact as a per-head one, and it lets the
+  attention step quantise the rows it owns without a pass over the whole
+  head first.
 * Q' additionally keeps its quantisation residual as a second e4m3 tensor with
   scale/16: t = x·448/amax, r = t − decode(code), code_lo = E4M3FN(16·r), so
   Q' ≈ scale·(decode(code) + decode(code_lo)/16). (With a single e4m3 term
@@ -65,6 +70,29 @@ def quantize_per_head_split(x):
     return codes, resid, scales
 
 
+def quantize_per_row_split(x):
+    """Two-term quantisation with one scale per row of x [B, H, N, d]:
+    (codes, residual codes, scales [B, H, N]).
+
+    x ≈ scale·(decode(codes) + decode(residual_codes)/16) per (b, h, row); a
+    row of zeros gets scale 1 and zero codes.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.max(np.abs(x), axis=3)
+    scales = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    a = amax[..., None]
+    t = np.where(a > 0, (x * E4M3_MAX) / np.where(a > 0, a, 1.0), x)
+    codes = e4m3_encode(t)
+    resid = e4m3_encode(RESIDUAL_SHIFT * (t - e4m3_decode(codes)))
+    return codes, resid, scales
+
+
+def dequantize_split_rows(codes, resid, scales):
+    """scale·(decode(codes) + decode(resid)/16) per (b, h, row)."""
+    return (e4m3_decode(codes) + e4m3_decode(resid) / RESIDUAL_SHIFT) * \
+        np.asarray(scales)[..., None]
+
+
 def dequantize(codes, scales):
     """decode(codes) · scale per (b, h)."""
     return e4m3_decode(codes) * np.asarray(scales)[:, :, None, None]
@@ -77,7 +105,8 @@ def dequantize_split(codes, resid, scales):
 
 
 def fp8_attention_model(q, k, v, causal, scale, rotate, seed):
-    """Rotate (optionally), quantise Q' (two terms), K', V per head, dequantise, attend.
+    """Rotate (optionally), quantise Q' (two terms, per row), K' and V (per
+    head), dequantise, attend.
 
     Returns a dict with the float64 output O and LSE of the model and the
     intermediate codes / scales for comparison with the quantisation step.
@@ -87,10 +116,10 @@ def fp8_attention_model(q, k, v, causal, scale, rotate, seed):
     v = np.asarray(v, dtype=np.float64)
     qr = _rotate(q, seed) if rotate else q
     kr = _rotate(k, seed) if rotate else k
-    q8, q8lo, sq = quantize_per_head_split(qr)
+    q8, q8lo, sq = quantize_per_row_split(qr)
     k8, sk = quantize_per_head(kr)
     v8, sv = quantize_per_head(v)
-    o, lse = attention_forward(dequantize_split(q8, q8lo, sq), dequantize(k8, sk),
+    o, lse = attention_forward(dequantize_split_rows(q8, q8lo, sq), dequantize(k8, sk),
                                dequantize(v8, sv), causal, scale)
     return {"o": o, "lse": lse, "q8": q8, "q8lo": q8lo, "k8": k8, "v8": v8,
             "sq": sq, "sk": sk, "sv": sv, "q_rot": qr, "k_rot": kr}

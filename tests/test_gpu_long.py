@@ -74,8 +74,8 @@ def test_fp8_long_sequence_sampled(outliers, causal):
     # oracle test pins that), so the kernel is held to the model at 4e-2 and
     # its error against exact attention is reported.
     import tiled_attention_fattn_amd as fa
-    from oracle.fp8_model import (dequantize, dequantize_split, quantize_per_head,
-                                  quantize_per_head_split)
+    from oracle.fp8_model import (dequantize, dequantize_split_rows, quantize_per_head,
+                                  quantize_per_row_split)
     from oracle.hadamard import rotate
     N, d, k = 32768, 128, 66 + int(outliers) + 2 * int(causal)
     shape = (1, 2, N, d)
@@ -89,10 +89,10 @@ def test_fp8_long_sequence_sampled(outliers, causal):
     torch.cuda.synchronize()
     rows = _rows(N, k)
     idx = torch.as_tensor(rows, device=o.device)
-    q8, q8lo, sq = quantize_per_head_split(rotate(inp["q"][0], k))
+    q8, q8lo, sq = quantize_per_row_split(rotate(inp["q"][0], k))
     k8, sk = quantize_per_head(rotate(inp["k"][0], k))
     v8, sv = quantize_per_head(inp["v"][0])
-    model = (dequantize_split(q8, q8lo, sq), dequantize(k8, sk), dequantize(v8, sv))
+    model = (dequantize_split_rows(q8, q8lo, sq), dequantize(k8, sk), dequantize(v8, sv))
     got, ref, mod = [], [], []
     for h in range(2):
         got.append(to_np(o[0, h][idx]))

@@ -89,8 +89,8 @@ def test_fp8_model_without_rotation_is_attention_on_dequantised():
     rng = np.random.default_rng(2)
     q, k, v = (rng.standard_normal((1, 2, 24, 16)) for _ in range(3))
     m = fp8_attention_model(q, k, v, False, 0.25, rotate=False, seed=0)
-    from oracle.fp8_model import dequantize_split
-    o, _ = attention_forward(dequantize_split(m["q8"], m["q8lo"], m["sq"]),
+    from oracle.fp8_model import dequantize_split_rows
+    o, _ = attention_forward(dequantize_split_rows(m["q8"], m["q8lo"], m["sq"]),
                              dequantize(m["k8"], m["sk"]), dequantize(m["v8"], m["sv"]),
                              False, 0.25)
     np.testing.assert_array_equal(m["o"], o)
@@ -142,3 +142,51 @@ def test_split_quantisation_residual():
     # the two-term value is closer than the one-term value
     one = dequantize(hi, scales)
     assert np.linalg.norm(xr - x) < np.linalg.norm(one - x) / 8
+
+
+def test_per_row_split_quantisation():
+    # One scale per row: each row's amax maps to the largest code, a zero row
+    # gets scale 1 and zero codes, and the row quantises exactly as a head of
+    # its own would (the per-head quantiser applied to that row alone).
+    from oracle.fp8_model import (dequantize_split_rows, quantize_per_head_split,
+                                  quantize_per_row_split)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 2, 16, 32))
+    x[0, 1, 3, 5] = 40.0
+    x[1, 0, 7] = 0.0
+    hi, lo, scales = quantize_per_row_split(x)
+    assert scales.shape == (2, 2, 16)
+    assert scales[1, 0, 7] == 1.0 and np.all(hi[1, 0, 7] == 0) and np.all(lo[1, 0, 7] == 0)
+    for b in range(2):
+        for h in range(2):
+            for r in range(16):
+                if b == 1 and h == 0 and r == 7:
+                    continue
+                assert hi[b, h, r, np.argmax(np.abs(x[b, h, r]))] in (0x7E, 0xFE)
+                h1, l1, s1 = quantize_per_head_split(x[b, h, r][None, None, None, :])
+                np.testing.assert_array_equal(hi[b, h, r], h1[0, 0, 0])
+                np.testing.assert_array_equal(lo[b, h, r], l1[0, 0, 0])
+                assert scales[b, h, r] == s1[0, 0]
+    # the outlier only coarsens its own row
+    assert scales[0, 1, 3] > 4 * np.max(np.delete(scales[0, 1], 3))
+    xr = dequantize_split_rows(hi, lo, scales)
+    t = x / scales[..., None]
+    big = np.abs(t) >= 1.0
+    rel = np.abs(xr - x)[big] / np.abs(x)[big]
+    assert rel.max() <= 2.0 ** -7
+
+
+def test_per_row_scale_is_invariant_under_row_scaling():
+    # Multiplying a row by a power of two leaves its codes unchanged and
+    # multiplies only its scale.
+    from oracle.fp8_model import quantize_per_row_split
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((1, 1, 8, 16))
+    y = x.copy()
+    y[0, 0, 2] *= 2.0 ** 5
+    a = quantize_per_row_split(x)
+    b = quantize_per_row_split(y)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    assert b[2][0, 0, 2] == a[2][0, 0, 2] * 32
+    np.testing.assert_array_equal(np.delete(a[2][0, 0], 2), np.delete(b[2][0, 0], 2))

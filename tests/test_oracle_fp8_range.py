@@ -1,6 +1,6 @@
 """How much of the fp8 error budget the operand quantisation alone uses: the
-oracle's e4m3 model (rotation, per-head scales, two-term Q', single-term K'
-and V, exact P) against exact attention, on the fp8 workload's input recipe
+oracle's e4m3 model (rotation, two-term Q' with one scale per row, K' and V
+with one scale per head, exact P) against exact attention, on the fp8 workload's input recipe
 (0.1% of Q and K entries x20) at N = 4096 and N = 32768.
 
 FlashAttention-3 page, innovation 3: the rotation spreads the outliers before
@@ -20,8 +20,9 @@ import numpy as np
 import pytest
 
 from oracle.attention import attention_forward_rows
-from oracle.fp8_model import (dequantize, dequantize_split, quantize_per_head,
-                              quantize_per_head_split)
+from oracle.fp8_model import (dequantize, dequantize_split, dequantize_split_rows,
+                              quantize_per_head, quantize_per_head_split,
+                              quantize_per_row_split)
 from oracle.hadamard import rotate
 from tiled_attention_fattn_amd.inputs import gen_workload
 
@@ -30,7 +31,7 @@ def _model_error(k, N, heads, rows, two_term_k=False):
     x = gen_workload(k, shape=(1, heads, N, 128), outlier_frac=0.001, outlier_factor=20.0)
     q, kk, v = x["q"][0], x["k"][0], x["v"][0]
     scale = 128 ** -0.5
-    q2 = dequantize_split(*quantize_per_head_split(rotate(q, k)))
+    q2 = dequantize_split_rows(*quantize_per_row_split(rotate(q, k)))
     kq = (dequantize_split(*quantize_per_head_split(rotate(kk, k))) if two_term_k
           else dequantize(*quantize_per_head(rotate(kk, k))))
     vq = dequantize(*quantize_per_head(v))
