@@ -137,8 +137,9 @@ def setup_part(part, torch, fa, exp_mode="auto"):
 
     def run(mode="full", em=exp_mode):
         if mode == "attend":  # the attention step alone on the operands of the last full call
-            return fa.fwd_fp8_attend(ws, B, H, N, d, causal=w["causal"], scale=scale,
-                                     want_lse=False, out=o2, exp_mode=em)
+            return fa.fwd_fp8_attend(t["q"], ws, causal=w["causal"], scale=scale,
+                                     rotate=w["rotate"], seed=k, want_lse=False, out=o2,
+                                     exp_mode=em)
         if mode == "outputs":  # O with and without the rotation (outside the timed region)
             outs = {}
             for rot in (True, False):
@@ -300,8 +301,8 @@ def sweep(args):
             ws8 = torch.empty(fa.fp8_workspace_bytes(1, H, N, d), dtype=torch.uint8, device="cuda")
             fa.fwd_fp8(q, k, v, scale=scale, rotate=True, seed=N, want_lse=False, workspace=ws8,
                        out=o)
-            ms = timed(lambda: fa.fwd_fp8_attend(ws8, 1, H, N, d, scale=scale, want_lse=False,
-                                                 out=o))
+            ms = timed(lambda: fa.fwd_fp8_attend(q, ws8, scale=scale, rotate=True, seed=N,
+                                                 want_lse=False, out=o))
             tf = flops_fwd(1, H, N, d, False) / (ms * 1e-3) / 1e12
             points.append({"part": "fp8_attend", "causal": False, "B": 1, "H": H, "N": N, "d": d,
                            "ms": round(ms, 4), "tflops": round(tf, 1),

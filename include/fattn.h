@@ -208,19 +208,21 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  *               i-th SplitMix64 output for state `seed`; 0: no rotation.
  *   workspace   at least fattn_fwd_fp8_workspace_bytes(B,H,N,d) bytes,
  *               256-byte aligned. Layout (see fattn_fwd_fp8_workspace_layout):
- *               e4m3 Q8 [B,H,N,d], e4m3 Q8lo [B,H,N,d] (residual of Q',
- *               see below), e4m3 K8 [B,H,N,d], e4m3 V8 stored
- *               transposed per head as [B,H,d,Npad] (Npad = N rounded up to
- *               64, zero padded; inside each block of 64 keys, position
- *               p = 32a + s holds key 32(s/16) + 8((s%16)/4) + 4a + s%4,
- *               the order in which the kernel's P operand holds keys),
- *               then fp32 scales [3][B·H]
- *               (Q', K', V per head: amax/448, or 1 for an all-zero head),
- *               then an fp32 [3][B·H][⌈N/128⌉] scratch of per-chunk amax.
- * Each operand is quantised per (b,h): code = e4m3(x·448/amax), the exact
- * ratio rounded to nearest even. Q' keeps a second e4m3 term for its
- * quantisation residual, Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that
+ *               e4m3 K8 [B,H,N,d], e4m3 V8 stored transposed per head as
+ *               [B,H,d,Npad] (Npad = N rounded up to 64, zero padded; inside
+ *               each block of 64 keys, position p = 32a + s holds key
+ *               32(s/16) + 8((s%16)/4) + 4a + s%4, the order in which the
+ *               kernel's P operand holds keys), then fp32 scales [2][B·H]
+ *               (K', V per head: amax/448, or 1 for an all-zero head), then
+ *               an fp32 [2][B·H][⌈N/128⌉] scratch of per-chunk amax.
+ * Each operand is quantised as code = e4m3(x·448/amax), the exact ratio
+ * rounded to nearest even: K' and V with one amax per (b,h), Q' with one
+ * amax per row (each query row meets the keys only through its own scores).
+ * Q' keeps a second e4m3 term for its quantisation residual,
+ * Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that
  * Q' ≈ scale_q·(Q8 + Q8lo/16); the scores use both terms (two fp8 MFMAs).
+ * Q' is rotated and quantised inside the attention kernel (each workgroup
+ * its own rows) and never stored.
  * The softmax keeps its exponent offset within a factor 2 of the running row
  * max (rescaling the partial output when the max grows by more), so every
  * unnormalised probability P̃ is at most 2; P is quantised to e4m3 as
@@ -237,7 +239,6 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  */
 size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d);
 fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d,
-                                            size_t* off_q8, size_t* off_q8lo,
                                             size_t* off_k8, size_t* off_v8t,
                                             size_t* off_scales);
 fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
@@ -249,19 +250,20 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
  * The attention step of fattn_fwd_fp8 alone (FlashAttention-3 page,
  * "Nuevas capacidades…" (FP8): the fp8 matrix products with the softmax
  * between them), on a workspace that a previous fattn_fwd_fp8 call with the
- * same B, H, N, d filled: it reads the e4m3 operands Q8, Q8lo, K8, V8ᵀ and
- * the scales from the workspace and writes o (and lse if non-NULL) exactly as
- * that call did for the same causal, scale and exp_mode. The workspace is
- * only read.
- * For re-running attention on operands already quantised and rotated, and
- * for timing the attention step apart from the quantisation.
+ * same B, H, N, d, rotate and seed filled: it reads the e4m3 operands K8,
+ * V8ᵀ and their scales from the workspace, rotates and quantises q itself
+ * (bf16 [B,H,N,d], as fattn_fwd_fp8 does) and writes o (and lse if
+ * non-NULL) exactly as that call did for the same q, causal, scale and
+ * exp_mode. The workspace is only read.
+ * For re-running attention on keys and values already quantised, and for
+ * timing the attention step apart from the K/V quantisation.
  * Errors as fattn_fwd_fp8 (a workspace never filled gives meaningless o,
  * not an error).
  */
-fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int d,
-                                  int causal, float scale, int exp_mode,
-                                  const void* workspace, size_t workspace_bytes,
-                                  void* stream);
+fattn_status fattn_fwd_fp8_attend(const void* q, void* o, float* lse, int B, int H, int N,
+                                  int d, int causal, float scale, int exp_mode, int rotate,
+                                  uint64_t seed, const void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* fattn_strerror(int status);

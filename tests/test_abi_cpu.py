@@ -83,14 +83,15 @@ def test_fp8_workspace_layout_and_checks():
     lib = fa.lib()
     B, H, N, d = 2, 3, 100, 128
     need = lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
-    offs = [ctypes.c_size_t() for _ in range(5)]
+    offs = [ctypes.c_size_t() for _ in range(3)]
     assert lib.fattn_fwd_fp8_workspace_layout(B, H, N, d, *[ctypes.byref(x) for x in offs]) == OK
-    oq, oql, ok, ov, osc = (x.value for x in offs)
+    ok, ov, osc = (x.value for x in offs)
     npad = 128
     n = B * H * N * d
-    assert oq == 0 and oql >= n and ok >= oql + n and ov >= ok + n
-    assert osc >= ov + B * H * d * npad and need >= osc + 2 * 12 * B * H
-    assert all(x % 256 == 0 for x in (oq, oql, ok, ov, osc))
+    assert ok == 0 and ov >= ok + n
+    # scales [2][B·H], then the per-chunk amax scratch [2][B·H][⌈N/128⌉]
+    assert osc >= ov + B * H * d * npad and need >= osc + 8 * B * H + 8 * B * H * 1
+    assert all(x % 256 == 0 for x in (ok, ov, osc))
 
     def call(ws, nbytes, **kw):
         a = dict(rotate=1, lse=P, d=d, exp=0)
@@ -112,12 +113,15 @@ def test_fp8_attend_checks():
     need = lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
 
     def call(ws, nbytes, **kw):
-        a = dict(o=P, lse=NUL, B=B, H=H, N=N, d=d, causal=0, scale=0.1, exp=0)
+        a = dict(q=P, o=P, lse=NUL, B=B, H=H, N=N, d=d, causal=0, scale=0.1, exp=0, rotate=1)
         a.update(kw)
-        return lib.fattn_fwd_fp8_attend(a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
-                                        a["causal"], ctypes.c_float(a["scale"]), a["exp"], ws,
-                                        nbytes, NUL)
+        return lib.fattn_fwd_fp8_attend(a["q"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                        a["causal"], ctypes.c_float(a["scale"]), a["exp"],
+                                        a["rotate"], ctypes.c_uint64(7), ws, nbytes, NUL)
     assert call(NUL, need) == EWORKSPACE
+    assert call(P, need, q=NUL) == EINVAL
+    assert call(P, need, q=MIS) == EINVAL
+    assert call(P, need, rotate=2) == EINVAL
     assert call(P, need - 1) == EWORKSPACE
     assert call(MIS, need) in (EINVAL, EWORKSPACE)
     assert call(P, need, o=NUL) == EINVAL

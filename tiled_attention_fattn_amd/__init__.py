@@ -288,24 +288,23 @@ def fp8_workspace_bytes(B, H, N, d):
 
 
 def fp8_workspace_views(ws, B, H, N, d):
-    """Views (q8, q8lo, k8, v8t, scales) into an fp8 workspace (uint8 tensor).
+    """Views (k8, v8t, scales) into an fp8 workspace (uint8 tensor).
 
-    q8, q8lo, k8: uint8 [B,H,N,d] e4m3 codes (q8lo: residual of Q'); v8t: uint8
-    [B,H,d,Npad] (V transposed, zero padded to Npad = N rounded up to 64, keys
-    permuted inside each 64-key block); scales: fp32 [3, B, H].
+    k8: uint8 [B,H,N,d] e4m3 codes of K'; v8t: uint8 [B,H,d,Npad] (V
+    transposed, zero padded to Npad = N rounded up to 64, keys permuted inside
+    each 64-key block); scales: fp32 [2, B, H] (K', V). Q' is quantised inside
+    the attention kernel and not stored.
     """
     torch = _torch()
-    offs = [ctypes.c_size_t() for _ in range(5)]
+    offs = [ctypes.c_size_t() for _ in range(3)]
     _call(lib().fattn_fwd_fp8_workspace_layout(B, H, N, d, *[ctypes.byref(x) for x in offs]))
-    oq, oql, ok, ov, osc = (x.value for x in offs)
+    ok, ov, osc = (x.value for x in offs)
     npad = (N + 63) // 64 * 64
     n = B * H * N * d
-    q8 = ws[oq:oq + n].view(B, H, N, d)
-    q8lo = ws[oql:oql + n].view(B, H, N, d)
     k8 = ws[ok:ok + n].view(B, H, N, d)
     v8t = ws[ov:ov + B * H * d * npad].view(B, H, d, npad)
-    sc = ws[osc:osc + 12 * B * H].view(torch.float32).view(3, B, H)
-    return q8, q8lo, k8, v8t, sc
+    sc = ws[osc:osc + 8 * B * H].view(torch.float32).view(2, B, H)
+    return k8, v8t, sc
 
 
 def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=True,
@@ -324,21 +323,22 @@ def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=Tru
     return o, lse_t
 
 
-def fwd_fp8_attend(workspace, B, H, N, d, causal=False, scale=None, want_lse=True, out=None,
-                   exp_mode="auto"):
-    """The attention step of fwd_fp8 alone, on a workspace a previous fwd_fp8
-    call of the same (B, H, N, d) filled (outputs on the workspace's device).
-    Returns (O, LSE or None)."""
+def fwd_fp8_attend(q, workspace, causal=False, scale=None, rotate=True, seed=0, want_lse=True,
+                   out=None, exp_mode="auto"):
+    """The attention step of fwd_fp8 alone: q (bf16 [B,H,N,d]) against the K/V
+    operands a previous fwd_fp8 call of the same shape, rotate and seed left
+    in `workspace`. Returns (O, LSE or None)."""
     torch = _torch()
-    B, H, N, d = (int(x) for x in (B, H, N, d))
+    _check(q, "q", torch.bfloat16)
+    B, H, N, d = _shape(q)
     _check(workspace, "workspace", torch.uint8)
-    ws = _workspace(workspace, fp8_workspace_bytes(B, H, N, d), workspace)
-    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=ws.device) if out is None else out
-    _check(o, "out", torch.bfloat16, (B, H, N, d))
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=ws.device) if want_lse else None
-    _on_device(ws, ((o, "out"), (lse_t, "lse")), "workspace")
-    with torch.cuda.device(ws.device):
-        _call(lib().fattn_fwd_fp8_attend(_ptr(o), _ptr(lse_t), B, H, N, d, int(bool(causal)),
-                                         ctypes.c_float(_scale(scale, d)), _EXP[exp_mode],
-                                         _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(o)))
+    ws = _workspace(workspace, fp8_workspace_bytes(B, H, N, d), q)
+    o, lse_t = _outputs(q, out, None, want_lse)
+    _on_device(q, ((ws, "workspace"), (o, "out"), (lse_t, "lse")))
+    with torch.cuda.device(q.device):
+        _call(lib().fattn_fwd_fp8_attend(_ptr(q), _ptr(o), _ptr(lse_t), B, H, N, d,
+                                         int(bool(causal)), ctypes.c_float(_scale(scale, d)),
+                                         _EXP[exp_mode], int(bool(rotate)),
+                                         ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
+                                         ctypes.c_size_t(ws.numel()), _stream(q)))
     return o, lse_t

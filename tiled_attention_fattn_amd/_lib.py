@@ -21,11 +21,11 @@ PROTOTYPES = {
     "fattn_bwd": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float, c_void_p, c_size_t, c_void_p]),
     "fattn_bwd_noalloc": (c_int, [c_void_p] * 9 + [c_int] * 5 + [c_float, c_void_p]),
     "fattn_fwd_fp8_workspace_bytes": (c_size_t, [c_int] * 4),
-    "fattn_fwd_fp8_workspace_layout": (c_int, [c_int] * 4 + [ctypes.POINTER(c_size_t)] * 5),
+    "fattn_fwd_fp8_workspace_layout": (c_int, [c_int] * 4 + [ctypes.POINTER(c_size_t)] * 3),
     "fattn_fwd_fp8": (c_int, [c_void_p] * 5 + [c_int] * 5
                       + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t, c_void_p]),
-    "fattn_fwd_fp8_attend": (c_int, [c_void_p] * 2 + [c_int] * 5
-                             + [c_float, c_int, c_void_p, c_size_t, c_void_p]),
+    "fattn_fwd_fp8_attend": (c_int, [c_void_p] * 3 + [c_int] * 5
+                             + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t, c_void_p]),
     "fattn_strerror": (ctypes.c_char_p, [c_int]),
     "fattn_last_error": (ctypes.c_char_p, []),
     "fattn_version": (c_int, []),

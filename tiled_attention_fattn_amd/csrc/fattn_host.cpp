@@ -84,21 +84,19 @@ fattn_status hip_status(hipError_t e, const char* what) {
   } while (0)
 
 struct Fp8Layout {
-  size_t q8, q8lo, k8, v8t, scales, partial, total;
+  size_t k8, v8t, scales, partial, total;
 };
 
 Fp8Layout fp8_layout(int B, int H, int N, int d) {
   const size_t bh = (size_t)B * H;
   const size_t npad = round_up((size_t)N, fattn::kFp8Npad);
   Fp8Layout L;
-  L.q8 = 0;
-  L.q8lo = round_up(L.q8 + bh * N * d, 256);
-  L.k8 = round_up(L.q8lo + bh * N * d, 256);
+  L.k8 = 0;
   L.v8t = round_up(L.k8 + bh * N * d, 256);
   L.scales = round_up(L.v8t + bh * d * npad, 256);
   const size_t nchunks = (N + fattn::kFp8AmaxRows - 1) / fattn::kFp8AmaxRows;
-  L.partial = round_up(L.scales + 3 * bh * sizeof(float), 256);
-  L.total = round_up(L.partial + 3 * bh * nchunks * sizeof(float), 256);
+  L.partial = round_up(L.scales + 2 * bh * sizeof(float), 256);
+  L.total = round_up(L.partial + 2 * bh * nchunks * sizeof(float), 256);
   return L;
 }
 
@@ -325,13 +323,10 @@ size_t fattn_fwd_fp8_workspace_bytes(int B, int H, int N, int d) {
   return fp8_layout(B, H, N, d).total;
 }
 
-fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d, size_t* off_q8,
-                                            size_t* off_q8lo, size_t* off_k8, size_t* off_v8t,
-                                            size_t* off_scales) {
+fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d, size_t* off_k8,
+                                            size_t* off_v8t, size_t* off_scales) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return fail(FATTN_EINVAL, "B, H, N and d must be >= 1");
   const Fp8Layout L = fp8_layout(B, H, N, d);
-  if (off_q8) *off_q8 = L.q8;
-  if (off_q8lo) *off_q8lo = L.q8lo;
   if (off_k8) *off_k8 = L.k8;
   if (off_v8t) *off_v8t = L.v8t;
   if (off_scales) *off_scales = L.scales;
@@ -358,22 +353,23 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
     return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, L.total);
   FATTN_TRY(check_device());
   char* ws = (char*)workspace;
-  return hip_status(fattn::launch_fwd_fp8(q, k, v, o, lse, (uint8_t*)(ws + L.q8),
-                                          (uint8_t*)(ws + L.q8lo), (uint8_t*)(ws + L.k8), (uint8_t*)(ws + L.v8t),
-                                          (float*)(ws + L.scales), (float*)(ws + L.partial), B,
-                                          H, N, d, causal != 0, scale,
+  return hip_status(fattn::launch_fwd_fp8(q, k, v, o, lse, (uint8_t*)(ws + L.k8),
+                                          (uint8_t*)(ws + L.v8t), (float*)(ws + L.scales),
+                                          (float*)(ws + L.partial), B, H, N, d, causal != 0, scale,
                                           exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode,
                                           rotate != 0, seed, (hipStream_t)stream),
                     "fattn_fwd_fp8 launch");
 }
 
-fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int d, int causal,
-                                  float scale, int exp_mode, const void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+fattn_status fattn_fwd_fp8_attend(const void* q, void* o, float* lse, int B, int H, int N, int d,
+                                  int causal, float scale, int exp_mode, int rotate, uint64_t seed,
+                                  const void* workspace, size_t workspace_bytes, void* stream) {
+  FATTN_TRY(check_ptr(q, "q"));
   FATTN_TRY(check_ptr(o, "o"));
   if (lse != nullptr && !aligned16(lse)) return fail(FATTN_EINVAL, "lse is not 16-byte aligned");
   FATTN_TRY(check_shape(B, H, N, d, causal, scale));
   FATTN_TRY(check_exp_mode(exp_mode));
+  if (rotate != 0 && rotate != 1) return fail(FATTN_EINVAL, "rotate must be 0 or 1 (got %d)", rotate);
   if ((long long)B * H > 65535)
     return fail(FATTN_ENOTSUP, "fp8 forward supports B*H <= 65535 (got %lld)", (long long)B * H);
   if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
@@ -383,14 +379,12 @@ fattn_status fattn_fwd_fp8_attend(void* o, float* lse, int B, int H, int N, int 
     return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, L.total);
   FATTN_TRY(check_device());
   const char* ws = (const char*)workspace;
-  return hip_status(fattn::launch_fwd_fp8_attend(o, lse, (const uint8_t*)(ws + L.q8),
-                                                 (const uint8_t*)(ws + L.q8lo),
-                                                 (const uint8_t*)(ws + L.k8),
+  return hip_status(fattn::launch_fwd_fp8_attend(q, o, lse, (const uint8_t*)(ws + L.k8),
                                                  (const uint8_t*)(ws + L.v8t),
                                                  (const float*)(ws + L.scales), B, H, N, d,
                                                  causal != 0, scale,
                                                  exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode,
-                                                 (hipStream_t)stream),
+                                                 rotate != 0, seed, (hipStream_t)stream),
                     "fattn_fwd_fp8_attend launch");
 }
 

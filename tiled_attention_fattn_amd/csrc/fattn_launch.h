@@ -48,20 +48,21 @@ hipError_t launch_bwd_bf16_blocksparse(const void* q, const void* k, const void*
 
 constexpr int kBwdRowPad = 64;
 
-// fp8 forward: q8/q8lo/k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32
-// [3][B*H]; partial fp32 [3][B*H][ceil(N/kFp8AmaxRows)] scratch.
+// fp8 forward: k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32
+// [2][B*H] (K, V); partial fp32 [2][B*H][ceil(N/kFp8AmaxRows)] scratch. Q is
+// rotated and quantised (one scale per row) inside the attention kernel.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
-                          uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
-                          float* partial,
-                          int B, int H, int N, int d, bool causal, float scale, int exp_mode,
-                          bool rotate, uint64_t seed, hipStream_t stream);
+                          uint8_t* k8, uint8_t* v8t, float* scales, float* partial, int B, int H,
+                          int N, int d, bool causal, float scale, int exp_mode, bool rotate,
+                          uint64_t seed, hipStream_t stream);
 
-// fp8 attention only (the last launch of launch_fwd_fp8) on operands a
-// previous launch_fwd_fp8 of the same shape left in q8/q8lo/k8/v8t/scales.
-hipError_t launch_fwd_fp8_attend(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
-                                 const uint8_t* k8, const uint8_t* v8t, const float* scales, int B,
-                                 int H, int N, int d, bool causal, float scale, int exp_mode,
-                                 hipStream_t stream);
+// fp8 attention only (the last launch of launch_fwd_fp8) on the K/V operands
+// a previous launch_fwd_fp8 of the same shape left in k8/v8t/scales; Q is
+// read in bf16 as in launch_fwd_fp8.
+hipError_t launch_fwd_fp8_attend(const void* q, void* o, float* lse, const uint8_t* k8,
+                                 const uint8_t* v8t, const float* scales, int B, int H, int N,
+                                 int d, bool causal, float scale, int exp_mode, bool rotate,
+                                 uint64_t seed, hipStream_t stream);
 
 // Library-owned backward workspace (static_ws.hip): its capacity, and its
 // device address on `device`, which must be the current device (looked up on

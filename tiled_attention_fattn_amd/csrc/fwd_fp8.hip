@@ -6,18 +6,26 @@
 // SplitMix64 (Steele, Lea & Flood 2014) and H_d the Sylvester Hadamard matrix,
 // applied row by row with a fast Walsh–Hadamard transform in registers.
 //
+// Scales: K' and V one per (b,h) (amax over the head); Q' one per row (the
+// row's own amax), which lets the attention kernel quantise the query rows
+// it owns itself, so Q never makes a round trip through memory in e4m3.
+//
 // Launches (one stream):
-//   1. fp8_amax   — amax of |Q·R|, |K·R| and |V| over each chunk of
-//                   kFp8AmaxRows (128) rows of each (b,h), one plain store
-//                   per block (no atomics).
-//   2. fp8_quant_qk — recompute Q·R, K·R; code = e4m3(t), t = x·448/amax
-//                   (one correctly rounded division), round to nearest even;
-//                   for Q' also the residual code e4m3(16·(t − decode(code)));
-//                   write Q8, Q8lo, K8 and the scales.
+//   1. fp8_amax   — amax of |K·R| and |V| over each chunk of kFp8AmaxRows
+//                   (128) rows of each (b,h), one plain store per block (no
+//                   atomics).
+//   2. fp8_quant_k — recompute K·R; code = e4m3(t), t = x·448/amax (one
+//                   correctly rounded division), round to nearest even;
+//                   write K8 and the K scales.
 //   3. fp8_quant_v  — V codes written transposed ([d][keys]) in the key order
 //                   the attention kernel's P operand uses.
-//   4. fwd_fp8    — attention: Sᵀ = K8·(Q8 + Q8lo/16)ᵀ (two MFMAs, the second
-//                   with the block scale 2^-4) and Oᵀ += V8ᵀ·P8ᵀ on the
+//   4. fwd_fp8    — attention. Prologue: each lane rotates its half of one
+//                   bf16 Q row (the Walsh–Hadamard stages across the two
+//                   lanes of the row by a lane-half swap), takes the row's
+//                   amax and quantises it to Q8 and the residual term
+//                   Q8lo = e4m3(16·(t − decode(Q8))). Loop: Sᵀ =
+//                   K8·(Q8 + Q8lo/16)ᵀ (two MFMAs, the second with the
+//                   block scale 2^-4) and Oᵀ += V8ᵀ·P8ᵀ on the
 //                   32x32x64 f8f6f4 MFMA; P̃ = 2^(s·c − m + 8) quantised to
 //                   e4m3 as P̃·2^(8−τ) with τ = 1: the exponent offset moves
 //                   only when a tile max exceeds it by more than τ
@@ -118,24 +126,23 @@ __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, i
   return ok;
 }
 
-// grid (row chunks, BH, 3 tensors): block max of |x| over kFp8AmaxRows rows.
-// The tensors are taken in the order V, K, Q (blockIdx.z = 0, 1, 2), so that
-// Q and K, which the quantisation kernel reads next, are the most recently
-// read lines in the last-level cache.
+// grid (row chunks, BH, 2 tensors): block max of |x| over kFp8AmaxRows rows.
+// Tensor t = 0 is K·R, t = 1 is V; they are taken in the order V, K
+// (blockIdx.z = 0, 1), so that K, which the quantisation kernel reads next,
+// holds the most recently read lines in the last-level cache.
 template <int D>
-__global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ Q,
-                                                      const bf16* __restrict__ K,
+__global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ K,
                                                       const bf16* __restrict__ V,
                                                       float* __restrict__ partial, int N, int BH,
                                                       int rotate, uint64_t seed) {
   constexpr int LPR = D / kEpl, RPB = 256 / LPR;
   __shared__ float sgn[D];
   __shared__ float wmax[4];
-  const int t = 2 - (int)blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;  // tensor: 0 Q, 1 K, 2 V
-  const bool rot = rotate && t < 2;
+  const int t = 1 - (int)blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
+  const bool rot = rotate && t == 0;
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
   __syncthreads();
-  const bf16* src = (t == 0 ? Q : t == 1 ? K : V) + (size_t)bh * N * D;
+  const bf16* src = (t == 0 ? K : V) + (size_t)bh * N * D;
   const int part = threadIdx.x % LPR;
   float m = 0.0f;
   // kRowSets row-sets per step so that that many loads per thread are in
@@ -211,28 +218,26 @@ __device__ __forceinline__ float ratio448(float x, const Ratio448& r) {
   return fmaf(e, r.inv, q0);
 }
 
-// grid (row chunks, BH, 2 tensors): kFp8AmaxRows rows per block.
+// grid (row chunks, BH): K·R quantised with the head's scale, kFp8AmaxRows
+// rows per block.
 template <int D>
-__global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restrict__ Q,
-                                                          const bf16* __restrict__ K,
-                                                          uint8_t* __restrict__ q8,
-                                                          uint8_t* __restrict__ q8lo,
-                                                          uint8_t* __restrict__ k8,
-                                                          const float* __restrict__ partial,
-                                                          float* __restrict__ scales, int N, int BH,
-                                                          int rotate, uint64_t seed) {
+__global__ __launch_bounds__(256) void fp8_quant_k_kernel(const bf16* __restrict__ K,
+                                                         uint8_t* __restrict__ k8,
+                                                         const float* __restrict__ partial,
+                                                         float* __restrict__ scales, int N,
+                                                         int rotate, uint64_t seed) {
   constexpr int LPR = D / kEpl, RPB = 256 / LPR;
   __shared__ float sgn[D];
   __shared__ float am_slot;
-  const int t = blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
+  const int bh = blockIdx.y, chunk = blockIdx.x;
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
   const int nchunks = gridDim.x;
-  const float am = head_amax(partial + ((size_t)t * BH + bh) * nchunks, nchunks, &am_slot);
-  const Ratio448 rq(am);
+  const float am = head_amax(partial + (size_t)bh * nchunks, nchunks, &am_slot);
+  const Ratio448 rk(am);
   const size_t head = (size_t)bh * N * D;
-  const bf16* src = (t == 0 ? Q : K) + head;
-  uint8_t* dst = (t == 0 ? q8 : k8) + head;
-  if (chunk == 0 && threadIdx.x == 0) scales[t * BH + bh] = scale_from_amax(am);
+  const bf16* src = K + head;
+  uint8_t* dst = k8 + head;
+  if (chunk == 0 && threadIdx.x == 0) scales[bh] = scale_from_amax(am);
   const int part = threadIdx.x % LPR;
   const int r_end = min(N, (chunk + 1) * kFp8AmaxRows);
   for (int r0 = chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
@@ -253,26 +258,13 @@ __global__ __launch_bounds__(256) void fp8_quant_qk_kernel(const bf16* __restric
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float x = xs[u][16 * c + e];
-          tt[e] = am > 0.0f ? clamp448(ratio448(x, rq)) : x;
+          tt[e] = am > 0.0f ? clamp448(ratio448(x, rk)) : x;
         }
         i32x4 w;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           w[g] = cvt_fp8x4(tt[4 * g], tt[4 * g + 1], tt[4 * g + 2], tt[4 * g + 3]);
         *(i32x4*)(dst + off + 16 * c) = w;
-        if (t == 0) {
-          // residual term: 16·(t − decode(code)), exact in fp32, then e4m3 again
-          i32x4 wl;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float dec[4], r[4];
-            dec_fp8x4(w[g], dec);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = 16.0f * (tt[4 * g + e] - dec[e]);
-            wl[g] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
-          }
-          *(i32x4*)(q8lo + head + off + 16 * c) = wl;
-        }
       }
     }
   }
@@ -298,9 +290,9 @@ __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict
   constexpr int CHUNKS = D / 8;
   const int bh = blockIdx.y, kb = blockIdx.x;
   __shared__ float am_slot;
-  const float am = head_amax(partial + ((size_t)2 * BH + bh) * nchunks, nchunks, &am_slot);
+  const float am = head_amax(partial + ((size_t)BH + bh) * nchunks, nchunks, &am_slot);
   const Ratio448 rv(am);
-  if (kb == 0 && threadIdx.x == 0) scales[2 * BH + bh] = scale_from_amax(am);
+  if (kb == 0 && threadIdx.x == 0) scales[BH + bh] = scale_from_amax(am);
   const bf16* src = V + (size_t)bh * N * D;
   uint8_t* dst = v8t + (size_t)bh * D * Npad + (size_t)kb * 64;
   for (int ch = threadIdx.x; ch < 16 * CHUNKS; ch += 256) {
@@ -338,19 +330,19 @@ constexpr int kF8BN = 64;
 
 template <int D, bool CAUSAL, bool WANT_LSE, int EXPM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ q8lo,
-                    const uint8_t* __restrict__ k8,
+void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
                     const uint8_t* __restrict__ v8t, const float* __restrict__ scales,
                     bf16* __restrict__ O, float* __restrict__ LSE, int N, int Npad, int BH,
-                    int n_qtiles, float scale_log2) {
+                    int n_qtiles, float scale_log2, int rotate, uint64_t seed) {
   constexpr int KD = D / 64;           // fp8 MFMA k-steps over d
   constexpr int KTILE = kF8BN * D;     // K8 tile [64 keys][D bytes]
   constexpr int VTILE = D * kF8BN;     // V8ᵀ tile [D][64 keys]
   constexpr int DT = D / 32;
   constexpr int KLOADS = KTILE / 1024 / kF8Waves;  // 1 KB wave loads per tile and wave
   constexpr int VLOADS = VTILE / 1024 / kF8Waves;
-  // LDS: K slots 0, 1 then V slots 0, 1.
+  // LDS: K slots 0, 1 then V slots 0, 1; the rotation's signs.
   __shared__ __attribute__((aligned(16))) char lds[2 * KTILE + 2 * VTILE];
+  __shared__ __attribute__((aligned(16))) float sgn[D];
   char* const k_lds = lds;
   char* const v_lds = lds + 2 * KTILE;
 
@@ -375,34 +367,18 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
     qt = logical - bh * n_qtiles;
   }
 
-  const float sq = scales[bh], sk = scales[BH + bh], sv = scales[2 * BH + bh];
-  const float c_log2 = sq * sk * scale_log2;
+  const float sk = scales[bh], sv = scales[BH + bh];
 
   const size_t head = (size_t)bh * N * D;
-  const uint8_t* Qh = q8 + head;
-  const uint8_t* Ql = q8lo + head;
   const uint8_t* Kh = k8 + head;
   const uint8_t* Vt = v8t + (size_t)bh * D * Npad;
   const int q_start = qt * kF8BM;
   const int q0 = q_start + wave * 32;
   const int qi = q0 + c;
-
+  // Q' operands (two e4m3 terms) and the exp2-domain score factor of this
+  // lane's query row, formed in the prologue below.
   i32x8 qreg[KD], qlo[KD];
-#pragma unroll
-  for (int kk = 0; kk < KD; ++kk) {
-    if (qi < N) {
-      const size_t off = (size_t)qi * D + kk * 64 + 32 * h;
-      const i32x4 a = *(const i32x4*)(Qh + off);
-      const i32x4 b = *(const i32x4*)(Qh + off + 16);
-      qreg[kk] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-      const i32x4 al = *(const i32x4*)(Ql + off);
-      const i32x4 bl = *(const i32x4*)(Ql + off + 16);
-      qlo[kk] = __builtin_shufflevector(al, bl, 0, 1, 2, 3, 4, 5, 6, 7);
-    } else {
-      qreg[kk] = i32x8{};
-      qlo[kk] = i32x8{};
-    }
-  }
+  float c_log2;
 
   // Per-lane LDS offsets of the MFMA A operands: K8 row c (key), bytes
   // kk·64 + 32h .. +32 (two 16-byte chunks); V8ᵀ row c (d within a 32-row
@@ -490,6 +466,91 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   gload_k(k_lds, 0);
   if (n_kv > 1) gload_k(k_lds + KTILE, 1);
   gload_v(v_lds, 0);
+  if (rotate && tid < D) sgn[tid] = rotation_sign(seed, tid);
+  __syncthreads();
+
+  // Q' operands while the first tiles load. Lane (c, h) holds elements
+  // d = 64kk + 32h + e (e < 32) of query row qi: the B operand layout of the
+  // score MFMA. Rotation: signs, then the unnormalised Walsh–Hadamard
+  // butterflies over d bits 0–4 (in lane), bit 5 (the two lane halves, by a
+  // half swap) and bit 6 (in lane, kk), in the same order and form as the
+  // row-wise prep kernels (lower index a + b, upper a − b), then 1/√d. The
+  // row's amax over both halves sets its scale; codes and the residual
+  // term as in the K quantisation.
+  {
+    float x[KD][32];
+    const bf16* Qrow = Q + head + (size_t)qi * D + 32 * h;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 v = qi < N ? *(const bf16x8*)(Qrow + 64 * kk + 8 * u) : bf16x8{};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[kk][8 * u + e] = (float)v[e];
+      }
+    if (rotate) {
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) x[kk][e] *= sgn[64 * kk + 32 * h + e];
+#pragma unroll
+        for (int w = 1; w < 32; w <<= 1)
+#pragma unroll
+          for (int e = 0; e < 32; ++e)
+            if (!(e & w)) {
+              const float a = x[kk][e], b = x[kk][e + w];
+              x[kk][e] = a + b;
+              x[kk][e + w] = a - b;
+            }
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[kk][e]),
+                                                          __float_as_uint(x[kk][e]), false, false);
+          const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+          x[kk][e] = h ? (lo - hi) : (lo + hi);
+        }
+      }
+      if constexpr (KD == 2) {
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          const float a = x[0][e], b = x[1][e];
+          x[0][e] = a + b;
+          x[1][e] = a - b;
+        }
+      }
+      const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+        for (int e = 0; e < 32; ++e) x[kk][e] *= inv_sqrt_d;
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+      for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(x[kk][e]));
+    am = half_max(am);
+    const Ratio448 rq(am);
+    // Scores in the exp2 domain: s·c with c = scale·log2(e)·s_q(row)·s_k.
+    c_log2 = scale_from_amax(am) * sk * scale_log2;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        float tt[4], dec[4], r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = x[kk][4 * g + e];
+          tt[e] = am > 0.0f ? clamp448(ratio448(v, rq)) : v;
+        }
+        const int w = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
+        dec_fp8x4(w, dec);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = 16.0f * (tt[e] - dec[e]);
+        qreg[kk][g] = w;
+        qlo[kk][g] = cvt_fp8x4(r[0], r[1], r[2], r[3]);
+      }
+  }
   wait_vmem();
   __syncthreads();
   f32x16 s[2];
@@ -592,77 +653,86 @@ void fwd_fp8_kernel(const uint8_t* __restrict__ q8, const uint8_t* __restrict__ 
   }
 }
 
+// The attention launch; `a` carries the operands shared by every variant.
+struct Fp8Attend {
+  const bf16* q;
+  const uint8_t* k8;
+  const uint8_t* v8t;
+  const float* scales;
+  bf16* o;
+  float* lse;
+  int BH, N;
+  float scale;
+  int rotate;
+  uint64_t seed;
+};
+
 template <int D, bool CAUSAL, int EXPM>
-static hipError_t launch_attend_m(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
-                                  const uint8_t* k8, const uint8_t* v8t, const float* scales, int BH,
-                                  int N, float scale, hipStream_t stream) {
-  const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
-  const int n_qtiles = (N + kF8BM - 1) / kF8BM;
-  if (lse != nullptr)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, EXPM>), dim3(n_qtiles * BH), dim3(256), 0,
-                       stream, q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
-                       scale * kLog2e);
+static hipError_t launch_attend_m(const Fp8Attend& a, hipStream_t stream) {
+  const int Npad = (a.N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
+  const int n_qtiles = (a.N + kF8BM - 1) / kF8BM;
+  if (a.lse != nullptr)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, EXPM>), dim3(n_qtiles * a.BH), dim3(256),
+                       0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad, a.BH,
+                       n_qtiles, a.scale * kLog2e, a.rotate, a.seed);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, EXPM>), dim3(n_qtiles * BH), dim3(256), 0,
-                       stream, q8, q8lo, k8, v8t, scales, (bf16*)o, lse, N, Npad, BH, n_qtiles,
-                       scale * kLog2e);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, EXPM>), dim3(n_qtiles * a.BH), dim3(256),
+                       0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad, a.BH,
+                       n_qtiles, a.scale * kLog2e, a.rotate, a.seed);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
-static hipError_t launch_attend_t(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
-                                  const uint8_t* k8, const uint8_t* v8t, const float* scales, int BH,
-                                  int N, float scale, int exp_mode, hipStream_t stream) {
-  if (exp_mode == EXP_POLY)
-    return launch_attend_m<D, CAUSAL, EXP_POLY>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
-  if (exp_mode == EXP_SPLIT)
-    return launch_attend_m<D, CAUSAL, EXP_SPLIT>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
-  return launch_attend_m<D, CAUSAL, EXP_HW>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, stream);
+static hipError_t launch_attend_t(const Fp8Attend& a, int exp_mode, hipStream_t stream) {
+  if (exp_mode == EXP_POLY) return launch_attend_m<D, CAUSAL, EXP_POLY>(a, stream);
+  if (exp_mode == EXP_SPLIT) return launch_attend_m<D, CAUSAL, EXP_SPLIT>(a, stream);
+  return launch_attend_m<D, CAUSAL, EXP_HW>(a, stream);
 }
 
-template <int D, bool CAUSAL>
-static hipError_t launch_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse,
-                               uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
-                               float* partial, int BH, int N, float scale, int exp_mode,
-                               bool rotate, uint64_t seed, hipStream_t stream) {
+static hipError_t launch_attend(const Fp8Attend& a, int d, bool causal, int exp_mode,
+                                hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_attend_t<64, true>(a, exp_mode, stream)
+                  : launch_attend_t<64, false>(a, exp_mode, stream);
+  return causal ? launch_attend_t<128, true>(a, exp_mode, stream)
+                : launch_attend_t<128, false>(a, exp_mode, stream);
+}
+
+template <int D>
+static void launch_prep(const void* k, const void* v, uint8_t* k8, uint8_t* v8t, float* scales,
+                        float* partial, int BH, int N, bool rotate, uint64_t seed,
+                        hipStream_t stream) {
   const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
   const unsigned nchunks = (unsigned)((N + kFp8AmaxRows - 1) / kFp8AmaxRows);
-  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(nchunks, BH, 3), dim3(256), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, partial, N, BH, (int)rotate,
-                     seed);
-  hipLaunchKernelGGL((fp8_quant_qk_kernel<D>), dim3(nchunks, BH, 2), dim3(256), 0, stream,
-                     (const bf16*)q, (const bf16*)k, q8, q8lo, k8, (const float*)partial, scales, N,
-                     BH, (int)rotate, seed);
+  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(nchunks, BH, 2), dim3(256), 0, stream,
+                     (const bf16*)k, (const bf16*)v, partial, N, BH, (int)rotate, seed);
+  hipLaunchKernelGGL((fp8_quant_k_kernel<D>), dim3(nchunks, BH), dim3(256), 0, stream,
+                     (const bf16*)k, k8, (const float*)partial, scales, N, (int)rotate, seed);
   hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(Npad / 64, BH), dim3(256), 0, stream,
                      (const bf16*)v, v8t, (const float*)partial, scales, N, Npad, BH, (int)nchunks);
-  return launch_attend_t<D, CAUSAL>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode,
-                                    stream);
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
-                          uint8_t* q8, uint8_t* q8lo, uint8_t* k8, uint8_t* v8t, float* scales,
-                          float* partial, int B, int H, int N, int d, bool causal, float scale,
-                          int exp_mode, bool rotate, uint64_t seed, hipStream_t stream) {
+                          uint8_t* k8, uint8_t* v8t, float* scales, float* partial, int B, int H,
+                          int N, int d, bool causal, float scale, int exp_mode, bool rotate,
+                          uint64_t seed, hipStream_t stream) {
   const int BH = B * H;
-  if (d == 64) {
-    return causal ? launch_fp8_t<64, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream)
-                  : launch_fp8_t<64, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream);
-  }
-  return causal ? launch_fp8_t<128, true>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream)
-                : launch_fp8_t<128, false>(q, k, v, o, lse, q8, q8lo, k8, v8t, scales, partial, BH, N, scale, exp_mode, rotate, seed, stream);
+  if (d == 64) launch_prep<64>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, stream);
+  else launch_prep<128>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, BH, N, scale, (int)rotate,
+                    seed};
+  return launch_attend(a, d, causal, exp_mode, stream);
 }
 
-hipError_t launch_fwd_fp8_attend(void* o, float* lse, const uint8_t* q8, const uint8_t* q8lo,
-                                 const uint8_t* k8, const uint8_t* v8t, const float* scales, int B,
-                                 int H, int N, int d, bool causal, float scale, int exp_mode,
-                                 hipStream_t stream) {
-  const int BH = B * H;
-  if (d == 64) {
-    return causal ? launch_attend_t<64, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream)
-                  : launch_attend_t<64, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream);
-  }
-  return causal ? launch_attend_t<128, true>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream)
-                : launch_attend_t<128, false>(o, lse, q8, q8lo, k8, v8t, scales, BH, N, scale, exp_mode, stream);
+hipError_t launch_fwd_fp8_attend(const void* q, void* o, float* lse, const uint8_t* k8,
+                                 const uint8_t* v8t, const float* scales, int B, int H, int N,
+                                 int d, bool causal, float scale, int exp_mode, bool rotate,
+                                 uint64_t seed, hipStream_t stream) {
+  const Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, B * H, N, scale, (int)rotate,
+                    seed};
+  return launch_attend(a, d, causal, exp_mode, stream);
 }
 
 }  // namespace fattn
