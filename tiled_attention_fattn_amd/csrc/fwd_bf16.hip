@@ -46,6 +46,7 @@
 //  * Block masks (SPARSE): each workgroup is one 128-query block; it reads
 //    its row of the 128×128-block mask once (as 64-bit ballots) and runs the
 //    same schedule over the visible 64-key tiles only.
+#include <algorithm>
 #include <type_traits>
 
 #include "fattn_device.hpp"
@@ -69,6 +70,13 @@ constexpr float kRescaleTau = 8.0f;         // log2 units: P̃ ≤ 2^8 between r
 constexpr float kSumGuard = 256.0f;         // 2^kRescaleTau
 constexpr int kLead = 3;                    // LDS operand reads in flight ahead of the MFMAs
 constexpr int kMaskBlock = kMaskBlockRows;  // block-mask granularity (queries and keys)
+// Causal issue groups (see the workgroup mapping): used for d = 128 when a
+// unit has between these many query tiles. Longer sequences reuse each K/V
+// tile across enough query tiles that cache locality between them no longer
+// matters, very short ones have too little K/V for it to matter, and at
+// d = 64 (three workgroups per compute unit) the groups were slower (all
+// measured).
+constexpr int kCausalGroupMinTiles = 4, kCausalGroupMaxTiles = 16;
 
 
 // Running softmax state of one 32-query sub-tile (per lane: one query).
@@ -142,7 +150,8 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O, float* __restrict__ LSE,
                      int N, int BH, int n_qtiles, float c_log2, const int* __restrict__ cu,
-                     int nseq, const uint8_t* __restrict__ bmask, long mask_stride) {
+                     int nseq, const uint8_t* __restrict__ bmask, long mask_stride,
+                     int group_units) {
   static_assert(!(VARLEN && SPARSE), "block masks apply to whole sequences");
   static_assert(WAVES == 4 || (WAVES == 8 && !CAUSAL && !VARLEN && !SPARSE),
                 "eight waves only for plain non-causal attention");
@@ -166,10 +175,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // Workgroup → (head[, segment], query tile).
   //  * Causal: tile-major from the last query tile down, so the heaviest
   //    tiles (a tile's work grows with its index) of every head and segment
-  //    are issued before any lighter one, longest-processing-time first over
-  //    the whole grid; consecutive ids run round-robin over the XCDs, so
-  //    (with a multiple of 8 units) an XCD keeps the same (head, segment)
-  //    units from tile to tile.
+  //    are issued before any lighter one, longest-processing-time first
+  //    (within a group of units, below); consecutive ids run round-robin over
+  //    the XCDs, so (with a multiple of 8 units) an XCD keeps the same
+  //    (head, segment) units from tile to tile.
   //  * Packed segments without the mask: longest segment first (every tile
   //    of a segment costs its length): the workgroup's rank r picks the r-th
   //    longest segment, heads interleaved within a rank.
@@ -177,9 +186,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   //    tiles of one head share that XCD's L2.
   int unit, qt;
   if constexpr (CAUSAL) {
+    // Units are issued in groups of group_units (chosen by the launch), each
+    // group tile-major as above: for short sequences one group fills the
+    // resident workgroups once, so the few units on each XCD keep their K
+    // and V in its L2 while all their tiles run.
     const int units = BH * (VARLEN ? nseq : 1);
-    const int step = (int)(blockIdx.x / units);
-    unit = blockIdx.x - step * units;
+    const int gh = min(units, group_units);
+    const int g0 = (int)(blockIdx.x / (gh * n_qtiles)) * gh;
+    const int gsize = min(gh, units - g0);
+    const int rem = (int)blockIdx.x - g0 * n_qtiles;
+    const int step = rem / gsize;
+    unit = g0 + (rem - step * gsize);
     qt = n_qtiles - 1 - step;
   } else if constexpr (VARLEN) {
     const int per_rank = BH * n_qtiles;
@@ -530,12 +547,34 @@ template <int D, bool CAUSAL, int EXPM, int MODE, int WAVES>
 static hipError_t launch_fwd_w(const void* q, const void* k, const void* v, void* o, float* lse,
                                int BH, int N, float scale, const FwdAux& x, hipStream_t stream) {
   constexpr int bm = kFwdQW * WAVES;
+  const auto kernel =
+      fwd_bf16_kernel<D, CAUSAL, EXPM, MODE == FWD_VARLEN, MODE == FWD_SPARSE, WAVES>;
   const int n_qtiles = ((MODE == FWD_VARLEN ? x.max_len : N) + bm - 1) / bm;
-  const dim3 grid(n_qtiles * BH * (MODE == FWD_VARLEN ? x.nseq : 1)), block(64 * WAVES);
-  hipLaunchKernelGGL(
-      (fwd_bf16_kernel<D, CAUSAL, EXPM, MODE == FWD_VARLEN, MODE == FWD_SPARSE, WAVES>), grid,
-      block, 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, BH,
-      n_qtiles, scale * kLog2e, x.cu, x.nseq, x.bmask, x.mask_stride);
+  const int units = BH * (MODE == FWD_VARLEN ? x.nseq : 1);
+  int group_units = units;
+  if constexpr (CAUSAL) {
+    // One group = the workgroups the device keeps resident (queried once per
+    // kernel instance), rounded down to whole units, a multiple of 8 (the
+    // XCD count) so that each XCD holds the same units from tile to tile.
+    static const int resident = [kernel] {
+      int occ = 0, dev = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 64 * WAVES, 0) !=
+              hipSuccess ||
+          hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+      }
+      return occ * cus;
+    }();
+    if (D == 128 && n_qtiles >= kCausalGroupMinTiles && n_qtiles <= kCausalGroupMaxTiles &&
+        resident > 0)
+      group_units = std::max(8, resident / n_qtiles / 8 * 8);
+  }
+  hipLaunchKernelGGL(kernel, dim3(n_qtiles * units), dim3(64 * WAVES), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, BH,
+                     n_qtiles, scale * kLog2e, x.cu, x.nseq, x.bmask, x.mask_stride,
+                     group_units);
   return hipGetLastError();
 }
 
