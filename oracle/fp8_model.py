@@ -104,12 +104,15 @@ def dequantize_split(codes, resid, scales):
         np.asarray(scales)[:, :, None, None]
 
 
-def fp8_attention_model(q, k, v, causal, scale, rotate, seed):
+def fp8_attention_model(q, k, v, causal, scale, rotate, seed, block_mask=None):
     """Rotate (optionally), quantise Q' (two terms, per row), K' and V (per
     head), dequantise, attend.
 
     Returns a dict with the float64 output O and LSE of the model and the
     intermediate codes / scales for comparison with the quantisation step.
+    ``block_mask`` (optional) is the block mask of ``attention_forward``: the
+    quantisation is unchanged, the attention of the dequantised operands is
+    restricted to the visible blocks.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -120,6 +123,6 @@ def fp8_attention_model(q, k, v, causal, scale, rotate, seed):
     k8, sk = quantize_per_head(kr)
     v8, sv = quantize_per_head(v)
     o, lse = attention_forward(dequantize_split_rows(q8, q8lo, sq), dequantize(k8, sk),
-                               dequantize(v8, sv), causal, scale)
+                               dequantize(v8, sv), causal, scale, block_mask=block_mask)
     return {"o": o, "lse": lse, "q8": q8, "q8lo": q8lo, "k8": k8, "v8": v8,
             "sq": sq, "sk": sk, "sv": sv, "q_rot": qr, "k_rot": kr}

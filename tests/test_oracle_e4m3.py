@@ -190,3 +190,28 @@ def test_per_row_scale_is_invariant_under_row_scaling():
     np.testing.assert_array_equal(a[1], b[1])
     assert b[2][0, 0, 2] == a[2][0, 0, 2] * 32
     np.testing.assert_array_equal(np.delete(a[2][0, 0], 2), np.delete(b[2][0, 0], 2))
+
+
+def test_fp8_model_block_mask_is_attention_on_dequantised_with_the_mask():
+    # The block mask leaves the quantisation alone and restricts the
+    # attention of the dequantised operands: the same codes as without a mask,
+    # the output equal to the masked attention of the dequantised operands,
+    # and an all-ones mask equal to no mask.
+    from oracle.fp8_model import dequantize_split_rows
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((1, 2, 300, 16)) for _ in range(3))
+    mask = (rng.random((3, 3)) < 0.6).astype(np.uint8)
+    mask[1] = 0
+    m = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=2, block_mask=mask)
+    m0 = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=2)
+    for key in ("q8", "q8lo", "k8", "v8"):
+        np.testing.assert_array_equal(m[key], m0[key])
+    o, lse = attention_forward(dequantize_split_rows(m["q8"], m["q8lo"], m["sq"]),
+                               dequantize(m["k8"], m["sk"]), dequantize(m["v8"], m["sv"]),
+                               False, 0.25, block_mask=mask)
+    np.testing.assert_array_equal(m["o"], o)
+    np.testing.assert_array_equal(m["lse"], lse)
+    assert np.all(m["o"][:, :, 128:256] == 0) and np.all(np.isneginf(m["lse"][:, :, 128:256]))
+    ones = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=2,
+                               block_mask=np.ones((3, 3), dtype=np.uint8))
+    np.testing.assert_allclose(ones["o"], m0["o"], rtol=0, atol=1e-14)
