@@ -265,6 +265,28 @@ fattn_status fattn_fwd_fp8_attend(const void* q, void* o, float* lse, int B, int
                                   uint64_t seed, const void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * Block-sparse fp8 forward: fattn_fwd_fp8 restricted by a block mask
+ * (FlashAttention-4 gist, closing summary: block-sparse named among the
+ * variants the design admits; FlashAttention-3 page, innovation 3 for the
+ * fp8 operands). block_mask and per_head exactly as for
+ * fattn_fwd_blocksparse (uint8 over 128-query × 128-key blocks, device
+ * memory, read as given; key blocks a query block does not see are never
+ * loaded). The quantisation is that of fattn_fwd_fp8: K' and V with one
+ * scale per (b, h) taken over all N keys, whether visible or not, and Q'
+ * per row; the workspace is filled the same way, so a later
+ * fattn_fwd_fp8_attend on it computes dense attention of the same operands.
+ * A query that sees no key gets O = 0 and LSE = −∞. With every block set
+ * the result equals fattn_fwd_fp8's. Supports N <= 32768 (ENOTSUP beyond);
+ * everything else, errors included, as fattn_fwd_fp8.
+ */
+fattn_status fattn_fwd_fp8_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const uint8_t* block_mask, int per_head,
+                                       int B, int H, int N, int d, int causal, float scale,
+                                       int exp_mode, int rotate, uint64_t seed,
+                                       void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
 /* Static description of a status code. */
 const char* fattn_strerror(int status);
 /* Detail of the last error on the calling thread (argument or HIP message). */

@@ -192,6 +192,32 @@ def test_fwd_blocksparse_checks():
     assert fa.lib().fattn_last_error()
 
 
+def test_fp8_blocksparse_checks():
+    lib = fa.lib()
+    B, H, N, d = 1, 2, 300, 128
+    need = lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
+
+    def call(ws, nbytes, **kw):
+        a = dict(q=P, mask=P, per_head=0, N=N, d=d, causal=0, exp=0, rotate=1, lse=NUL)
+        a.update(kw)
+        return lib.fattn_fwd_fp8_blocksparse(a["q"], P, P, P, a["lse"], a["mask"], a["per_head"],
+                                             B, H, a["N"], a["d"], a["causal"],
+                                             ctypes.c_float(0.1), a["exp"], a["rotate"],
+                                             ctypes.c_uint64(7), ws, nbytes, NUL)
+    assert call(P, need, mask=NUL) == EINVAL
+    assert call(P, need, per_head=2) == EINVAL
+    assert call(P, need, q=MIS) == EINVAL
+    assert call(P, need, lse=MIS) == EINVAL
+    assert call(P, need, d=80) == ENOTSUP
+    assert call(P, need, causal=3) == EINVAL
+    assert call(P, need, exp=7) == EINVAL
+    assert call(P, need, rotate=-1) == EINVAL
+    assert call(P, need - 1) == EWORKSPACE
+    assert call(NUL, need) == EWORKSPACE
+    assert call(P, lib.fattn_fwd_fp8_workspace_bytes(B, H, 40000, d), N=40000) == ENOTSUP
+    assert fa.lib().fattn_last_error()
+
+
 def test_bwd_blocksparse_checks():
     lib = fa.lib()
     B, H, N, d = 1, 2, 300, 128

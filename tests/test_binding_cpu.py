@@ -49,6 +49,10 @@ lse = t(B, H, N, dtype=torch.float32)
     (lambda: fa.fwd_fp8(q, q, t(B, H, N, D, dtype=torch.float32)), "v must be"),
     (lambda: fa.fwd_fp8(q, q, q, out=t(B, H, N, D, dtype=torch.float16)), "out must be"),
     (lambda: fa.fwd_fp8(q, q, q, workspace=t(64, dtype=torch.uint8)), "at least"),
+    (lambda: fa.fwd_fp8_blocksparse(q, q, q, t(2, 2, dtype=torch.uint8)), "block_mask must be"),
+    (lambda: fa.fwd_fp8_blocksparse(q, q, q, t(1, 1, dtype=torch.float32)), "block_mask must be"),
+    (lambda: fa.fwd_fp8_blocksparse(q, q, q, t(1, 1, dtype=torch.uint8),
+                                    workspace=t(64, dtype=torch.uint8)), "at least"),
     (lambda: fa.fwd_fp8_attend(q, t(64, dtype=torch.uint8)), "at least"),
     (lambda: fa.fwd_fp8_attend(q, None), "workspace must be"),
     (lambda: fa.fwd_fp8_attend(t(B, H, N, D, dtype=torch.float32), t(10 ** 6, dtype=torch.uint8)),
@@ -66,6 +70,7 @@ def test_malformed_arguments_raise_before_any_call(call, msg):
     lambda: fa.bwd(q, q, q, q, lse, q),
     lambda: fa.fwd_fp8(q, q, q),
     lambda: fa.fwd_fp8_attend(q, t(10 ** 6, dtype=torch.uint8)),
+    lambda: fa.fwd_fp8_blocksparse(q, q, q, t(1, 1, dtype=torch.uint8)),
 ])
 def test_well_formed_cpu_tensors_reach_the_device_check(call):
     with pytest.raises(ValueError, match="must be on a GPU device"):

@@ -75,7 +75,7 @@ CASES = [
     ((1, 1, 1, 128), False),
     ((1, 3, 300, 64), True),
     ((1, 2, 1000, 128), False),
-    ((1, 1, 4100, 128), False),  # 256-query workgroups (non-causal, d=128, N >= 4096), ragged
+    ((1, 1, 4100, 128), False),  # many key tiles, ragged
     ((1, 2, 2085, 128), True),   # causal over many tiles, ragged
 ]
 

@@ -11,6 +11,7 @@ an exception is raised.
     o, lse = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False)
     dq, dk, dv = bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False)
     o, lse = fwd_blocksparse(q, k, v, block_mask, causal=False)
+    o, lse = fwd_fp8_blocksparse(q, k, v, block_mask, causal=False, rotate=True, seed=0)
     dq, dk, dv = bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=False)
 
 Tensors are contiguous CUDA (HIP) bfloat16 [B, H, N, d], d ∈ {64, 128};
@@ -21,7 +22,7 @@ import os
 
 from ._lib import FattnError, lib, lib_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_WORKSPACE_BYTES", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "bwd_blocksparse", "fwd_fp8", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_WORKSPACE_BYTES", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "bwd_blocksparse", "fwd_fp8", "fwd_fp8_blocksparse", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
            "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
            "EXP_AUTO", "EXP_HW", "EXP_POLY", "EXP_SPLIT"]
 
@@ -320,6 +321,26 @@ def fwd_fp8(q, k, v, causal=False, scale=None, rotate=True, seed=0, want_lse=Tru
                                   _EXP[exp_mode], int(bool(rotate)),
                                   ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
                                   ctypes.c_size_t(ws.numel()), _stream(q)))
+    return o, lse_t
+
+
+def fwd_fp8_blocksparse(q, k, v, block_mask, causal=False, scale=None, rotate=True, seed=0,
+                        want_lse=True, workspace=None, out=None, exp_mode="auto"):
+    """fwd_fp8 restricted by a block mask (as for fwd_blocksparse): the same
+    quantisation, attention over the visible key blocks only. Returns
+    (O, LSE or None)."""
+    B, H, N, d = _check_qkv(q, k, v)
+    per_head = _bmask(block_mask, q)
+    o, lse_t = _outputs(q, out, None, want_lse)
+    ws = _workspace(workspace, fp8_workspace_bytes(B, H, N, d), q)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "out"), (ws, "workspace")))
+    with _torch().cuda.device(q.device):
+        _call(lib().fattn_fwd_fp8_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
+                                              _ptr(block_mask), per_head, B, H, N, d,
+                                              int(bool(causal)), ctypes.c_float(_scale(scale, d)),
+                                              _EXP[exp_mode], int(bool(rotate)),
+                                              ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
+                                              ctypes.c_size_t(ws.numel()), _stream(q)))
     return o, lse_t
 
 

@@ -24,6 +24,9 @@ PROTOTYPES = {
     "fattn_fwd_fp8_workspace_layout": (c_int, [c_int] * 4 + [ctypes.POINTER(c_size_t)] * 3),
     "fattn_fwd_fp8": (c_int, [c_void_p] * 5 + [c_int] * 5
                       + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t, c_void_p]),
+    "fattn_fwd_fp8_blocksparse": (c_int, [c_void_p] * 6 + [c_int] * 6
+                                  + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t,
+                                     c_void_p]),
     "fattn_fwd_fp8_attend": (c_int, [c_void_p] * 3 + [c_int] * 5
                              + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t, c_void_p]),
     "fattn_strerror": (ctypes.c_char_p, [c_int]),

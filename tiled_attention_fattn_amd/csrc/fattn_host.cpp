@@ -333,9 +333,13 @@ fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d, size_t* 
   return FATTN_OK;
 }
 
-fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                           int H, int N, int d, int causal, float scale, int exp_mode, int rotate,
-                           uint64_t seed, void* workspace, size_t workspace_bytes, void* stream) {
+// fattn_fwd_fp8 and fattn_fwd_fp8_blocksparse: one validation and launch path
+// (block_mask NULL for dense attention).
+static fattn_status fwd_fp8_impl(const char* name, const void* q, const void* k, const void* v,
+                                 void* o, float* lse, const uint8_t* block_mask, int per_head,
+                                 int B, int H, int N, int d, int causal, float scale, int exp_mode,
+                                 int rotate, uint64_t seed, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   FATTN_TRY(check_ptr(q, "q"));
   FATTN_TRY(check_ptr(k, "k"));
   FATTN_TRY(check_ptr(v, "v"));
@@ -346,6 +350,12 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
   if (rotate != 0 && rotate != 1) return fail(FATTN_EINVAL, "rotate must be 0 or 1 (got %d)", rotate);
   if ((long long)B * H > 65535)
     return fail(FATTN_ENOTSUP, "fp8 forward supports B*H <= 65535 (got %lld)", (long long)B * H);
+  if (block_mask != nullptr) {
+    if (per_head != 0 && per_head != 1)
+      return fail(FATTN_EINVAL, "per_head must be 0 or 1 (got %d)", per_head);
+    if (N > 32768)
+      return fail(FATTN_ENOTSUP, "block-sparse forward supports N <= 32768 (got %d)", N);
+  }
   if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
   if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
   const Fp8Layout L = fp8_layout(B, H, N, d);
@@ -357,8 +367,27 @@ fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o,
                                           (uint8_t*)(ws + L.v8t), (float*)(ws + L.scales),
                                           (float*)(ws + L.partial), B, H, N, d, causal != 0, scale,
                                           exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode,
-                                          rotate != 0, seed, (hipStream_t)stream),
-                    "fattn_fwd_fp8 launch");
+                                          rotate != 0, seed, block_mask, per_head != 0,
+                                          (hipStream_t)stream),
+                    name);
+}
+
+fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int N, int d, int causal, float scale, int exp_mode, int rotate,
+                           uint64_t seed, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_fp8_impl("fattn_fwd_fp8 launch", q, k, v, o, lse, nullptr, 0, B, H, N, d, causal,
+                      scale, exp_mode, rotate, seed, workspace, workspace_bytes, stream);
+}
+
+fattn_status fattn_fwd_fp8_blocksparse(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, const uint8_t* block_mask, int per_head, int B,
+                                       int H, int N, int d, int causal, float scale, int exp_mode,
+                                       int rotate, uint64_t seed, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (block_mask == nullptr) return fail(FATTN_EINVAL, "block_mask is NULL");
+  return fwd_fp8_impl("fattn_fwd_fp8_blocksparse launch", q, k, v, o, lse, block_mask, per_head, B,
+                      H, N, d, causal, scale, exp_mode, rotate, seed, workspace, workspace_bytes,
+                      stream);
 }
 
 fattn_status fattn_fwd_fp8_attend(const void* q, void* o, float* lse, int B, int H, int N, int d,

@@ -328,12 +328,18 @@ constexpr int kF8Waves = 4;
 constexpr int kF8BM = 32 * kF8Waves;
 constexpr int kF8BN = 64;
 
-template <int D, bool CAUSAL, bool WANT_LSE, int EXPM>
+// SPARSE: a block mask over 128-query × 128-key blocks (one per head, or
+// shared): the workgroup (one 128-query block) reads its mask row once and
+// walks only the visible 64-key tiles with the same schedule; a row that
+// sees no key writes O = 0 (and LSE = −∞).
+template <int D, bool CAUSAL, bool WANT_LSE, int EXPM, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
                     const uint8_t* __restrict__ v8t, const float* __restrict__ scales,
                     bf16* __restrict__ O, float* __restrict__ LSE, int N, int Npad, int BH,
-                    int n_qtiles, float scale_log2, int rotate, uint64_t seed) {
+                    int n_qtiles, float scale_log2, int rotate, uint64_t seed,
+                    const uint8_t* __restrict__ bmask, long mask_stride) {
+  static_assert(!SPARSE || kF8BM == kMaskBlockRows, "one query tile per mask block row");
   constexpr int KD = D / 64;           // fp8 MFMA k-steps over d
   constexpr int KTILE = kF8BN * D;     // K8 tile [64 keys][D bytes]
   constexpr int VTILE = D * kF8BN;     // V8ᵀ tile [D][64 keys]
@@ -463,9 +469,36 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     return half_max(mx) * c_log2;
   };
 
-  gload_k(k_lds, 0);
-  if (n_kv > 1) gload_k(k_lds + KTILE, 1);
-  gload_v(v_lds, 0);
+  // Key tiles in processing order: all of [0, n_kv), or under a block mask
+  // only those whose 128-key block this 128-query block sees (its mask row,
+  // read once into 64-bit ballots).
+  uint64_t mb[kMaskWords] = {};
+  if constexpr (SPARSE) {
+    const int nb = (N + kMaskBlockRows - 1) / kMaskBlockRows;
+    load_mask_bits(bmask + bh * mask_stride + (long)qt * nb, 1, nb, lane, mb);
+  }
+  auto next_tile = [&](int j) __device__ {
+    if constexpr (SPARSE) return next_mask_tile(mb, j, n_kv);
+    return j;
+  };
+  const int c0 = next_tile(0), c1 = next_tile(c0 + 1);
+  if (c0 >= n_kv) {  // no visible key for any row of the block: O = 0, LSE = −∞
+    if (qi < N) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(i32x2*)(O + head + (size_t)qi * D + 32 * dt + 8 * g + 4 * h) = i32x2{};
+      if constexpr (WANT_LSE) {
+        if (h == 0) LSE[(size_t)bh * N + qi] = -INFINITY;
+      }
+    }
+    return;
+  }
+
+  gload_k(k_lds, c0);
+  if (c1 < n_kv) gload_k(k_lds + KTILE, c1);
+  gload_v(v_lds, c0);
   if (rotate && tid < D) sgn[tid] = rotation_sign(seed, tid);
   __syncthreads();
 
@@ -555,18 +588,21 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   __syncthreads();
   f32x16 s[2];
   scores(k_lds, s);
-  if (first_masked == 0) mask(s, 0);
+  if (c0 >= first_masked) mask(s, c0 * kF8BN);
   // The exponent offset starts at tile 0's row max; P̃ ≤ 2^τ afterwards.
   float m_c = tile_max(s);
   // The first iteration refills K slot 0: every wave must have read K(0).
   __syncthreads();
 
-  auto iteration = [&](int j, auto parity_tag, auto has_next_tag) __device__ {
+  // Tile j (this iteration), jn and jn2 (the next two in processing order;
+  // j + 1 and j + 2 without a block mask).
+  auto iteration = [&](int j, int jn, int jn2, auto parity_tag, auto has_next_tag) __device__ {
     constexpr int PAR = decltype(parity_tag)::value;
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    (void)j;
     if constexpr (HAS_NEXT) {
-      if (j + 2 < n_kv) gload_k(k_lds + PAR * KTILE, j + 2);
-      gload_v(v_lds + (PAR ^ 1) * VTILE, j + 1);
+      if (jn2 < n_kv) gload_k(k_lds + PAR * KTILE, jn2);
+      gload_v(v_lds + (PAR ^ 1) * VTILE, jn);
     }
     // P̃·2^(8−τ) in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
     const float off = kF8PExp - m_c;
@@ -590,7 +626,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
       scores(k_lds + (PAR ^ 1) * KTILE, ns);
       // Keep the softmax of tile j beside these MFMAs.
       asm volatile("" ::"v"(p8));
-      if (j + 1 >= first_masked) mask(ns, (j + 1) * kF8BN);
+      if (jn >= first_masked) mask(ns, jn * kF8BN);
     }
     const char* vt = v_lds + PAR * VTILE;
 #pragma unroll
@@ -622,16 +658,40 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  int j = 0;
-  for (; j + 2 < n_kv; j += 2) {
-    iteration(j, I0{}, std::true_type{});
-    iteration(j + 1, I1{}, std::true_type{});
-  }
-  if (j + 1 < n_kv) {
-    iteration(j, I0{}, std::true_type{});
-    iteration(j + 1, I1{}, std::false_type{});
+  if constexpr (!SPARSE) {
+    int j = 0;
+    for (; j + 2 < n_kv; j += 2) {
+      iteration(j, j + 1, j + 2, I0{}, std::true_type{});
+      iteration(j + 1, j + 2, j + 3, I1{}, std::true_type{});
+    }
+    if (j + 1 < n_kv) {
+      iteration(j, j + 1, j + 2, I0{}, std::true_type{});
+      iteration(j + 1, n_kv, n_kv, I1{}, std::false_type{});
+    } else {
+      iteration(j, n_kv, n_kv, I0{}, std::false_type{});
+    }
   } else {
-    iteration(j, I0{}, std::false_type{});
+    // The same schedule over the visible tiles only (n_act of them; slots
+    // alternate by position): a, b, cc are the tiles at positions p, p+1, p+2.
+    const int n_act = count_mask_tiles(mb, 0, n_kv);
+    int a = c0, b = c1, cc = next_tile(c1 + 1);
+    int p = 0;
+    for (; p + 2 < n_act; p += 2) {
+      iteration(a, b, cc, I0{}, std::true_type{});
+      a = b;
+      b = cc;
+      cc = next_tile(cc + 1);
+      iteration(a, b, cc, I1{}, std::true_type{});
+      a = b;
+      b = cc;
+      cc = next_tile(cc + 1);
+    }
+    if (p + 1 < n_act) {
+      iteration(a, b, cc, I0{}, std::true_type{});
+      iteration(b, n_kv, n_kv, I1{}, std::false_type{});
+    } else {
+      iteration(a, n_kv, n_kv, I0{}, std::false_type{});
+    }
   }
 
   const float inv = sv / lacc[0];
@@ -665,21 +725,31 @@ struct Fp8Attend {
   float scale;
   int rotate;
   uint64_t seed;
+  const uint8_t* bmask = nullptr;  // block mask (SPARSE launches)
+  long mask_stride = 0;            // elements between the masks of consecutive heads (0: shared)
 };
 
-template <int D, bool CAUSAL, int EXPM>
-static hipError_t launch_attend_m(const Fp8Attend& a, hipStream_t stream) {
+template <int D, bool CAUSAL, int EXPM, bool SPARSE>
+static hipError_t launch_attend_s(const Fp8Attend& a, hipStream_t stream) {
   const int Npad = (a.N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
   const int n_qtiles = (a.N + kF8BM - 1) / kF8BM;
   if (a.lse != nullptr)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, EXPM>), dim3(n_qtiles * a.BH), dim3(256),
-                       0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad, a.BH,
-                       n_qtiles, a.scale * kLog2e, a.rotate, a.seed);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, EXPM, SPARSE>), dim3(n_qtiles * a.BH),
+                       dim3(256), 0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad,
+                       a.BH, n_qtiles, a.scale * kLog2e, a.rotate, a.seed, a.bmask,
+                       a.mask_stride);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, EXPM>), dim3(n_qtiles * a.BH), dim3(256),
-                       0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad, a.BH,
-                       n_qtiles, a.scale * kLog2e, a.rotate, a.seed);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, EXPM, SPARSE>), dim3(n_qtiles * a.BH),
+                       dim3(256), 0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad,
+                       a.BH, n_qtiles, a.scale * kLog2e, a.rotate, a.seed, a.bmask,
+                       a.mask_stride);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, int EXPM>
+static hipError_t launch_attend_m(const Fp8Attend& a, hipStream_t stream) {
+  return a.bmask != nullptr ? launch_attend_s<D, CAUSAL, EXPM, true>(a, stream)
+                            : launch_attend_s<D, CAUSAL, EXPM, false>(a, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -715,14 +785,19 @@ static void launch_prep(const void* k, const void* v, uint8_t* k8, uint8_t* v8t,
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                           uint8_t* k8, uint8_t* v8t, float* scales, float* partial, int B, int H,
                           int N, int d, bool causal, float scale, int exp_mode, bool rotate,
-                          uint64_t seed, hipStream_t stream) {
+                          uint64_t seed, const uint8_t* block_mask, bool per_head,
+                          hipStream_t stream) {
   const int BH = B * H;
   if (d == 64) launch_prep<64>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, stream);
   else launch_prep<128>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, BH, N, scale, (int)rotate,
-                    seed};
+  Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, BH, N, scale, (int)rotate, seed};
+  if (block_mask != nullptr) {
+    const long nb = (N + kMaskBlockRows - 1) / kMaskBlockRows;
+    a.bmask = block_mask;
+    a.mask_stride = per_head ? nb * nb : 0;
+  }
   return launch_attend(a, d, causal, exp_mode, stream);
 }
 
