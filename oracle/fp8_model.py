@@ -104,7 +104,34 @@ def dequantize_split(codes, resid, scales):
         np.asarray(scales)[:, :, None, None]
 
 
-def fp8_attention_model(q, k, v, causal, scale, rotate, seed, block_mask=None):
+def quantize_per_segment(x, cu_seqlens):
+    """quantize_per_head applied to each segment's rows [cu[s], cu[s+1]) of
+    x [B, H, N, d] on its own: (codes [B,H,N,d], scales [B,H,nseq]).
+
+    Rows outside every segment keep code 0.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    cu = [int(c) for c in cu_seqlens]
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.ones(x.shape[:2] + (len(cu) - 1,), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if b > a:
+            codes[:, :, a:b], scales[:, :, s] = quantize_per_head(x[:, :, a:b])
+    return codes, scales
+
+
+def dequantize_per_segment(codes, scales, cu_seqlens):
+    """decode(codes) · the scale of the row's segment."""
+    out = np.zeros(codes.shape, dtype=np.float64)
+    cu = [int(c) for c in cu_seqlens]
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        out[:, :, a:b] = e4m3_decode(codes[:, :, a:b]) * np.asarray(scales)[:, :, s, None, None]
+    return out
+
+
+def fp8_attention_model(q, k, v, causal, scale, rotate, seed, block_mask=None, cu_seqlens=None):
     """Rotate (optionally), quantise Q' (two terms, per row), K' and V (per
     head), dequantise, attend.
 
@@ -112,7 +139,11 @@ def fp8_attention_model(q, k, v, causal, scale, rotate, seed, block_mask=None):
     intermediate codes / scales for comparison with the quantisation step.
     ``block_mask`` (optional) is the block mask of ``attention_forward``: the
     quantisation is unchanged, the attention of the dequantised operands is
-    restricted to the visible blocks.
+    restricted to the visible blocks. ``cu_seqlens`` (optional) packs
+    variable-length sequences as in ``attention_forward``; each segment is a
+    sequence of its own, so K' and V get one scale per (batch, head,
+    segment), taken over the segment's rows only (sk, sv are then
+    [B, H, nseq]), and a query attends to its own segment's keys.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -120,9 +151,16 @@ def fp8_attention_model(q, k, v, causal, scale, rotate, seed, block_mask=None):
     qr = _rotate(q, seed) if rotate else q
     kr = _rotate(k, seed) if rotate else k
     q8, q8lo, sq = quantize_per_row_split(qr)
-    k8, sk = quantize_per_head(kr)
-    v8, sv = quantize_per_head(v)
-    o, lse = attention_forward(dequantize_split_rows(q8, q8lo, sq), dequantize(k8, sk),
-                               dequantize(v8, sv), causal, scale, block_mask=block_mask)
+    if cu_seqlens is None:
+        k8, sk = quantize_per_head(kr)
+        v8, sv = quantize_per_head(v)
+        kd, vd = dequantize(k8, sk), dequantize(v8, sv)
+    else:
+        k8, sk = quantize_per_segment(kr, cu_seqlens)
+        v8, sv = quantize_per_segment(v, cu_seqlens)
+        kd = dequantize_per_segment(k8, sk, cu_seqlens)
+        vd = dequantize_per_segment(v8, sv, cu_seqlens)
+    o, lse = attention_forward(dequantize_split_rows(q8, q8lo, sq), kd, vd, causal, scale,
+                               cu_seqlens=cu_seqlens, block_mask=block_mask)
     return {"o": o, "lse": lse, "q8": q8, "q8lo": q8lo, "k8": k8, "v8": v8,
             "sq": sq, "sk": sk, "sv": sv, "q_rot": qr, "k_rot": kr}

@@ -215,3 +215,43 @@ def test_fp8_model_block_mask_is_attention_on_dequantised_with_the_mask():
     ones = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=2,
                                block_mask=np.ones((3, 3), dtype=np.uint8))
     np.testing.assert_allclose(ones["o"], m0["o"], rtol=0, atol=1e-14)
+
+
+def test_fp8_model_segments_are_sequences_of_their_own():
+    # Packed segments: every segment's rows equal the model run on that
+    # segment alone as a separate input (its own K'/V scales over its own
+    # rows, its own keys only), one segment over all rows equals the plain
+    # model, and scaling one segment's K and V by 32 changes no other
+    # segment's codes or outputs.
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((1, 2, 200, 16)) for _ in range(3))
+    cu = [0, 37, 37, 130, 200]
+    for causal in (False, True):
+        m = fp8_attention_model(q, k, v, causal, 0.25, rotate=True, seed=4, cu_seqlens=cu)
+        assert m["sk"].shape == (1, 2, 4) and m["sv"].shape == (1, 2, 4)
+        for s in range(4):
+            a, b = cu[s], cu[s + 1]
+            if b == a:
+                continue
+            alone = fp8_attention_model(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], causal, 0.25,
+                                        rotate=True, seed=4)
+            np.testing.assert_array_equal(m["k8"][:, :, a:b], alone["k8"])
+            np.testing.assert_array_equal(m["v8"][:, :, a:b], alone["v8"])
+            np.testing.assert_array_equal(m["sk"][:, :, s], alone["sk"])
+            np.testing.assert_array_equal(m["sv"][:, :, s], alone["sv"])
+            np.testing.assert_allclose(m["o"][:, :, a:b], alone["o"], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(m["lse"][:, :, a:b], alone["lse"], rtol=0, atol=1e-13)
+    whole = fp8_attention_model(q, k, v, True, 0.25, rotate=True, seed=4, cu_seqlens=[0, 200])
+    plain = fp8_attention_model(q, k, v, True, 0.25, rotate=True, seed=4)
+    for key in ("k8", "v8", "o", "lse"):
+        np.testing.assert_array_equal(whole[key], plain[key])
+    np.testing.assert_array_equal(whole["sk"][:, :, 0], plain["sk"])
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, 37:130] *= 32
+    v2[:, :, 37:130] *= 32
+    m1 = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=4, cu_seqlens=cu)
+    m2 = fp8_attention_model(q, k2, v2, False, 0.25, rotate=True, seed=4, cu_seqlens=cu)
+    keep = np.r_[0:37, 130:200]
+    for key in ("k8", "v8", "o", "lse"):
+        np.testing.assert_array_equal(m1[key][:, :, keep], m2[key][:, :, keep])
+    assert not np.array_equal(m1["o"][:, :, 37:130], m2["o"][:, :, 37:130])
