@@ -287,6 +287,37 @@ fattn_status fattn_fwd_fp8_blocksparse(const void* q, const void* k, const void*
                                        void* workspace, size_t workspace_bytes,
                                        void* stream);
 
+/*
+ * fp8 forward over packed variable-length sequences: fattn_fwd_fp8 with the
+ * segments of fattn_fwd_varlen (cu_seqlens, nseq, max_seqlen as there; FA4
+ * gist, closing summary: varlen named among the variants the design admits;
+ * FlashAttention-3 page, innovation 3 for the fp8 operands). Each segment
+ * is a sequence of its own, also for the quantisation: K' and V get one
+ * scale per (b, h, segment) over that segment's rows, Q' one per row as
+ * always, so each segment's O and LSE are exactly those fattn_fwd_fp8 gives
+ * for that segment alone (same rotate, seed, causal, scale, exp_mode).
+ *   workspace   at least fattn_fwd_fp8_varlen_workspace_bytes(B, H, N, d,
+ *               nseq, max_seqlen) bytes, 256-byte aligned: K8 as for
+ *               fattn_fwd_fp8; V8ᵀ [B,H,d,Npad] with Npad = roundup(N, 64) +
+ *               64·nseq, segment s in the 64-key blocks from column
+ *               roundup(cu[s], 64) + 64·s on (same key order); scales
+ *               [2][B·H][nseq]; then an fp32 [2][B·H][nseq][⌈max_seqlen/128⌉]
+ *               scratch.
+ * The offsets are read on the device and clamped to [0, N], and every
+ * segment is cut to its first max_seqlen rows (the caller keeps lengths
+ * within max_seqlen; rows outside every segment, or past that cut, are not
+ * written). Additionally ENOTSUP when d·Npad ≥ 2^31 or
+ * nseq·⌈max_seqlen/64⌉ ≥ 2^31. Errors otherwise as fattn_fwd_varlen and
+ * fattn_fwd_fp8.
+ */
+size_t fattn_fwd_fp8_varlen_workspace_bytes(int B, int H, int N, int d, int nseq,
+                                            int max_seqlen);
+fattn_status fattn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int32_t* cu_seqlens, int nseq,
+                                  int max_seqlen, int B, int H, int N, int d, int causal,
+                                  float scale, int exp_mode, int rotate, uint64_t seed,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* fattn_strerror(int status);
 /* Detail of the last error on the calling thread (argument or HIP message). */

@@ -218,6 +218,41 @@ def test_fp8_blocksparse_checks():
     assert fa.lib().fattn_last_error()
 
 
+def test_fp8_varlen_workspace_and_checks():
+    lib = fa.lib()
+    B, H, N, d, nseq, maxl = 1, 2, 300, 128, 3, 200
+    need = lib.fattn_fwd_fp8_varlen_workspace_bytes(B, H, N, d, nseq, maxl)
+    # K8, V8ᵀ with 64 more columns per segment, scales and chunk partials per
+    # (head, segment), each region 256-byte aligned.
+    npad = (N + 63) // 64 * 64 + 64 * nseq
+    assert need >= B * H * N * d + B * H * d * npad + 8 * B * H * nseq + 8 * B * H * nseq * 2
+    assert need > lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
+    assert lib.fattn_fwd_fp8_varlen_workspace_bytes(B, H, N, d, 0, maxl) == 0
+
+    def call(ws, nbytes, **kw):
+        a = dict(q=P, cu=P, nseq=nseq, maxl=maxl, N=N, d=d, causal=0, exp=0, rotate=1, lse=NUL)
+        a.update(kw)
+        return lib.fattn_fwd_fp8_varlen(a["q"], P, P, P, a["lse"], a["cu"], a["nseq"], a["maxl"],
+                                        B, H, a["N"], a["d"], a["causal"], ctypes.c_float(0.1),
+                                        a["exp"], a["rotate"], ctypes.c_uint64(7), ws, nbytes,
+                                        NUL)
+    assert call(P, need, cu=NUL) == EINVAL
+    assert call(P, need, nseq=0) == EINVAL
+    assert call(P, need, maxl=0) == EINVAL
+    assert call(P, need, maxl=N + 1) == EINVAL
+    assert call(P, need, q=MIS) == EINVAL
+    assert call(P, need, lse=MIS) == EINVAL
+    assert call(P, need, d=80) == ENOTSUP
+    assert call(P, need, rotate=3) == EINVAL
+    assert call(P, need, exp=5) == EINVAL
+    assert call(P, need - 1) == EWORKSPACE
+    assert call(NUL, need) == EWORKSPACE
+    # V8ᵀ rows of d·(N + 64·nseq) bytes must stay addressable with 32 bits.
+    big = 2 ** 24
+    assert call(P, need, nseq=big // 64, maxl=1) == ENOTSUP
+    assert fa.lib().fattn_last_error()
+
+
 def test_bwd_blocksparse_checks():
     lib = fa.lib()
     B, H, N, d = 1, 2, 300, 128

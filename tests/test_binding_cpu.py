@@ -53,6 +53,10 @@ lse = t(B, H, N, dtype=torch.float32)
     (lambda: fa.fwd_fp8_blocksparse(q, q, q, t(1, 1, dtype=torch.float32)), "block_mask must be"),
     (lambda: fa.fwd_fp8_blocksparse(q, q, q, t(1, 1, dtype=torch.uint8),
                                     workspace=t(64, dtype=torch.uint8)), "at least"),
+    (lambda: fa.fwd_fp8_varlen(q, q, q, t(3, dtype=torch.int64), N), "cu_seqlens must be"),
+    (lambda: fa.fwd_fp8_varlen(q, q, q, t(1, dtype=torch.int32), N), "cu_seqlens must be"),
+    (lambda: fa.fwd_fp8_varlen(q, q, q, t(3, dtype=torch.int32), N,
+                               workspace=t(64, dtype=torch.uint8)), "at least"),
     (lambda: fa.fwd_fp8_attend(q, t(64, dtype=torch.uint8)), "at least"),
     (lambda: fa.fwd_fp8_attend(q, None), "workspace must be"),
     (lambda: fa.fwd_fp8_attend(t(B, H, N, D, dtype=torch.float32), t(10 ** 6, dtype=torch.uint8)),
@@ -71,6 +75,7 @@ def test_malformed_arguments_raise_before_any_call(call, msg):
     lambda: fa.fwd_fp8(q, q, q),
     lambda: fa.fwd_fp8_attend(q, t(10 ** 6, dtype=torch.uint8)),
     lambda: fa.fwd_fp8_blocksparse(q, q, q, t(1, 1, dtype=torch.uint8)),
+    lambda: fa.fwd_fp8_varlen(q, q, q, t(3, dtype=torch.int32), N),
 ])
 def test_well_formed_cpu_tensors_reach_the_device_check(call):
     with pytest.raises(ValueError, match="must be on a GPU device"):

@@ -12,6 +12,7 @@ an exception is raised.
     dq, dk, dv = bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen, causal=False)
     o, lse = fwd_blocksparse(q, k, v, block_mask, causal=False)
     o, lse = fwd_fp8_blocksparse(q, k, v, block_mask, causal=False, rotate=True, seed=0)
+    o, lse = fwd_fp8_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, rotate=True, seed=0)
     dq, dk, dv = bwd_blocksparse(q, k, v, o, lse, do, block_mask, causal=False)
 
 Tensors are contiguous CUDA (HIP) bfloat16 [B, H, N, d], d ∈ {64, 128};
@@ -22,8 +23,8 @@ import os
 
 from ._lib import FattnError, lib, lib_path  # noqa: F401
 
-__all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_WORKSPACE_BYTES", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "bwd_blocksparse", "fwd_fp8", "fwd_fp8_blocksparse", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
-           "fp8_workspace_bytes", "FattnError", "lib", "lib_path",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_WORKSPACE_BYTES", "fwd_varlen", "bwd_varlen", "fwd_blocksparse", "bwd_blocksparse", "fwd_fp8", "fwd_fp8_blocksparse", "fwd_fp8_varlen", "fwd_fp8_attend", "fp8_workspace_views", "bwd_workspace_bytes",
+           "fp8_workspace_bytes", "fp8_varlen_workspace_bytes", "FattnError", "lib", "lib_path",
            "EXP_AUTO", "EXP_HW", "EXP_POLY", "EXP_SPLIT"]
 
 EXP_AUTO, EXP_HW, EXP_POLY, EXP_SPLIT = 0, 1, 2, 3
@@ -341,6 +342,31 @@ def fwd_fp8_blocksparse(q, k, v, block_mask, causal=False, scale=None, rotate=Tr
                                               _EXP[exp_mode], int(bool(rotate)),
                                               ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
                                               ctypes.c_size_t(ws.numel()), _stream(q)))
+    return o, lse_t
+
+
+def fp8_varlen_workspace_bytes(B, H, N, d, nseq, max_seqlen):
+    return int(lib().fattn_fwd_fp8_varlen_workspace_bytes(B, H, N, d, nseq, max_seqlen))
+
+
+def fwd_fp8_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None, rotate=True, seed=0,
+                   want_lse=True, workspace=None, out=None, exp_mode="auto"):
+    """fwd_fp8 over packed variable-length sequences (cu_seqlens, max_seqlen
+    as for fwd_varlen); each segment is quantised and attended as a sequence
+    of its own. Returns (O, LSE or None)."""
+    B, H, N, d = _check_qkv(q, k, v)
+    nseq = _cu(cu_seqlens, q)
+    o, lse_t = _outputs(q, out, None, want_lse)
+    need = fp8_varlen_workspace_bytes(B, H, N, d, nseq, max(1, int(max_seqlen)))
+    ws = _workspace(workspace, need, q)
+    _on_device(q, ((k, "k"), (v, "v"), (o, "out"), (ws, "workspace")))
+    with _torch().cuda.device(q.device):
+        _call(lib().fattn_fwd_fp8_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t),
+                                         _ptr(cu_seqlens), nseq, int(max_seqlen), B, H, N, d,
+                                         int(bool(causal)), ctypes.c_float(_scale(scale, d)),
+                                         _EXP[exp_mode], int(bool(rotate)),
+                                         ctypes.c_uint64(seed & (2 ** 64 - 1)), _ptr(ws),
+                                         ctypes.c_size_t(ws.numel()), _stream(q)))
     return o, lse_t
 
 

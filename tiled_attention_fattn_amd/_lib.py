@@ -27,6 +27,9 @@ PROTOTYPES = {
     "fattn_fwd_fp8_blocksparse": (c_int, [c_void_p] * 6 + [c_int] * 6
                                   + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t,
                                      c_void_p]),
+    "fattn_fwd_fp8_varlen_workspace_bytes": (c_size_t, [c_int] * 6),
+    "fattn_fwd_fp8_varlen": (c_int, [c_void_p] * 6 + [c_int] * 7
+                             + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t, c_void_p]),
     "fattn_fwd_fp8_attend": (c_int, [c_void_p] * 3 + [c_int] * 5
                              + [c_float, c_int, c_int, c_uint64, c_void_p, c_size_t, c_void_p]),
     "fattn_strerror": (ctypes.c_char_p, [c_int]),

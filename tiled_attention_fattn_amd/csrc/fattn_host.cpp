@@ -87,16 +87,21 @@ struct Fp8Layout {
   size_t k8, v8t, scales, partial, total;
 };
 
-Fp8Layout fp8_layout(int B, int H, int N, int d) {
+// nseq = 0: no packed segments (one per head, all N rows). With segments
+// V8ᵀ has 64 more columns per segment, scales and partials one set per
+// (head, segment), and the partials cover max_seqlen rows.
+Fp8Layout fp8_layout(int B, int H, int N, int d, int nseq = 0, int max_seqlen = 0) {
   const size_t bh = (size_t)B * H;
-  const size_t npad = round_up((size_t)N, fattn::kFp8Npad);
+  const size_t units = bh * (nseq > 0 ? nseq : 1);
+  const size_t npad = round_up((size_t)N, fattn::kFp8Npad) + (size_t)fattn::kFp8Npad * nseq;
+  const size_t rows = nseq > 0 ? (size_t)max_seqlen : (size_t)N;
   Fp8Layout L;
   L.k8 = 0;
   L.v8t = round_up(L.k8 + bh * N * d, 256);
   L.scales = round_up(L.v8t + bh * d * npad, 256);
-  const size_t nchunks = (N + fattn::kFp8AmaxRows - 1) / fattn::kFp8AmaxRows;
-  L.partial = round_up(L.scales + 2 * bh * sizeof(float), 256);
-  L.total = round_up(L.partial + 2 * bh * nchunks * sizeof(float), 256);
+  const size_t nchunks = (rows + fattn::kFp8AmaxRows - 1) / fattn::kFp8AmaxRows;
+  L.partial = round_up(L.scales + 2 * units * sizeof(float), 256);
+  L.total = round_up(L.partial + 2 * units * nchunks * sizeof(float), 256);
   return L;
 }
 
@@ -333,11 +338,13 @@ fattn_status fattn_fwd_fp8_workspace_layout(int B, int H, int N, int d, size_t* 
   return FATTN_OK;
 }
 
-// fattn_fwd_fp8 and fattn_fwd_fp8_blocksparse: one validation and launch path
-// (block_mask NULL for dense attention).
+// fattn_fwd_fp8, fattn_fwd_fp8_blocksparse and fattn_fwd_fp8_varlen: one
+// validation and launch path (block_mask and cu_seqlens NULL for dense
+// attention; the callers set at most one of them).
 static fattn_status fwd_fp8_impl(const char* name, const void* q, const void* k, const void* v,
                                  void* o, float* lse, const uint8_t* block_mask, int per_head,
-                                 int B, int H, int N, int d, int causal, float scale, int exp_mode,
+                                 const int32_t* cu_seqlens, int nseq, int max_seqlen, int B,
+                                 int H, int N, int d, int causal, float scale, int exp_mode,
                                  int rotate, uint64_t seed, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   FATTN_TRY(check_ptr(q, "q"));
@@ -356,9 +363,22 @@ static fattn_status fwd_fp8_impl(const char* name, const void* q, const void* k,
     if (N > 32768)
       return fail(FATTN_ENOTSUP, "block-sparse forward supports N <= 32768 (got %d)", N);
   }
+  const bool varlen = cu_seqlens != nullptr;
+  if (varlen) {
+    FATTN_TRY(check_varlen(cu_seqlens, nseq, max_seqlen, B, H, N));
+    // V8ᵀ rows of d·(roundup(N, 64) + 64·nseq) bytes per head, addressed
+    // with 32-bit offsets; 64-key blocks per segment in one grid dimension.
+    const unsigned long long vcols =
+        (unsigned long long)round_up((size_t)N, fattn::kFp8Npad) + 64ull * nseq;
+    if ((unsigned long long)d * vcols >= (1ull << 31))
+      return fail(FATTN_ENOTSUP, "d*(N+64*nseq) = %llu bytes of V8 per head exceed 2^31-1",
+                  (unsigned long long)d * vcols);
+    if ((unsigned long long)nseq * ((max_seqlen + 63) / 64) >= (1ull << 31))
+      return fail(FATTN_ENOTSUP, "nseq*ceil(max_seqlen/64) exceeds 2^31-1");
+  }
   if (workspace == nullptr) return fail(FATTN_EWORKSPACE, "workspace is NULL");
   if (!aligned256(workspace)) return fail(FATTN_EWORKSPACE, "workspace is not 256-byte aligned");
-  const Fp8Layout L = fp8_layout(B, H, N, d);
+  const Fp8Layout L = varlen ? fp8_layout(B, H, N, d, nseq, max_seqlen) : fp8_layout(B, H, N, d);
   if (workspace_bytes < L.total)
     return fail(FATTN_EWORKSPACE, "workspace of %zu bytes, %zu required", workspace_bytes, L.total);
   FATTN_TRY(check_device());
@@ -368,15 +388,16 @@ static fattn_status fwd_fp8_impl(const char* name, const void* q, const void* k,
                                           (float*)(ws + L.partial), B, H, N, d, causal != 0, scale,
                                           exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode,
                                           rotate != 0, seed, block_mask, per_head != 0,
-                                          (hipStream_t)stream),
+                                          cu_seqlens, nseq, max_seqlen, (hipStream_t)stream),
                     name);
 }
 
 fattn_status fattn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                            int H, int N, int d, int causal, float scale, int exp_mode, int rotate,
                            uint64_t seed, void* workspace, size_t workspace_bytes, void* stream) {
-  return fwd_fp8_impl("fattn_fwd_fp8 launch", q, k, v, o, lse, nullptr, 0, B, H, N, d, causal,
-                      scale, exp_mode, rotate, seed, workspace, workspace_bytes, stream);
+  return fwd_fp8_impl("fattn_fwd_fp8 launch", q, k, v, o, lse, nullptr, 0, nullptr, 0, 0, B, H,
+                      N, d, causal, scale, exp_mode, rotate, seed, workspace, workspace_bytes,
+                      stream);
 }
 
 fattn_status fattn_fwd_fp8_blocksparse(const void* q, const void* k, const void* v, void* o,
@@ -385,9 +406,26 @@ fattn_status fattn_fwd_fp8_blocksparse(const void* q, const void* k, const void*
                                        int rotate, uint64_t seed, void* workspace,
                                        size_t workspace_bytes, void* stream) {
   if (block_mask == nullptr) return fail(FATTN_EINVAL, "block_mask is NULL");
-  return fwd_fp8_impl("fattn_fwd_fp8_blocksparse launch", q, k, v, o, lse, block_mask, per_head, B,
-                      H, N, d, causal, scale, exp_mode, rotate, seed, workspace, workspace_bytes,
-                      stream);
+  return fwd_fp8_impl("fattn_fwd_fp8_blocksparse launch", q, k, v, o, lse, block_mask, per_head,
+                      nullptr, 0, 0, B, H, N, d, causal, scale, exp_mode, rotate, seed, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t fattn_fwd_fp8_varlen_workspace_bytes(int B, int H, int N, int d, int nseq,
+                                            int max_seqlen) {
+  if (B < 1 || H < 1 || N < 1 || d < 1 || nseq < 1 || max_seqlen < 1) return 0;
+  return fp8_layout(B, H, N, d, nseq, max_seqlen).total;
+}
+
+fattn_status fattn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const int32_t* cu_seqlens, int nseq,
+                                  int max_seqlen, int B, int H, int N, int d, int causal,
+                                  float scale, int exp_mode, int rotate, uint64_t seed,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (cu_seqlens == nullptr) return fail(FATTN_EINVAL, "cu_seqlens is NULL");
+  return fwd_fp8_impl("fattn_fwd_fp8_varlen launch", q, k, v, o, lse, nullptr, 0, cu_seqlens,
+                      nseq, max_seqlen, B, H, N, d, causal, scale, exp_mode, rotate, seed,
+                      workspace, workspace_bytes, stream);
 }
 
 fattn_status fattn_fwd_fp8_attend(const void* q, void* o, float* lse, int B, int H, int N, int d,

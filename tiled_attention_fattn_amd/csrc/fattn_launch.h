@@ -53,11 +53,15 @@ constexpr int kBwdRowPad = 64;
 // rotated and quantised (one scale per row) inside the attention kernel.
 // block_mask: optional uint8 mask over 128×128 blocks ([nb][nb], or
 // [B·H][nb][nb] when per_head), as for launch_fwd_bf16_blocksparse.
+// cu_seqlens: optional packed segments (nseq, max_seqlen), as for
+// launch_fwd_bf16_varlen; then the workspace holds V8ᵀ with
+// roundup(N, 64) + 64·nseq columns per head, scales [2][B·H][nseq] and
+// partial [2][B·H][nseq][ceil(max_seqlen/128)]. Not both.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                           uint8_t* k8, uint8_t* v8t, float* scales, float* partial, int B, int H,
                           int N, int d, bool causal, float scale, int exp_mode, bool rotate,
                           uint64_t seed, const uint8_t* block_mask, bool per_head,
-                          hipStream_t stream);
+                          const int* cu_seqlens, int nseq, int max_seqlen, hipStream_t stream);
 
 // fp8 attention only (the last launch of launch_fwd_fp8) on the K/V operands
 // a previous launch_fwd_fp8 of the same shape left in k8/v8t/scales; Q is

@@ -56,6 +56,31 @@ __device__ __forceinline__ float rotation_sign(uint64_t seed, int i) {
   return (z >> 63) ? -1.0f : 1.0f;
 }
 
+// Packed variable-length sequences: rows [cu[s], cu[s+1]) of every head
+// form segment s, a sequence of its own with its own K'/V scales. Without
+// segments (cu = nullptr) the whole head is segment 0 (nseq = 1). Offsets are
+// clamped to [0, N] and lengths to max_len, so no contents of cu address
+// outside the tensors. A segment's V8ᵀ columns start at the 64-aligned
+// column roundup64(row0) + 64·s, which leaves every segment its own whole
+// 64-key blocks inside [0, roundup64(N) + 64·nseq).
+struct Fp8Segs {
+  const int* cu = nullptr;
+  int nseq = 1;
+  int max_len = 0;  // N without segments
+};
+__device__ __forceinline__ void seg_rows(const Fp8Segs& sg, int N, int s, int& row0, int& L) {
+  if (sg.cu == nullptr) {
+    row0 = 0;
+    L = N;
+    return;
+  }
+  row0 = min(max(sg.cu[s], 0), N);
+  L = min(min(max(sg.cu[s + 1], row0), N) - row0, sg.max_len);
+}
+__device__ __forceinline__ int seg_vcol(const Fp8Segs& sg, int s, int row0) {
+  return sg.cu == nullptr ? 0 : ((row0 + 63) & ~63) + 64 * s;
+}
+
 // Row-wise work of the prep kernels: a row of D elements is held by
 // kLpr = D/32 consecutive lanes (a quad for D = 128), kEpl = 32 consecutive
 // elements each (element index = lane_in_row·32 + e).
@@ -126,19 +151,25 @@ __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, i
   return ok;
 }
 
-// grid (row chunks, BH, 2 tensors): block max of |x| over kFp8AmaxRows rows.
-// Tensor t = 0 is K·R, t = 1 is V; they are taken in the order V, K
-// (blockIdx.z = 0, 1), so that K, which the quantisation kernel reads next,
-// holds the most recently read lines in the last-level cache.
+// grid (segments × row chunks, BH, 2 tensors): block max of |x| over
+// kFp8AmaxRows rows of one segment. Tensor t = 0 is K·R, t = 1 is V; they are
+// taken in the order V, K (blockIdx.z = 0, 1), so that K, which the
+// quantisation kernel reads next, holds the most recently read lines in the
+// last-level cache. partial: [2][BH][nseq][nchunks] (0 for a chunk past its
+// segment's end).
 template <int D>
 __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ K,
                                                       const bf16* __restrict__ V,
                                                       float* __restrict__ partial, int N, int BH,
-                                                      int rotate, uint64_t seed) {
+                                                      int rotate, uint64_t seed, Fp8Segs sg,
+                                                      int nchunks) {
   constexpr int LPR = D / kEpl, RPB = 256 / LPR;
   __shared__ float sgn[D];
   __shared__ float wmax[4];
-  const int t = 1 - (int)blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
+  const int t = 1 - (int)blockIdx.z, bh = blockIdx.y;
+  const int seg = (int)blockIdx.x / nchunks, chunk = (int)blockIdx.x - seg * nchunks;
+  int row0, L;
+  seg_rows(sg, N, seg, row0, L);
   const bool rot = rotate && t == 0;
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
   __syncthreads();
@@ -147,8 +178,8 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ 
   float m = 0.0f;
   // kRowSets row-sets per step so that that many loads per thread are in
   // flight together.
-  const int r_end = min(N, (chunk + 1) * kFp8AmaxRows);
-  for (int r0 = chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
+  const int r_end = row0 + min(L, (chunk + 1) * kFp8AmaxRows);
+  for (int r0 = row0 + chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
     float x[kRowSets][kEpl];
 #pragma unroll
     for (int u = 0; u < kRowSets; ++u)
@@ -162,11 +193,9 @@ __global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ 
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int nchunks = gridDim.x;
-    partial[((size_t)t * BH + bh) * nchunks + chunk] =
+  if (threadIdx.x == 0)
+    partial[(((size_t)t * BH + bh) * sg.nseq + seg) * nchunks + chunk] =
         fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  }
 }
 
 // amax of one (tensor, head) from its chunk partials, reduced by wave 0 and
@@ -218,29 +247,34 @@ __device__ __forceinline__ float ratio448(float x, const Ratio448& r) {
   return fmaf(e, r.inv, q0);
 }
 
-// grid (row chunks, BH): K·R quantised with the head's scale, kFp8AmaxRows
-// rows per block.
+// grid (segments × row chunks, BH): K·R quantised with its segment's scale
+// (the head's without segments), kFp8AmaxRows rows per block; scales[0] is
+// [BH][nseq].
 template <int D>
 __global__ __launch_bounds__(256) void fp8_quant_k_kernel(const bf16* __restrict__ K,
                                                          uint8_t* __restrict__ k8,
                                                          const float* __restrict__ partial,
                                                          float* __restrict__ scales, int N,
-                                                         int rotate, uint64_t seed) {
+                                                         int rotate, uint64_t seed, Fp8Segs sg,
+                                                         int nchunks) {
   constexpr int LPR = D / kEpl, RPB = 256 / LPR;
   __shared__ float sgn[D];
   __shared__ float am_slot;
-  const int bh = blockIdx.y, chunk = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int seg = (int)blockIdx.x / nchunks, chunk = (int)blockIdx.x - seg * nchunks;
+  int row0, L;
+  seg_rows(sg, N, seg, row0, L);
   if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
-  const int nchunks = gridDim.x;
-  const float am = head_amax(partial + (size_t)bh * nchunks, nchunks, &am_slot);
+  const int unit = bh * sg.nseq + seg;
+  const float am = head_amax(partial + (size_t)unit * nchunks, nchunks, &am_slot);
   const Ratio448 rk(am);
   const size_t head = (size_t)bh * N * D;
   const bf16* src = K + head;
   uint8_t* dst = k8 + head;
-  if (chunk == 0 && threadIdx.x == 0) scales[bh] = scale_from_amax(am);
+  if (chunk == 0 && threadIdx.x == 0) scales[unit] = scale_from_amax(am);
   const int part = threadIdx.x % LPR;
-  const int r_end = min(N, (chunk + 1) * kFp8AmaxRows);
-  for (int r0 = chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
+  const int r_end = row0 + min(L, (chunk + 1) * kFp8AmaxRows);
+  for (int r0 = row0 + chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
     float xs[kRowSets][kEpl];
     bool ok[kRowSets];
 #pragma unroll
@@ -276,25 +310,35 @@ __device__ __forceinline__ int v8_pos(int r) {
   return 32 * ((r >> 2) & 1) + s;
 }
 
-// grid (Npad/64, BH): one 64-key block of one head. Thread (m, cc) reads the
-// 8 values of d-chunk cc of keys 4m .. 4m+3 and writes, for each of those 8
-// d, the 4 codes of the 4 keys as one 4-byte word: the four keys are
-// adjacent in the P-operand key order (v8_pos), and the 16 threads of one
-// chunk fill 64 contiguous bytes of each V8ᵀ row. Keys past N give code 0.
+// grid (segments × 64-key blocks, BH): one 64-key block of one segment of
+// one head. Thread (m, cc) reads the 8 values of d-chunk cc of keys
+// 4m .. 4m+3 and writes, for each of those 8 d, the 4 codes of the 4 keys as
+// one 4-byte word: the four keys are adjacent in the P-operand key order
+// (v8_pos), and the 16 threads of one chunk fill 64 contiguous bytes of each
+// V8ᵀ row. Keys past the segment's end give code 0; blocks past it write
+// nothing. scales[1] is [BH][nseq].
 template <int D>
 __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict__ V,
                                                          uint8_t* __restrict__ v8t,
                                                          const float* __restrict__ partial,
                                                          float* __restrict__ scales, int N,
-                                                         int Npad, int BH, int nchunks) {
+                                                         int Npad, int BH, int nchunks,
+                                                         Fp8Segs sg, int nvblocks) {
   constexpr int CHUNKS = D / 8;
-  const int bh = blockIdx.y, kb = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int seg = (int)blockIdx.x / nvblocks, kb = (int)blockIdx.x - seg * nvblocks;
+  int row0, L;
+  seg_rows(sg, N, seg, row0, L);
+  if (kb > 0 && 64 * kb >= L) return;  // whole block (block 0 still writes the scale)
   __shared__ float am_slot;
-  const float am = head_amax(partial + ((size_t)BH + bh) * nchunks, nchunks, &am_slot);
+  const int unit = bh * sg.nseq + seg;
+  const float am =
+      head_amax(partial + ((size_t)BH * sg.nseq + unit) * nchunks, nchunks, &am_slot);
   const Ratio448 rv(am);
-  if (kb == 0 && threadIdx.x == 0) scales[BH + bh] = scale_from_amax(am);
-  const bf16* src = V + (size_t)bh * N * D;
-  uint8_t* dst = v8t + (size_t)bh * D * Npad + (size_t)kb * 64;
+  if (kb == 0 && threadIdx.x == 0) scales[(size_t)BH * sg.nseq + unit] = scale_from_amax(am);
+  if (64 * kb >= L) return;  // an empty segment: its scale only
+  const bf16* src = V + ((size_t)bh * N + row0) * D;
+  uint8_t* dst = v8t + (size_t)bh * D * Npad + seg_vcol(sg, seg, row0) + (size_t)kb * 64;
   for (int ch = threadIdx.x; ch < 16 * CHUNKS; ch += 256) {
     const int m = ch % 16, cc = ch / 16;
     float x[4][8];
@@ -302,7 +346,7 @@ __global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict
     for (int u = 0; u < 4; ++u) {
       const int key = kb * 64 + 4 * m + u;
       bf16x8 v = {};
-      if (key < N) v = *(const bf16x8*)(src + (size_t)key * D + cc * 8);
+      if (key < L) v = *(const bf16x8*)(src + (size_t)key * D + cc * 8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float a = (float)v[e];
@@ -332,14 +376,18 @@ constexpr int kF8BN = 64;
 // shared): the workgroup (one 128-query block) reads its mask row once and
 // walks only the visible 64-key tiles with the same schedule; a row that
 // sees no key writes O = 0 (and LSE = −∞).
-template <int D, bool CAUSAL, bool WANT_LSE, int EXPM, bool SPARSE>
+// VARLEN: packed segments (sg); the grid runs over (head, segment, query
+// tile) and each workgroup treats its segment as a sequence of its own
+// (rows offset to the segment start, its own K'/V scales and V8ᵀ columns).
+template <int D, bool CAUSAL, bool WANT_LSE, int EXPM, bool SPARSE, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
                     const uint8_t* __restrict__ v8t, const float* __restrict__ scales,
                     bf16* __restrict__ O, float* __restrict__ LSE, int N, int Npad, int BH,
                     int n_qtiles, float scale_log2, int rotate, uint64_t seed,
-                    const uint8_t* __restrict__ bmask, long mask_stride) {
+                    const uint8_t* __restrict__ bmask, long mask_stride, Fp8Segs sg) {
   static_assert(!SPARSE || kF8BM == kMaskBlockRows, "one query tile per mask block row");
+  static_assert(!(SPARSE && VARLEN), "block masks apply to whole sequences");
   constexpr int KD = D / 64;           // fp8 MFMA k-steps over d
   constexpr int KTILE = kF8BN * D;     // K8 tile [64 keys][D bytes]
   constexpr int VTILE = D * kF8BN;     // V8ᵀ tile [D][64 keys]
@@ -356,29 +404,46 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c = lane & 31;
 
-  // Workgroup → (head, query tile). Causal: tile-major from the last query
-  // tile down, heaviest first over the whole grid (ids round-robin over the
-  // XCDs). Otherwise each XCD gets a contiguous run of tiles (one head's
-  // tiles share its L2).
-  int bh, qt;
+  // Workgroup → (unit, query tile), a unit being a head or (head, segment).
+  // Causal: tile-major from the last query tile down, heaviest first over
+  // the whole grid (ids round-robin over the XCDs). Packed segments without
+  // the mask: longest segment first (rank r takes the r-th longest), heads
+  // interleaved within a rank. Otherwise each XCD gets a contiguous run of
+  // tiles (one head's tiles share its L2).
+  int unit, qt;
   if constexpr (CAUSAL) {
-    const int step = (int)(blockIdx.x / BH);
-    bh = blockIdx.x - step * BH;
+    const int units = BH * sg.nseq;
+    const int step = (int)(blockIdx.x / units);
+    unit = blockIdx.x - step * units;
     qt = n_qtiles - 1 - step;
+  } else if constexpr (VARLEN) {
+    const int per_rank = BH * n_qtiles;
+    const int r = (int)(blockIdx.x / per_rank);
+    const int rem = blockIdx.x - r * per_rank;
+    qt = rem / BH;
+    const int b = rem - qt * BH;
+    unit = b * sg.nseq + segment_of_rank(sg.cu, sg.nseq, N, r, lane);
   } else {
     const int total = n_qtiles * BH;
     int logical = blockIdx.x;
     if ((total & 7) == 0) logical = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-    bh = logical / n_qtiles;
-    qt = logical - bh * n_qtiles;
+    unit = logical / n_qtiles;
+    qt = logical - unit * n_qtiles;
   }
-
-  const float sk = scales[bh], sv = scales[BH + bh];
-
-  const size_t head = (size_t)bh * N * D;
-  const uint8_t* Kh = k8 + head;
-  const uint8_t* Vt = v8t + (size_t)bh * D * Npad;
+  const int bh = VARLEN ? unit / sg.nseq : unit;
+  const int seg = unit - bh * sg.nseq;
+  // Rows [row0, row0 + L) of the head: the whole head, or one segment.
+  int row0 = 0, L = N;
+  if constexpr (VARLEN) seg_rows(sg, N, seg, row0, L);
   const int q_start = qt * kF8BM;
+  if (q_start >= L) return;  // whole workgroup: a segment shorter than the grid's longest
+
+  const float sk = scales[unit], sv = scales[BH * sg.nseq + unit];
+
+  const size_t head = ((size_t)bh * N + row0) * D;
+  const uint8_t* Kh = k8 + head;
+  const int vcol = VARLEN ? seg_vcol(sg, seg, row0) : 0;
+  const uint8_t* Vt = v8t + (size_t)bh * D * Npad + vcol;
   const int q0 = q_start + wave * 32;
   const int qi = q0 + c;
   // Q' operands (two e4m3 terms) and the exp2-domain score factor of this
@@ -397,9 +462,9 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
 #pragma unroll
   for (int u = 0; u < 2; ++u) voff[u] = tile_off_rb<64>(c, 2 * h + u);
 
-  const int kv_end = CAUSAL ? min(N, q_start + kF8BM) : N;
+  const int kv_end = CAUSAL ? min(L, q_start + kF8BM) : L;
   const int n_kv = (kv_end + kF8BN - 1) / kF8BN;
-  const int first_masked = CAUSAL ? min(q_start / kF8BN, N / kF8BN) : N / kF8BN;
+  const int first_masked = CAUSAL ? min(q_start / kF8BN, L / kF8BN) : L / kF8BN;
 
   // Wave loads of the tiles (swizzle applied on the source side). K8 rows
   // past N read as zero (buffer range check); V8ᵀ is zero-padded to Npad.
@@ -416,11 +481,11 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   }
   auto gload_k = [&](char* tile, int j) __device__ {
     const int key0 = j * kF8BN;
-    buffer_to_lds<KLOADS>(Kh + (size_t)key0 * D, (N - key0) * D, tile, ldk, wave * KLOADS);
+    buffer_to_lds<KLOADS>(Kh + (size_t)key0 * D, (L - key0) * D, tile, ldk, wave * KLOADS);
   };
   auto gload_v = [&](char* tile, int j) __device__ {
     const int key0 = j * kF8BN;
-    buffer_to_lds<VLOADS>(Vt + key0, D * Npad - key0, tile, ldv, wave * VLOADS);
+    buffer_to_lds<VLOADS>(Vt + key0, D * Npad - vcol - key0, tile, ldv, wave * VLOADS);
   };
 
   f32x16 oacc[DT];
@@ -457,7 +522,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 32 * t + acc_row(r, h);
-        if (key >= N || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
+        if (key >= L || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
       }
   };
   auto tile_max = [&](const f32x16 (&s)[2]) {
@@ -483,14 +548,14 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   };
   const int c0 = next_tile(0), c1 = next_tile(c0 + 1);
   if (c0 >= n_kv) {  // no visible key for any row of the block: O = 0, LSE = −∞
-    if (qi < N) {
+    if (qi < L) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *(i32x2*)(O + head + (size_t)qi * D + 32 * dt + 8 * g + 4 * h) = i32x2{};
       if constexpr (WANT_LSE) {
-        if (h == 0) LSE[(size_t)bh * N + qi] = -INFINITY;
+        if (h == 0) LSE[(size_t)bh * N + row0 + qi] = -INFINITY;
       }
     }
     return;
@@ -517,7 +582,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 v = qi < N ? *(const bf16x8*)(Qrow + 64 * kk + 8 * u) : bf16x8{};
+        const bf16x8 v = qi < L ? *(const bf16x8*)(Qrow + 64 * kk + 8 * u) : bf16x8{};
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[kk][8 * u + e] = (float)v[e];
       }
@@ -695,7 +760,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   }
 
   const float inv = sv / lacc[0];
-  if (qi < N) {
+  if (qi < L) {
     bf16* Orow = O + head + (size_t)qi * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -708,7 +773,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
       }
     if constexpr (WANT_LSE) {
       const float l = half_sum(l_part);
-      if (h == 0) LSE[(size_t)bh * N + qi] = (m_c + __builtin_log2f(l) - kF8PExp) * kLn2;
+      if (h == 0) LSE[(size_t)bh * N + row0 + qi] = (m_c + __builtin_log2f(l) - kF8PExp) * kLn2;
     }
   }
 }
@@ -727,29 +792,40 @@ struct Fp8Attend {
   uint64_t seed;
   const uint8_t* bmask = nullptr;  // block mask (SPARSE launches)
   long mask_stride = 0;            // elements between the masks of consecutive heads (0: shared)
+  Fp8Segs sg{};                    // packed segments (VARLEN launches: sg.cu set)
 };
 
-template <int D, bool CAUSAL, int EXPM, bool SPARSE>
+// Columns of one head's V8ᵀ: N rounded up to 64, plus 64 per segment with
+// packed segments (each starts on its own 64-key block).
+static int fp8_vcols(int N, const Fp8Segs& sg) {
+  const int npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
+  return sg.cu != nullptr ? npad + kFp8Npad * sg.nseq : npad;
+}
+
+template <int D, bool CAUSAL, int EXPM, bool SPARSE, bool VARLEN>
 static hipError_t launch_attend_s(const Fp8Attend& a, hipStream_t stream) {
-  const int Npad = (a.N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
-  const int n_qtiles = (a.N + kF8BM - 1) / kF8BM;
+  const int Npad = fp8_vcols(a.N, a.sg);
+  const int rows = VARLEN ? a.sg.max_len : a.N;
+  const int n_qtiles = (rows + kF8BM - 1) / kF8BM;
+  const dim3 grid((unsigned)n_qtiles * a.BH * a.sg.nseq);
   if (a.lse != nullptr)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, EXPM, SPARSE>), dim3(n_qtiles * a.BH),
-                       dim3(256), 0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad,
-                       a.BH, n_qtiles, a.scale * kLog2e, a.rotate, a.seed, a.bmask,
-                       a.mask_stride);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, true, EXPM, SPARSE, VARLEN>), grid, dim3(256),
+                       0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad, a.BH,
+                       n_qtiles, a.scale * kLog2e, a.rotate, a.seed, a.bmask, a.mask_stride,
+                       a.sg);
   else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, EXPM, SPARSE>), dim3(n_qtiles * a.BH),
-                       dim3(256), 0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad,
-                       a.BH, n_qtiles, a.scale * kLog2e, a.rotate, a.seed, a.bmask,
-                       a.mask_stride);
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, false, EXPM, SPARSE, VARLEN>), grid, dim3(256),
+                       0, stream, a.q, a.k8, a.v8t, a.scales, a.o, a.lse, a.N, Npad, a.BH,
+                       n_qtiles, a.scale * kLog2e, a.rotate, a.seed, a.bmask, a.mask_stride,
+                       a.sg);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, int EXPM>
 static hipError_t launch_attend_m(const Fp8Attend& a, hipStream_t stream) {
-  return a.bmask != nullptr ? launch_attend_s<D, CAUSAL, EXPM, true>(a, stream)
-                            : launch_attend_s<D, CAUSAL, EXPM, false>(a, stream);
+  if (a.sg.cu != nullptr) return launch_attend_s<D, CAUSAL, EXPM, false, true>(a, stream);
+  return a.bmask != nullptr ? launch_attend_s<D, CAUSAL, EXPM, true, false>(a, stream)
+                            : launch_attend_s<D, CAUSAL, EXPM, false, false>(a, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -771,28 +847,41 @@ static hipError_t launch_attend(const Fp8Attend& a, int d, bool causal, int exp_
 template <int D>
 static void launch_prep(const void* k, const void* v, uint8_t* k8, uint8_t* v8t, float* scales,
                         float* partial, int BH, int N, bool rotate, uint64_t seed,
-                        hipStream_t stream) {
-  const int Npad = (N + kFp8Npad - 1) / kFp8Npad * kFp8Npad;
-  const unsigned nchunks = (unsigned)((N + kFp8AmaxRows - 1) / kFp8AmaxRows);
-  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(nchunks, BH, 2), dim3(256), 0, stream,
-                     (const bf16*)k, (const bf16*)v, partial, N, BH, (int)rotate, seed);
-  hipLaunchKernelGGL((fp8_quant_k_kernel<D>), dim3(nchunks, BH), dim3(256), 0, stream,
-                     (const bf16*)k, k8, (const float*)partial, scales, N, (int)rotate, seed);
-  hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(Npad / 64, BH), dim3(256), 0, stream,
-                     (const bf16*)v, v8t, (const float*)partial, scales, N, Npad, BH, (int)nchunks);
+                        const Fp8Segs& sg, hipStream_t stream) {
+  const int Npad = fp8_vcols(N, sg);
+  const unsigned nchunks = (unsigned)((sg.max_len + kFp8AmaxRows - 1) / kFp8AmaxRows);
+  const unsigned nvblocks = (unsigned)((sg.max_len + 63) / 64);
+  const unsigned nseq = (unsigned)sg.nseq;
+  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(nseq * nchunks, BH, 2), dim3(256), 0, stream,
+                     (const bf16*)k, (const bf16*)v, partial, N, BH, (int)rotate, seed, sg,
+                     (int)nchunks);
+  hipLaunchKernelGGL((fp8_quant_k_kernel<D>), dim3(nseq * nchunks, BH), dim3(256), 0, stream,
+                     (const bf16*)k, k8, (const float*)partial, scales, N, (int)rotate, seed, sg,
+                     (int)nchunks);
+  hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(nseq * nvblocks, BH), dim3(256), 0, stream,
+                     (const bf16*)v, v8t, (const float*)partial, scales, N, Npad, BH,
+                     (int)nchunks, sg, (int)nvblocks);
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                           uint8_t* k8, uint8_t* v8t, float* scales, float* partial, int B, int H,
                           int N, int d, bool causal, float scale, int exp_mode, bool rotate,
                           uint64_t seed, const uint8_t* block_mask, bool per_head,
-                          hipStream_t stream) {
+                          const int* cu_seqlens, int nseq, int max_seqlen, hipStream_t stream) {
   const int BH = B * H;
-  if (d == 64) launch_prep<64>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, stream);
-  else launch_prep<128>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, stream);
+  Fp8Segs sg;
+  sg.max_len = N;
+  if (cu_seqlens != nullptr) {
+    sg.cu = cu_seqlens;
+    sg.nseq = nseq;
+    sg.max_len = max_seqlen;
+  }
+  if (d == 64) launch_prep<64>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, sg, stream);
+  else launch_prep<128>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, sg, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, BH, N, scale, (int)rotate, seed};
+  a.sg = sg;
   if (block_mask != nullptr) {
     const long nb = (N + kMaskBlockRows - 1) / kMaskBlockRows;
     a.bmask = block_mask;
@@ -805,8 +894,8 @@ hipError_t launch_fwd_fp8_attend(const void* q, void* o, float* lse, const uint8
                                  const uint8_t* v8t, const float* scales, int B, int H, int N,
                                  int d, bool causal, float scale, int exp_mode, bool rotate,
                                  uint64_t seed, hipStream_t stream) {
-  const Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, B * H, N, scale, (int)rotate,
-                    seed};
+  Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, B * H, N, scale, (int)rotate, seed};
+  a.sg.max_len = N;
   return launch_attend(a, d, causal, exp_mode, stream);
 }
 
