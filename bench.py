@@ -232,7 +232,7 @@ def cpu_baseline(parts, heads):
 
 
 SWEEP_TOKENS = 262144   # B·H·N per point (that of the B=2 H=16 N=8192 forward)
-SWEEP_N = (4096, 8192, 16384, 32768)
+SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768)
 
 
 def sweep(args):
@@ -341,6 +341,21 @@ def sweep(args):
                    "segments": len(lengths), "max_seqlen": maxl, "ms": round(ms, 4),
                    "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                    "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16, 4)})
+    del grads, ws
+    # The fp8 forward over the same packing (whole call: per-segment K/V
+    # quantisation, then attention).
+    ws8 = torch.empty(fa.fp8_varlen_workspace_bytes(1, H, N, d, len(lengths), maxl),
+                      dtype=torch.uint8, device="cuda")
+    for causal in (False, True):
+        ms = timed(lambda: fa.fwd_fp8_varlen(q, k, v, cu, maxl, causal=causal, scale=scale,
+                                             rotate=True, seed=5, want_lse=False, workspace=ws8,
+                                             out=o))
+        fl = sum(flops_fwd(1, H, n, d, causal) for n in lengths)
+        points.append({"part": "fp8_varlen", "causal": causal, "B": 1, "H": H, "N": N, "d": d,
+                       "segments": len(lengths), "max_seqlen": maxl, "ms": round(ms, 4),
+                       "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                       "frac_of_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP8, 4)})
+    del ws8
     print(f"[sweep] varlen done ({len(lengths)} segments, max {maxl})", file=sys.stderr,
           flush=True)
 
@@ -354,6 +369,7 @@ def sweep(args):
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     grads = tuple(torch.empty_like(q) for _ in range(3))
     ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    ws8 = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
     nb = N // 128
     scale = d ** -0.5
     for dens in (1.0, 0.5, 0.25, 0.1):
@@ -364,12 +380,17 @@ def sweep(args):
         ms_f = timed(lambda: fa.fwd_blocksparse(q, k, v, mt, scale=scale, out=o, lse=lse))
         ms_b = timed(lambda: fa.bwd_blocksparse(q, k, v, o, lse, do, mt, scale=scale,
                                                 workspace=ws, out=grads))
-        for part, ms, fl in (("fwd_blocksparse", ms_f, 4 * d * vis),
-                             ("bwd_blocksparse", ms_b, 10 * d * vis)):
+        # fp8 whole call (quantisation over all keys, attention over the
+        # visible blocks).
+        ms_8 = timed(lambda: fa.fwd_fp8_blocksparse(q, k, v, mt, scale=scale, rotate=True, seed=5,
+                                                    want_lse=False, workspace=ws8, out=o))
+        for part, ms, fl, peak in (("fwd_blocksparse", ms_f, 4 * d * vis, PEAK_BF16),
+                                   ("bwd_blocksparse", ms_b, 10 * d * vis, PEAK_BF16),
+                                   ("fp8_blocksparse", ms_8, 4 * d * vis, PEAK_FP8)):
             tf = fl / (ms * 1e-3) / 1e12
             points.append({"part": part, "causal": False, "B": B, "H": H, "N": N, "d": d,
                            "density": round(float(m.mean()), 4), "ms": round(ms, 4),
-                           "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16, 4)})
+                           "tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4)})
     print("[sweep] block masks done", file=sys.stderr, flush=True)
 
     print(json.dumps({"sweep": "tokens per point B*H*N = %d, B = 1" % SWEEP_TOKENS,
