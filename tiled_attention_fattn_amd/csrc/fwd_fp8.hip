@@ -216,7 +216,10 @@ __device__ __forceinline__ float scale_from_amax(float a) { return a > 0.0f ? a 
 
 // Four e4m3 codes (round to nearest even), a in the lowest byte.
 __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // The first conversion writes the low half of a word whose high half the
+  // second overwrites: starting from a's own bits lets the result take a's
+  // register instead of a zeroed copy (one move fewer per four codes).
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -kE4m3Max), kE4m3Max); }
