@@ -33,6 +33,13 @@
 //                   P̃ ≤ 2^τ and P̃·2^(8−τ) ≤ 256 < 448; O = Oᵀ·s_v/l with
 //                   l the sum of the quantised P̃ (formed by one more MFMA);
 //                   the optional LSE uses the fp32 sum before quantisation.
+//
+// Variants of the same launches: a block mask over 128×128 blocks (the
+// attention kernel walks only the visible key tiles; the quantisation is
+// unchanged), and packed variable-length sequences (each segment a sequence
+// of its own: the preparation kernels run over (segment, chunk) with one
+// K'/V scale per (b,h, segment), the attention kernel over (head, segment,
+// query tile)).
 #include <type_traits>
 
 #include "fattn_device.hpp"
