@@ -225,3 +225,22 @@ def test_fp8_exp_modes(shape, causal, exp_mode):
                                 rotate=True, seed=5)
     lse_err = np.abs(to_np(l_x) - model["lse"])
     assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 2, 300, 128), False), ((1, 3, 500, 64), True),
+                                          ((2, 2, 4100, 128), False)])
+def test_fp8_output_does_not_depend_on_the_lse_request(shape, causal):
+    # The kernel without the LSE output (the one the bench times) and the one
+    # with it form O by the same arithmetic: bit for bit the same O.
+    import tiled_attention_fattn_amd as fa
+    inp = _inputs(90 + shape[2], shape)
+    q, k, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    B, H, N, d = shape
+    ws = torch.empty(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    print(f"[fp8] lse / no lse shape={shape} causal={causal}", flush=True)
+    o1, l1 = fa.fwd_fp8(q, k, v, causal=causal, rotate=True, seed=8, workspace=ws)
+    o2, l2 = fa.fwd_fp8(q, k, v, causal=causal, rotate=True, seed=8, workspace=ws,
+                        want_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None
+    assert torch.equal(o1, o2)
