@@ -41,11 +41,13 @@ from .attention import (attention_forward, attention_backward,
                         attention_forward_rows, softmax_rows)
 from .hadamard import (sylvester, fwht, splitmix64, rotation_signs, rotate)
 from .e4m3 import (E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_values)
-from .fp8_model import (quantize_per_head, quantize_per_row_split, fp8_attention_model)
+from .fp8_model import (quantize_per_head, quantize_per_block, quantize_per_block_pow2,
+                        quantize_per_row_split, fp8_attention_model)
 
 __all__ = [
     "attention_forward", "attention_backward", "attention_forward_rows",
     "softmax_rows", "sylvester", "fwht", "splitmix64", "rotation_signs",
     "rotate", "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_values",
-    "quantize_per_head", "quantize_per_row_split", "fp8_attention_model",
+    "quantize_per_head", "quantize_per_block", "quantize_per_block_pow2",
+    "quantize_per_row_split", "fp8_attention_model",
 ]

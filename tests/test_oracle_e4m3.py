@@ -10,7 +10,9 @@ import torch
 
 from oracle.attention import attention_forward
 from oracle.e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode, e4m3_values
-from oracle.fp8_model import dequantize, fp8_attention_model, quantize_per_head
+from oracle.fp8_model import (dequantize, dequantize_rows, fp8_attention_model, pow2_scale,
+                              quantize_per_block, quantize_per_block_pow2, quantize_per_head,
+                              row_blocks)
 
 
 def test_decode_known_codes():
@@ -91,7 +93,7 @@ def test_fp8_model_without_rotation_is_attention_on_dequantised():
     m = fp8_attention_model(q, k, v, False, 0.25, rotate=False, seed=0)
     from oracle.fp8_model import dequantize_split_rows
     o, _ = attention_forward(dequantize_split_rows(m["q8"], m["q8lo"], m["sq"]),
-                             dequantize(m["k8"], m["sk"]), dequantize(m["v8"], m["sv"]),
+                             dequantize_rows(m["k8"], m["sk"]), dequantize_rows(m["v8"], m["sv"]),
                              False, 0.25)
     np.testing.assert_array_equal(m["o"], o)
     np.testing.assert_array_equal(m["q_rot"], q)
@@ -106,9 +108,10 @@ def test_fp8_model_with_rotation_quantises_rotated_operands():
     m = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=9)
     from oracle.hadamard import rotate
     np.testing.assert_allclose(m["q_rot"], rotate(q, 9), atol=0)
+    # Eight keys are one scale block: K' as with one scale per head.
     codes, scales = quantize_per_head(rotate(k, 9))
     np.testing.assert_array_equal(m["k8"], codes)
-    np.testing.assert_array_equal(m["sk"], scales)
+    np.testing.assert_array_equal(m["sk"], np.broadcast_to(scales[:, :, None], (1, 1, 8)))
 
 
 def test_quantisation_uses_the_exact_ratio_at_ties():
@@ -207,8 +210,8 @@ def test_fp8_model_block_mask_is_attention_on_dequantised_with_the_mask():
     for key in ("q8", "q8lo", "k8", "v8"):
         np.testing.assert_array_equal(m[key], m0[key])
     o, lse = attention_forward(dequantize_split_rows(m["q8"], m["q8lo"], m["sq"]),
-                               dequantize(m["k8"], m["sk"]), dequantize(m["v8"], m["sv"]),
-                               False, 0.25, block_mask=mask)
+                               dequantize_rows(m["k8"], m["sk"]),
+                               dequantize_rows(m["v8"], m["sv"]), False, 0.25, block_mask=mask)
     np.testing.assert_array_equal(m["o"], o)
     np.testing.assert_array_equal(m["lse"], lse)
     assert np.all(m["o"][:, :, 128:256] == 0) and np.all(np.isneginf(m["lse"][:, :, 128:256]))
@@ -228,7 +231,7 @@ def test_fp8_model_segments_are_sequences_of_their_own():
     cu = [0, 37, 37, 130, 200]
     for causal in (False, True):
         m = fp8_attention_model(q, k, v, causal, 0.25, rotate=True, seed=4, cu_seqlens=cu)
-        assert m["sk"].shape == (1, 2, 4) and m["sv"].shape == (1, 2, 4)
+        assert m["sk"].shape == (1, 2, 200) and m["sv"].shape == (1, 2, 200)
         for s in range(4):
             a, b = cu[s], cu[s + 1]
             if b == a:
@@ -237,15 +240,15 @@ def test_fp8_model_segments_are_sequences_of_their_own():
                                         rotate=True, seed=4)
             np.testing.assert_array_equal(m["k8"][:, :, a:b], alone["k8"])
             np.testing.assert_array_equal(m["v8"][:, :, a:b], alone["v8"])
-            np.testing.assert_array_equal(m["sk"][:, :, s], alone["sk"])
-            np.testing.assert_array_equal(m["sv"][:, :, s], alone["sv"])
+            np.testing.assert_array_equal(m["sk"][:, :, a:b], alone["sk"])
+            np.testing.assert_array_equal(m["sv"][:, :, a:b], alone["sv"])
             np.testing.assert_allclose(m["o"][:, :, a:b], alone["o"], rtol=0, atol=1e-13)
             np.testing.assert_allclose(m["lse"][:, :, a:b], alone["lse"], rtol=0, atol=1e-13)
     whole = fp8_attention_model(q, k, v, True, 0.25, rotate=True, seed=4, cu_seqlens=[0, 200])
     plain = fp8_attention_model(q, k, v, True, 0.25, rotate=True, seed=4)
     for key in ("k8", "v8", "o", "lse"):
         np.testing.assert_array_equal(whole[key], plain[key])
-    np.testing.assert_array_equal(whole["sk"][:, :, 0], plain["sk"])
+    np.testing.assert_array_equal(whole["sk"], plain["sk"])
     k2, v2 = k.copy(), v.copy()
     k2[:, :, 37:130] *= 32
     v2[:, :, 37:130] *= 32
@@ -255,3 +258,74 @@ def test_fp8_model_segments_are_sequences_of_their_own():
     for key in ("k8", "v8", "o", "lse"):
         np.testing.assert_array_equal(m1[key][:, :, keep], m2[key][:, :, keep])
     assert not np.array_equal(m1["o"][:, :, 37:130], m2["o"][:, :, 37:130])
+
+
+def test_scale_blocks_cover_each_segment_from_its_start():
+    assert row_blocks(300) == [(0, 128), (128, 256), (256, 300)]
+    assert row_blocks(300, [0, 5, 5, 140, 300]) == [(0, 5), (5, 133), (133, 140), (140, 268),
+                                                    (268, 300)]
+
+
+def test_per_block_quantisation_is_per_head_quantisation_of_each_block():
+    # K': each block of 128 rows is quantised exactly as a head of its own
+    # (the pinned per-head quantisation), and blocks do not see each other:
+    # scaling one block by 2.5 leaves every code alone and that block's scale
+    # times 2.5 (x·448/amax is the same exact ratio).
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((1, 2, 300, 16))
+    x[0, 1, 140, 3] = 40.0  # an outlier in the second block of head 1
+    codes, sc = quantize_per_block(x)
+    for a, b in row_blocks(300):
+        c1, s1 = quantize_per_head(x[:, :, a:b])
+        np.testing.assert_array_equal(codes[:, :, a:b], c1)
+        assert np.all(sc[:, :, a:b] == s1[:, :, None])
+    y = x.copy()
+    y[:, :, 128:256] *= 2.5
+    c2, s2 = quantize_per_block(y)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_allclose(s2[:, :, 128:256], 2.5 * sc[:, :, 128:256], rtol=1e-15)
+    np.testing.assert_array_equal(s2[:, :, :128], sc[:, :, :128])
+
+
+def test_pow2_scale_is_the_least_power_of_two_that_fits():
+    amax = np.array([448.0, 448.0 * 2 ** -5, 449.0, 100.0, 3.0, 0.0])
+    np.testing.assert_array_equal(pow2_scale(amax), [1.0, 2.0 ** -5, 2.0, 0.25, 2.0 ** -7, 1.0])
+    s = pow2_scale(amax[:-1])
+    assert np.all(amax[:-1] / s <= 448.0) and np.all(amax[:-1] / s > 224.0)
+
+
+def test_pow2_block_quantisation():
+    # V: code = E4M3FN(v / 2^e) with the block's least fitting power of two;
+    # the block maximum lands in (224, 448]; 448·2^k maps to code 0x7E
+    # exactly; scaling a block by a power of two moves only its scale.
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((1, 1, 200, 8))
+    x[0, 0, 5, 0] = 448.0 * 2.0 ** -4  # block 0's amax, a scaled maximum
+    codes, sc = quantize_per_block_pow2(x)
+    assert sc[0, 0, 0] == 2.0 ** -4 and codes[0, 0, 5, 0] == 0x7E
+    for a, b in row_blocks(200):
+        blk = np.abs(x[0, 0, a:b])
+        assert 224.0 < blk.max() / sc[0, 0, a] <= 448.0
+        np.testing.assert_array_equal(codes[0, 0, a:b], e4m3_encode(x[0, 0, a:b] / sc[0, 0, a]))
+    y = x.copy()
+    y[:, :, 128:] *= 8.0
+    c2, s2 = quantize_per_block_pow2(y)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(s2[:, :, 128:], 8.0 * sc[:, :, 128:])
+    np.testing.assert_array_equal(s2[:, :, :128], sc[:, :, :128])
+    # dequantised values within e4m3's half step of the inputs
+    rel = np.abs(dequantize_rows(codes, sc) - x) / np.maximum(np.abs(x), 1e-300)
+    big = np.abs(x) / sc[..., None] >= 2.0 ** -6  # normal e4m3 range
+    assert rel[big].max() <= 2.0 ** -4 + 1e-12
+
+
+def test_fp8_model_quantises_k_and_v_per_block():
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((1, 1, 260, 16)) for _ in range(3))
+    m = fp8_attention_model(q, k, v, False, 0.25, rotate=True, seed=5)
+    from oracle.hadamard import rotate as _rot
+    ck, sk = quantize_per_block(_rot(k, 5))
+    cv, sv = quantize_per_block_pow2(v)
+    for got, ref in ((m["k8"], ck), (m["sk"], sk), (m["v8"], cv), (m["sv"], sv)):
+        np.testing.assert_array_equal(got, ref)
+    assert len(np.unique(m["sk"][0, 0])) == 3 and len(np.unique(m["sv"][0, 0])) <= 3
