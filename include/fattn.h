@@ -212,12 +212,16 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  *               [B,H,d,Npad] (Npad = N rounded up to 64, zero padded; inside
  *               each block of 64 keys, position p = 32a + s holds key
  *               32(s/16) + 8((s%16)/4) + 4a + s%4, the order in which the
- *               kernel's P operand holds keys), then fp32 scales [2][B·H]
- *               (K', V per head: amax/448, or 1 for an all-zero head), then
- *               an fp32 [2][B·H][⌈N/128⌉] scratch of per-chunk amax.
- * Each operand is quantised as code = e4m3(x·448/amax), the exact ratio
- * rounded to nearest even: K' and V with one amax per (b,h), Q' with one
- * amax per row (each query row meets the keys only through its own scores).
+ *               kernel's P operand holds keys), then fp32 scales
+ *               [B·H][⌈N/128⌉][2]: the (K', V) pair of each chunk of 128
+ *               keys (keys 128c .. 128c + 127).
+ * K' and Q' are quantised as code = e4m3(x·448/amax), the exact ratio
+ * rounded to nearest even, with scale amax/448 (1 where amax = 0): K' with
+ * one amax per (b, h) and chunk of 128 keys, Q' with one amax per row (each
+ * query row meets the keys only through its own scores). V takes one power
+ * of two per (b, h) and chunk, 2^e with e the least integer such that
+ * amax ≤ 448·2^e (1 where amax = 0), and code = e4m3(v·2^−e), an exact
+ * scaling; the PV product applies 2^e as the fp8 MFMA's block scale.
  * Q' keeps a second e4m3 term for its quantisation residual,
  * Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that
  * Q' ≈ scale_q·(Q8 + Q8lo/16); the scores use both terms (two fp8 MFMAs).
@@ -226,14 +230,14 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  * The softmax keeps its exponent offset within a factor 2 of the running row
  * max (rescaling the partial output when the max grows by more), so every
  * unnormalised probability P̃ is at most 2; P is quantised to e4m3 as
- * P̃·2^7 ≤ 256.
+ * P̃·2^7 ≤ 256. O is normalised by the sum of the quantised P̃ of its row.
  * Additionally requires B·H ≤ 65535 (ENOTSUP otherwise).
  * Validated range (GPU parity tests against float64 attention): d ∈ {64,
  * 128}, N from 1 to 32768, causal and not. Error against exact attention,
  * relative RMS of O: within 6e-2 for N(0,1) inputs up to N = 32768 and for
  * inputs with 0.1% of the Q and K entries scaled by 20 at N = 4096 (every
  * element of B=4, H=16). With such outliers the e4m3 operands alone already
- * cost about 5.4% at N = 32768 (the quantised operands with exact P against
+ * cost about 5.5% at N = 32768 (the quantised operands with exact P against
  * exact attention), so there the output is held to 4e-2 of that operand
  * model instead. Longer sequences run but are not validated.
  */
@@ -273,8 +277,9 @@ fattn_status fattn_fwd_fp8_attend(const void* q, void* o, float* lse, int B, int
  * fattn_fwd_blocksparse (uint8 over 128-query × 128-key blocks, device
  * memory, read as given; key blocks a query block does not see are never
  * loaded). The quantisation is that of fattn_fwd_fp8: K' and V with one
- * scale per (b, h) taken over all N keys, whether visible or not, and Q'
- * per row; the workspace is filled the same way, so a later
+ * scale per (b, h) and chunk of 128 keys, taken over all of the chunk's keys
+ * whether visible or not, and Q' per row; the workspace is filled the same
+ * way, so a later
  * fattn_fwd_fp8_attend on it computes dense attention of the same operands.
  * A query that sees no key gets O = 0 and LSE = −∞. With every block set
  * the result equals fattn_fwd_fp8's. Supports N <= 32768 (ENOTSUP beyond);
@@ -293,16 +298,17 @@ fattn_status fattn_fwd_fp8_blocksparse(const void* q, const void* k, const void*
  * gist, closing summary: varlen named among the variants the design admits;
  * FlashAttention-3 page, innovation 3 for the fp8 operands). Each segment
  * is a sequence of its own, also for the quantisation: K' and V get one
- * scale per (b, h, segment) over that segment's rows, Q' one per row as
- * always, so each segment's O and LSE are exactly those fattn_fwd_fp8 gives
+ * scale per (b, h, segment) and chunk of 128 of that segment's rows counted
+ * from its first, Q' one per row as always, so each segment's O and LSE and
+ * its K8, V8ᵀ and scales are exactly those fattn_fwd_fp8 gives
  * for that segment alone (same rotate, seed, causal, scale, exp_mode).
  *   workspace   at least fattn_fwd_fp8_varlen_workspace_bytes(B, H, N, d,
  *               nseq, max_seqlen) bytes, 256-byte aligned: K8 as for
  *               fattn_fwd_fp8; V8ᵀ [B,H,d,Npad] with Npad = roundup(N, 64) +
  *               64·nseq, segment s in the 64-key blocks from column
  *               roundup(cu[s], 64) + 64·s on (same key order); scales
- *               [2][B·H][nseq]; then an fp32 [2][B·H][nseq][⌈max_seqlen/128⌉]
- *               scratch.
+ *               [B·H][nseq][⌈max_seqlen/128⌉][2] (the chunks a segment
+ *               has; the rest are not written).
  * The offsets are read on the device and clamped to [0, N], and every
  * segment is cut to its first max_seqlen rows (the caller keeps lengths
  * within max_seqlen; rows outside every segment, or past that cut, are not

@@ -89,8 +89,9 @@ def test_fp8_workspace_layout_and_checks():
     npad = 128
     n = B * H * N * d
     assert ok == 0 and ov >= ok + n
-    # scales [2][B·H], then the per-chunk amax scratch [2][B·H][⌈N/128⌉]
-    assert osc >= ov + B * H * d * npad and need >= osc + 8 * B * H + 8 * B * H * 1
+    # then the scales: a (K', V) fp32 pair per (b, h) and chunk of 128 keys
+    assert osc >= ov + B * H * d * npad
+    assert need == (osc + 8 * B * H * ((N + 127) // 128) + 255) // 256 * 256
     assert all(x % 256 == 0 for x in (ok, ov, osc))
 
     def call(ws, nbytes, **kw):
@@ -222,10 +223,12 @@ def test_fp8_varlen_workspace_and_checks():
     lib = fa.lib()
     B, H, N, d, nseq, maxl = 1, 2, 300, 128, 3, 200
     need = lib.fattn_fwd_fp8_varlen_workspace_bytes(B, H, N, d, nseq, maxl)
-    # K8, V8ᵀ with 64 more columns per segment, scales and chunk partials per
-    # (head, segment), each region 256-byte aligned.
+    # K8, V8ᵀ with 64 more columns per segment, a scale pair per (head,
+    # segment) and chunk of 128 keys of the longest segment, each region
+    # 256-byte aligned.
     npad = (N + 63) // 64 * 64 + 64 * nseq
-    assert need >= B * H * N * d + B * H * d * npad + 8 * B * H * nseq + 8 * B * H * nseq * 2
+    r = lambda x: (x + 255) // 256 * 256
+    assert need == r(r(r(B * H * N * d) + B * H * d * npad) + 8 * B * H * nseq * ((maxl + 127) // 128))
     assert need > lib.fattn_fwd_fp8_workspace_bytes(B, H, N, d)
     assert lib.fattn_fwd_fp8_varlen_workspace_bytes(B, H, N, d, 0, maxl) == 0
 

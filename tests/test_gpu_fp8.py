@@ -5,9 +5,10 @@ inputs (the rotation cannot change the exact result): relative RMS ≤ 6e-2
 with the rotation (the configuration the bound is stated for); without it
 the error is reported and only held to a loose sanity bound. The
 quantisation is checked separately against the oracle's E4M3 model: the K'
-and V codes in the workspace must equal the model's codes except for rare
+codes in the workspace must equal the model's codes except for rare
 one-step differences where the float32 rotation and the float64 one round on
-opposite sides of a tie. Q' is quantised (one scale per row, two terms)
+opposite sides of a tie, the V codes (a power-of-two scaling) exactly, and
+the per-chunk scales the model's. Q' is quantised (one scale per row, two terms)
 inside the attention kernel and never stored; the LSE, compared with the
 model's LSE, checks its scores (it isolates the kernel's own error from the
 quantisation error), and scaling one query row by a power of two must leave
@@ -104,12 +105,17 @@ def test_fp8_matches_exact_attention(shape, causal, rotate):
     B, H, N, d = shape
     k8, v8t, sc = (t.cpu().numpy() for t in fa.fp8_workspace_views(ws, B, H, N, d))
     v8 = _unpermute_v8t(v8t, N)
-    for name, got_c, ref_c in (("K8", k8, model["k8"]), ("V8", v8, model["v8"])):
-        steps = _code_steps(got_c, ref_c)
-        assert steps.max() <= 1, f"{name}: codes differ by {steps.max()} steps"
-        assert np.mean(steps == 0) >= 0.999, f"{name}: {np.mean(steps != 0):.2e} codes differ"
-    np.testing.assert_allclose(sc[0], model["sk"], rtol=1e-5)
-    np.testing.assert_allclose(sc[1], model["sv"], rtol=1e-6)
+    steps = _code_steps(k8, model["k8"])
+    assert steps.max() <= 1, f"K8: codes differ by {steps.max()} steps"
+    assert np.mean(steps == 0) >= 0.999, f"K8: {np.mean(steps != 0):.2e} codes differ"
+    # V is not rotated and its scale is a power of two: every code has the
+    # model's value (a negative value that rounds to zero may come out as
+    # the code of −0, which decodes equal to +0)
+    assert np.array_equal(e4m3_decode(v8), e4m3_decode(model["v8"])), "V8 differs from the model"
+    # one (K', V) scale pair per chunk of 128 keys; the model holds the
+    # scale of every row
+    np.testing.assert_allclose(sc[..., 0], model["sk"][..., ::128], rtol=1e-5)
+    np.testing.assert_array_equal(sc[..., 1], model["sv"][..., ::128])
     # padding keys of V8ᵀ are zero
     if v8t.shape[-1] > N:
         assert np.all(_unpermute_v8t(v8t, None)[:, :, N:] == 0)

@@ -1,7 +1,7 @@
 """GPU parity of the block-sparse fp8 forward (fattn_fwd_fp8_blocksparse).
 
 Its quantisation is that of the dense fp8 forward (K' and V with one scale
-per head over all keys, Q' per row), so the workspace it leaves must equal
+per 128-key chunk over all its keys, Q' per row), so the workspace it leaves must equal
 the dense call's byte for byte, and an all-ones mask must reproduce the dense
 fp8 output and LSE bit for bit. Against the oracle, on the rows that see at
 least one key: O within the fp8 bound (relative RMS) of float64 attention

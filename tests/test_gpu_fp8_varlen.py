@@ -1,8 +1,9 @@
 """GPU parity of the fp8 forward over packed variable-length sequences
 (fattn_fwd_fp8_varlen).
 
-Each segment is a sequence of its own, also for the quantisation (K' and V
-get one scale per (head, segment)), so every segment's O and LSE must come
+Each segment is a sequence of its own, also for the quantisation (the K' and
+V scale chunks of 128 keys start at the segment's first row), so every
+segment's O and LSE must come
 out bit for bit as fattn_fwd_fp8 computes them on that segment alone, and the
 segment's K8 codes, V8ᵀ columns and scales in the workspace must equal that
 call's. Against the oracle: O within the fp8 bound (relative RMS) of float64
@@ -71,13 +72,14 @@ def test_fp8_varlen_segments_equal_separate_calls(seed, H, d, lengths, causal, e
                                rotate=True, seed=6, workspace=ws, exp_mode=exp_mode)
     torch.cuda.synchronize()
     # workspace regions of the packed call: K8 [1,H,N,d], V8ᵀ [1,H,d,npad],
-    # scales [2][H][nseq]
+    # scales [H][nseq][ceil(maxl/128)][2]
     npad = (N + 63) // 64 * 64 + 64 * nseq
     k8 = ws[:H * N * d].view(1, H, N, d)
     v8_off = (H * N * d + 255) // 256 * 256
     v8t = ws[v8_off:v8_off + H * d * npad]
     sc_off = (v8_off + H * d * npad + 255) // 256 * 256
-    sc = ws[sc_off:sc_off + 8 * H * nseq].view(torch.float32).view(2, H, nseq)
+    nch = (maxl + 127) // 128
+    sc = ws[sc_off:sc_off + 8 * H * nseq * nch].view(torch.float32).view(H, nseq, nch, 2)
     for s, (a, b) in enumerate(zip(cu[:-1], cu[1:])):
         if b == a:
             continue
@@ -93,7 +95,7 @@ def test_fp8_varlen_segments_equal_separate_calls(seed, H, d, lengths, causal, e
         assert torch.equal(k8[:, :, a:b], k1)
         col0 = (int(a) + 63) // 64 * 64 + 64 * s
         assert torch.equal(_v8_cols(v8t, H, d, npad, col0, v1.shape[-1]), v1)
-        assert torch.equal(sc[:, :, s], s1[:, 0])
+        assert torch.equal(sc[:, s, :s1.shape[2]], s1[0])
 
 
 @pytest.mark.parametrize("seed,H,d,lengths,causal", CASES)

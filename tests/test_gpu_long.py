@@ -70,12 +70,12 @@ def test_fp8_long_sequence_sampled(outliers, causal):
     # the oracle's operand-quantised model on the same rows. Without outliers
     # the output is held to the fp8 bound against exact attention. With the
     # 0.1% x20 outliers of the fp8 workload the model alone (operands in
-    # e4m3, exact P) is about 5.4% from exact attention on these rows (a CPU
+    # e4m3, exact P) is about 5.5% from exact attention on these rows (a CPU
     # oracle test pins that), so the kernel is held to the model at 4e-2 and
     # its error against exact attention is reported.
     import tiled_attention_fattn_amd as fa
-    from oracle.fp8_model import (dequantize, dequantize_split_rows, quantize_per_head,
-                                  quantize_per_row_split)
+    from oracle.fp8_model import (dequantize_rows, dequantize_split_rows, quantize_per_block,
+                                  quantize_per_block_pow2, quantize_per_row_split)
     from oracle.hadamard import rotate
     N, d, k = 32768, 128, 66 + int(outliers) + 2 * int(causal)
     shape = (1, 2, N, d)
@@ -90,9 +90,10 @@ def test_fp8_long_sequence_sampled(outliers, causal):
     rows = _rows(N, k)
     idx = torch.as_tensor(rows, device=o.device)
     q8, q8lo, sq = quantize_per_row_split(rotate(inp["q"][0], k))
-    k8, sk = quantize_per_head(rotate(inp["k"][0], k))
-    v8, sv = quantize_per_head(inp["v"][0])
-    model = (dequantize_split_rows(q8, q8lo, sq), dequantize(k8, sk), dequantize(v8, sv))
+    k8, sk = quantize_per_block(rotate(inp["k"][0], k))
+    v8, sv = quantize_per_block_pow2(inp["v"][0])
+    model = (dequantize_split_rows(q8, q8lo, sq), dequantize_rows(k8, sk),
+             dequantize_rows(v8, sv))
     got, ref, mod = [], [], []
     for h in range(2):
         got.append(to_np(o[0, h][idx]))

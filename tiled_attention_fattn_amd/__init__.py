@@ -294,18 +294,20 @@ def fp8_workspace_views(ws, B, H, N, d):
 
     k8: uint8 [B,H,N,d] e4m3 codes of K'; v8t: uint8 [B,H,d,Npad] (V
     transposed, zero padded to Npad = N rounded up to 64, keys permuted inside
-    each 64-key block); scales: fp32 [2, B, H] (K', V). Q' is quantised inside
-    the attention kernel and not stored.
+    each 64-key block); scales: fp32 [B, H, ceil(N/128), 2], the (K', V) pair
+    of each chunk of 128 keys. Q' is quantised inside the attention kernel and
+    not stored.
     """
     torch = _torch()
     offs = [ctypes.c_size_t() for _ in range(3)]
     _call(lib().fattn_fwd_fp8_workspace_layout(B, H, N, d, *[ctypes.byref(x) for x in offs]))
     ok, ov, osc = (x.value for x in offs)
     npad = (N + 63) // 64 * 64
+    nch = (N + 127) // 128
     n = B * H * N * d
     k8 = ws[ok:ok + n].view(B, H, N, d)
     v8t = ws[ov:ov + B * H * d * npad].view(B, H, d, npad)
-    sc = ws[osc:osc + 8 * B * H].view(torch.float32).view(2, B, H)
+    sc = ws[osc:osc + 8 * B * H * nch].view(torch.float32).view(B, H, nch, 2)
     return k8, v8t, sc
 
 

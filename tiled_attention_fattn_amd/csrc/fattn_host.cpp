@@ -84,12 +84,13 @@ fattn_status hip_status(hipError_t e, const char* what) {
   } while (0)
 
 struct Fp8Layout {
-  size_t k8, v8t, scales, partial, total;
+  size_t k8, v8t, scales, total;
 };
 
 // nseq = 0: no packed segments (one per head, all N rows). With segments
-// V8ᵀ has 64 more columns per segment, scales and partials one set per
-// (head, segment), and the partials cover max_seqlen rows.
+// V8ᵀ has 64 more columns per segment and the scales one set per (head,
+// segment) over max_seqlen rows. Scales: a (K, V) fp32 pair per 128-key
+// chunk.
 Fp8Layout fp8_layout(int B, int H, int N, int d, int nseq = 0, int max_seqlen = 0) {
   const size_t bh = (size_t)B * H;
   const size_t units = bh * (nseq > 0 ? nseq : 1);
@@ -100,8 +101,7 @@ Fp8Layout fp8_layout(int B, int H, int N, int d, int nseq = 0, int max_seqlen = 
   L.v8t = round_up(L.k8 + bh * N * d, 256);
   L.scales = round_up(L.v8t + bh * d * npad, 256);
   const size_t nchunks = (rows + fattn::kFp8AmaxRows - 1) / fattn::kFp8AmaxRows;
-  L.partial = round_up(L.scales + 2 * units * sizeof(float), 256);
-  L.total = round_up(L.partial + 2 * units * nchunks * sizeof(float), 256);
+  L.total = round_up(L.scales + 2 * units * nchunks * sizeof(float), 256);
   return L;
 }
 
@@ -385,7 +385,7 @@ static fattn_status fwd_fp8_impl(const char* name, const void* q, const void* k,
   char* ws = (char*)workspace;
   return hip_status(fattn::launch_fwd_fp8(q, k, v, o, lse, (uint8_t*)(ws + L.k8),
                                           (uint8_t*)(ws + L.v8t), (float*)(ws + L.scales),
-                                          (float*)(ws + L.partial), B, H, N, d, causal != 0, scale,
+                                          B, H, N, d, causal != 0, scale,
                                           exp_mode == FATTN_EXP_AUTO ? FATTN_EXP_HW : exp_mode,
                                           rotate != 0, seed, block_mask, per_head != 0,
                                           cu_seqlens, nseq, max_seqlen, (hipStream_t)stream),

@@ -49,19 +49,19 @@ hipError_t launch_bwd_bf16_blocksparse(const void* q, const void* k, const void*
 constexpr int kBwdRowPad = 64;
 
 // fp8 forward: k8 e4m3 [B,H,N,d]; v8t e4m3 [B,H,d,Npad]; scales fp32
-// [2][B*H] (K, V); partial fp32 [2][B*H][ceil(N/kFp8AmaxRows)] scratch. Q is
-// rotated and quantised (one scale per row) inside the attention kernel.
+// [B*H(*nseq)][ceil(rows/128)][2] (K, V per 128-key chunk; rows = N, or
+// max_seqlen with packed segments). Q is rotated and quantised (one scale
+// per row) inside the attention kernel.
 // block_mask: optional uint8 mask over 128×128 blocks ([nb][nb], or
 // [B·H][nb][nb] when per_head), as for launch_fwd_bf16_blocksparse.
 // cu_seqlens: optional packed segments (nseq, max_seqlen), as for
-// launch_fwd_bf16_varlen; then the workspace holds V8ᵀ with
-// roundup(N, 64) + 64·nseq columns per head, scales [2][B·H][nseq] and
-// partial [2][B·H][nseq][ceil(max_seqlen/128)]. Not both.
+// launch_fwd_bf16_varlen; then V8ᵀ has roundup(N, 64) + 64·nseq columns per
+// head. Not both.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
-                          uint8_t* k8, uint8_t* v8t, float* scales, float* partial, int B, int H,
-                          int N, int d, bool causal, float scale, int exp_mode, bool rotate,
-                          uint64_t seed, const uint8_t* block_mask, bool per_head,
-                          const int* cu_seqlens, int nseq, int max_seqlen, hipStream_t stream);
+                          uint8_t* k8, uint8_t* v8t, float* scales, int B, int H, int N, int d,
+                          bool causal, float scale, int exp_mode, bool rotate, uint64_t seed,
+                          const uint8_t* block_mask, bool per_head, const int* cu_seqlens,
+                          int nseq, int max_seqlen, hipStream_t stream);
 
 // fp8 attention only (the last launch of launch_fwd_fp8) on the K/V operands
 // a previous launch_fwd_fp8 of the same shape left in k8/v8t/scales; Q is
@@ -78,6 +78,6 @@ constexpr size_t kStaticWorkspaceBytes = (size_t)16 << 20;
 hipError_t static_workspace(int device, void** ptr);
 
 constexpr int kFp8Npad = 64;
-constexpr int kFp8AmaxRows = 128;  // rows per amax chunk (measured: 128 beats 64 and 256)
+constexpr int kFp8AmaxRows = 128;  // keys per K/V scale chunk
 
 }  // namespace fattn

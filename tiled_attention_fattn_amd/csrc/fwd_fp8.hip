@@ -6,20 +6,21 @@
 // SplitMix64 (Steele, Lea & Flood 2014) and H_d the Sylvester Hadamard matrix,
 // applied row by row with a fast Walsh–Hadamard transform in registers.
 //
-// Scales: K' and V one per (b,h) (amax over the head); Q' one per row (the
-// row's own amax), which lets the attention kernel quantise the query rows
-// it owns itself, so Q never makes a round trip through memory in e4m3.
+// Scales: K' and V one per chunk of 128 keys of each (b,h) (K' the exact
+// ratio x·448/amax of its chunk, V a power of two that the fp8 MFMA's block
+// scale operand applies); Q' one per row (the row's own amax), which lets
+// the attention kernel quantise the query rows it owns itself, so Q never
+// makes a round trip through memory in e4m3.
 //
 // Launches (one stream):
-//   1. fp8_amax   — amax of |K·R| and |V| over each chunk of kFp8AmaxRows
-//                   (128) rows of each (b,h), one plain store per block (no
-//                   atomics).
-//   2. fp8_quant_k — recompute K·R; code = e4m3(t), t = x·448/amax (one
-//                   correctly rounded division), round to nearest even;
-//                   write K8 and the K scales.
-//   3. fp8_quant_v  — V codes written transposed ([d][keys]) in the key order
-//                   the attention kernel's P operand uses.
-//   4. fwd_fp8    — attention. Prologue: each lane rotates its half of one
+//   1. fp8_prep   — one pass over K and V: each block holds one 128-key chunk
+//                   of K·R (rotated in registers) or of V, takes its amax and
+//                   quantises it: K8 = e4m3(x·448/amax) (one correctly
+//                   rounded division, round to nearest even), V8 = e4m3(v·2^−e)
+//                   written transposed ([d][keys]) in the key order the
+//                   attention kernel's P operand uses; one (K, V) scale pair
+//                   per chunk.
+//   2. fwd_fp8    — attention. Prologue: each lane rotates its half of one
 //                   bf16 Q row (the Walsh–Hadamard stages across the two
 //                   lanes of the row by a lane-half swap), takes the row's
 //                   amax and quantises it to Q8 and the residual term
@@ -30,15 +31,17 @@
 //                   e4m3 as P̃·2^(8−τ) with τ = 1: the exponent offset moves
 //                   only when a tile max exceeds it by more than τ
 //                   (FlashAttention-4 gist, technical summary 2.B), so
-//                   P̃ ≤ 2^τ and P̃·2^(8−τ) ≤ 256 < 448; O = Oᵀ·s_v/l with
-//                   l the sum of the quantised P̃ (formed by one more MFMA);
-//                   the optional LSE uses the fp32 sum before quantisation.
+//                   P̃ ≤ 2^τ and P̃·2^(8−τ) ≤ 256 < 448; a tile's K scale
+//                   joins the score factor, its V scale the PV MFMA's A
+//                   block scale; O = Oᵀ/l with l the sum of the quantised P̃
+//                   (formed by one more MFMA); the optional LSE uses the
+//                   fp32 sum before quantisation.
 //
 // Variants of the same launches: a block mask over 128×128 blocks (the
 // attention kernel walks only the visible key tiles; the quantisation is
 // unchanged), and packed variable-length sequences (each segment a sequence
-// of its own: the preparation kernels run over (segment, chunk) with one
-// K'/V scale per (b,h, segment), the attention kernel over (head, segment,
+// of its own: the preparation runs over (segment, chunk), chunks counted
+// from the segment's first row; the attention kernel over (head, segment,
 // query tile)).
 #include <type_traits>
 
@@ -158,68 +161,16 @@ __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, i
   return ok;
 }
 
-// grid (segments × row chunks, BH, 2 tensors): block max of |x| over
-// kFp8AmaxRows rows of one segment. Tensor t = 0 is K·R, t = 1 is V; they are
-// taken in the order V, K (blockIdx.z = 0, 1), so that K, which the
-// quantisation kernel reads next, holds the most recently read lines in the
-// last-level cache. partial: [2][BH][nseq][nchunks] (0 for a chunk past its
-// segment's end).
-template <int D>
-__global__ __launch_bounds__(256) void fp8_amax_kernel(const bf16* __restrict__ K,
-                                                      const bf16* __restrict__ V,
-                                                      float* __restrict__ partial, int N, int BH,
-                                                      int rotate, uint64_t seed, Fp8Segs sg,
-                                                      int nchunks) {
-  constexpr int LPR = D / kEpl, RPB = 256 / LPR;
-  __shared__ float sgn[D];
-  __shared__ float wmax[4];
-  const int t = 1 - (int)blockIdx.z, bh = blockIdx.y;
-  const int seg = (int)blockIdx.x / nchunks, chunk = (int)blockIdx.x - seg * nchunks;
-  int row0, L;
-  seg_rows(sg, N, seg, row0, L);
-  const bool rot = rotate && t == 0;
-  if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
-  __syncthreads();
-  const bf16* src = (t == 0 ? K : V) + (size_t)bh * N * D;
-  const int part = threadIdx.x % LPR;
-  float m = 0.0f;
-  // kRowSets row-sets per step so that that many loads per thread are in
-  // flight together.
-  const int r_end = row0 + min(L, (chunk + 1) * kFp8AmaxRows);
-  for (int r0 = row0 + chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
-    float x[kRowSets][kEpl];
-#pragma unroll
-    for (int u = 0; u < kRowSets; ++u)
-      load_row_part<D>(src, r0 + u * RPB + threadIdx.x / LPR, r_end, part, rot, sgn, x[u]);
-#pragma unroll
-    for (int u = 0; u < kRowSets; ++u)
-#pragma unroll
-      for (int e = 0; e < kEpl; ++e) m = fmaxf(m, fabsf(x[u][e]));
-  }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    partial[(((size_t)t * BH + bh) * sg.nseq + seg) * nchunks + chunk] =
-        fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-}
-
-// amax of one (tensor, head) from its chunk partials, reduced by wave 0 and
-// broadcast through LDS. Every thread of the block must call it.
-__device__ __forceinline__ float head_amax(const float* partial, int nchunks, float* slot) {
-  if (threadIdx.x < 64) {
-    float m = 0.0f;
-    for (int i = threadIdx.x; i < nchunks; i += 64) m = fmaxf(m, partial[i]);
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-    if (threadIdx.x == 0) *slot = m;
-  }
-  __syncthreads();
-  return *slot;
-}
-
 __device__ __forceinline__ float scale_from_amax(float a) { return a > 0.0f ? a / kE4m3Max : 1.0f; }
+
+// E8M0 code of a positive normal power of two: its biased exponent.
+__device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__float_as_uint(pow2) >> 23); }
+
+// The fp8 product with the A operand scaled by 2^(e8 − 127) (E8M0 block
+// scale, the same for the lane's 32 k values).
+__device__ __forceinline__ f32x16 mfma32_fp8_ascale(i32x8 a, i32x8 b, f32x16 c, int e8) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, e8, 0, 127);
+}
 
 // Four e4m3 codes (round to nearest even), a in the lowest byte.
 __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
@@ -257,45 +208,77 @@ __device__ __forceinline__ float ratio448(float x, const Ratio448& r) {
   return fmaf(e, r.inv, q0);
 }
 
-// grid (segments × row chunks, BH): K·R quantised with its segment's scale
-// (the head's without segments), kFp8AmaxRows rows per block; scales[0] is
-// [BH][nseq].
+// Position of key r (0..63) inside its 64-key block of V8ᵀ.
+__device__ __forceinline__ int v8_pos(int r) {
+  const int s = 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3);
+  return 32 * ((r >> 2) & 1) + s;
+}
+
+// One pass of the preparation: grid (segments × 128-key chunks, BH, 2).
+// blockIdx.z = 0: the chunk's K rows, rotated (Walsh–Hadamard in registers),
+// take the chunk's amax and are quantised with the exact ratio
+// x·448/amax; = 1: the chunk's V rows take a power-of-two scale 2^e (e the
+// least with amax ≤ 448·2^e) and are quantised as e4m3(v·2^−e), an exact
+// scaling, into V8ᵀ ([d][keys], the P-operand key order of v8_pos). Each
+// thread holds its share of the chunk in registers between the two steps,
+// so K and V are read once. scales: [BH·nseq][nchunks][2] (K, V) fp32.
+// Keys past the segment's end give code 0; 64-key blocks past it are not
+// written.
 template <int D>
-__global__ __launch_bounds__(256) void fp8_quant_k_kernel(const bf16* __restrict__ K,
-                                                         uint8_t* __restrict__ k8,
-                                                         const float* __restrict__ partial,
-                                                         float* __restrict__ scales, int N,
-                                                         int rotate, uint64_t seed, Fp8Segs sg,
-                                                         int nchunks) {
-  constexpr int LPR = D / kEpl, RPB = 256 / LPR;
+__global__ __launch_bounds__(256) void fp8_prep_kernel(const bf16* __restrict__ K,
+                                                      const bf16* __restrict__ V,
+                                                      uint8_t* __restrict__ k8,
+                                                      uint8_t* __restrict__ v8t,
+                                                      float* __restrict__ scales, int N,
+                                                      int Npad, int rotate, uint64_t seed,
+                                                      Fp8Segs sg, int nchunks) {
+  constexpr int LPR = D / kEpl, RPB = 256 / LPR;   // K: lanes per row, rows per pass
+  constexpr int KPASS = kFp8AmaxRows / RPB;        // K: passes over the chunk's rows
+  constexpr int CHUNKS = D / 8;                    // V: 16-byte d-chunks per key row
+  constexpr int VITEMS = 2 * 16 * CHUNKS;          // V: (sub-block, key quad, d-chunk) items
+  constexpr int VPT = (VITEMS + 255) / 256;        // V: items per thread
+  static_assert(kFp8AmaxRows == 128, "two 64-key V blocks per chunk");
   __shared__ float sgn[D];
-  __shared__ float am_slot;
+  __shared__ float wmax[4];
   const int bh = blockIdx.y;
   const int seg = (int)blockIdx.x / nchunks, chunk = (int)blockIdx.x - seg * nchunks;
   int row0, L;
   seg_rows(sg, N, seg, row0, L);
-  if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
+  const int c0 = chunk * kFp8AmaxRows;  // first key of the chunk within the segment
+  if (c0 >= L) return;                  // whole block
   const int unit = bh * sg.nseq + seg;
-  const float am = head_amax(partial + (size_t)unit * nchunks, nchunks, &am_slot);
-  const Ratio448 rk(am);
-  const size_t head = (size_t)bh * N * D;
-  const bf16* src = K + head;
-  uint8_t* dst = k8 + head;
-  if (chunk == 0 && threadIdx.x == 0) scales[unit] = scale_from_amax(am);
-  const int part = threadIdx.x % LPR;
-  const int r_end = row0 + min(L, (chunk + 1) * kFp8AmaxRows);
-  for (int r0 = row0 + chunk * kFp8AmaxRows; r0 < r_end; r0 += kRowSets * RPB) {
-    float xs[kRowSets][kEpl];
-    bool ok[kRowSets];
+  float* sc = scales + ((size_t)unit * nchunks + chunk) * 2;
+  const int c_end = min(L, c0 + kFp8AmaxRows);
+  auto block_max = [&](float m) __device__ {
 #pragma unroll
-    for (int u = 0; u < kRowSets; ++u)
-      ok[u] = load_row_part<D>(src, r0 + u * RPB + threadIdx.x / LPR, r_end, part, rotate != 0, sgn,
-                               xs[u]);
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  };
+
+  if (blockIdx.z == 0) {
+    if (threadIdx.x < D) sgn[threadIdx.x] = rotation_sign(seed, threadIdx.x);
+    __syncthreads();
+    const size_t head = ((size_t)bh * N + row0) * D;
+    const int part = threadIdx.x % LPR;
+    float xs[KPASS][kEpl];
+    bool ok[KPASS];
+    float m = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kRowSets; ++u) {
+    for (int u = 0; u < KPASS; ++u) {
+      ok[u] = load_row_part<D>(K + head, c0 + u * RPB + threadIdx.x / LPR, c_end, part,
+                               rotate != 0, sgn, xs[u]);
+#pragma unroll
+      for (int e = 0; e < kEpl; ++e) m = fmaxf(m, fabsf(xs[u][e]));
+    }
+    const float am = block_max(m);
+    const Ratio448 rk(am);
+    if (threadIdx.x == 0) sc[0] = scale_from_amax(am);
+#pragma unroll
+    for (int u = 0; u < KPASS; ++u) {
       if (!ok[u]) continue;
-      const int row = r0 + u * RPB + threadIdx.x / LPR;
-      const size_t off = (size_t)row * D + part * kEpl;
+      const size_t off = head + (size_t)(c0 + u * RPB + threadIdx.x / LPR) * D + part * kEpl;
 #pragma unroll
       for (int c = 0; c < kEpl / 16; ++c) {  // 16 elements → one 16-byte store of codes
         float tt[16];
@@ -308,65 +291,56 @@ __global__ __launch_bounds__(256) void fp8_quant_k_kernel(const bf16* __restrict
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           w[g] = cvt_fp8x4(tt[4 * g], tt[4 * g + 1], tt[4 * g + 2], tt[4 * g + 3]);
-        *(i32x4*)(dst + off + 16 * c) = w;
+        *(i32x4*)(k8 + off + 16 * c) = w;
       }
     }
-  }
-}
-
-// Position of key r (0..63) inside its 64-key block of V8ᵀ.
-__device__ __forceinline__ int v8_pos(int r) {
-  const int s = 16 * (r >> 5) + 4 * ((r & 31) >> 3) + (r & 3);
-  return 32 * ((r >> 2) & 1) + s;
-}
-
-// grid (segments × 64-key blocks, BH): one 64-key block of one segment of
-// one head. Thread (m, cc) reads the 8 values of d-chunk cc of keys
-// 4m .. 4m+3 and writes, for each of those 8 d, the 4 codes of the 4 keys as
-// one 4-byte word: the four keys are adjacent in the P-operand key order
-// (v8_pos), and the 16 threads of one chunk fill 64 contiguous bytes of each
-// V8ᵀ row. Keys past the segment's end give code 0; blocks past it write
-// nothing. scales[1] is [BH][nseq].
-template <int D>
-__global__ __launch_bounds__(256) void fp8_quant_v_kernel(const bf16* __restrict__ V,
-                                                         uint8_t* __restrict__ v8t,
-                                                         const float* __restrict__ partial,
-                                                         float* __restrict__ scales, int N,
-                                                         int Npad, int BH, int nchunks,
-                                                         Fp8Segs sg, int nvblocks) {
-  constexpr int CHUNKS = D / 8;
-  const int bh = blockIdx.y;
-  const int seg = (int)blockIdx.x / nvblocks, kb = (int)blockIdx.x - seg * nvblocks;
-  int row0, L;
-  seg_rows(sg, N, seg, row0, L);
-  if (kb > 0 && 64 * kb >= L) return;  // whole block (block 0 still writes the scale)
-  __shared__ float am_slot;
-  const int unit = bh * sg.nseq + seg;
-  const float am =
-      head_amax(partial + ((size_t)BH * sg.nseq + unit) * nchunks, nchunks, &am_slot);
-  const Ratio448 rv(am);
-  if (kb == 0 && threadIdx.x == 0) scales[(size_t)BH * sg.nseq + unit] = scale_from_amax(am);
-  if (64 * kb >= L) return;  // an empty segment: its scale only
-  const bf16* src = V + ((size_t)bh * N + row0) * D;
-  uint8_t* dst = v8t + (size_t)bh * D * Npad + seg_vcol(sg, seg, row0) + (size_t)kb * 64;
-  for (int ch = threadIdx.x; ch < 16 * CHUNKS; ch += 256) {
-    const int m = ch % 16, cc = ch / 16;
-    float x[4][8];
+  } else {
+    // Item (sb, m, cc): sub-block sb (keys c0 + 64sb ..), keys 4m .. 4m+3,
+    // d-chunk cc; its 8 values of each of the 4 keys.
+    const bf16* src = V + ((size_t)bh * N + row0) * D;
+    float x[VPT][4][8];
+    float m = 0.0f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = kb * 64 + 4 * m + u;
-      bf16x8 v = {};
-      if (key < L) v = *(const bf16x8*)(src + (size_t)key * D + cc * 8);
+    for (int it = 0; it < VPT; ++it) {
+      const int item = threadIdx.x + 256 * it;
+      const int sb = item / (16 * CHUNKS), rem = item % (16 * CHUNKS);
+      const int mq = rem % 16, cc = rem / 16;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float a = (float)v[e];
-        x[u][e] = am > 0.0f ? clamp448(ratio448(a, rv)) : a;
+      for (int u = 0; u < 4; ++u) {
+        const int key = c0 + 64 * sb + 4 * mq + u;
+        bf16x8 v = {};
+        if (item < VITEMS && key < c_end) v = *(const bf16x8*)(src + (size_t)key * D + cc * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[it][u][e] = (float)v[e];
+          m = fmaxf(m, fabsf(x[it][u][e]));
+        }
       }
     }
-    const int p = v8_pos(4 * m);
+    const float am = block_max(m);
+    // Least e with am ≤ 448·2^e: am/448 = f·2^k, f ∈ [0.5, 1); e = k − 1 when
+    // f = 0.5 exactly (the quotient is exact there, a power of two).
+    int ex = 0;
+    if (am > 0.0f) {
+      int k;
+      const float f = frexpf(am / kE4m3Max, &k);
+      ex = f == 0.5f ? k - 1 : k;
+    }
+    if (threadIdx.x == 0) sc[1] = ldexpf(1.0f, ex);
+    uint8_t* dst = v8t + (size_t)bh * D * Npad + seg_vcol(sg, seg, row0) + c0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *(int*)(dst + (size_t)(cc * 8 + e) * Npad + p) = cvt_fp8x4(x[0][e], x[1][e], x[2][e], x[3][e]);
+    for (int it = 0; it < VPT; ++it) {
+      const int item = threadIdx.x + 256 * it;
+      const int sb = item / (16 * CHUNKS), rem = item % (16 * CHUNKS);
+      const int mq = rem % 16, cc = rem / 16;
+      if (item >= VITEMS || c0 + 64 * sb >= c_end) continue;  // a block past the end
+      const int p = 64 * sb + v8_pos(4 * mq);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *(int*)(dst + (size_t)(cc * 8 + e) * Npad + p) =
+            cvt_fp8x4(ldexpf(x[it][0][e], -ex), ldexpf(x[it][1][e], -ex),
+                      ldexpf(x[it][2][e], -ex), ldexpf(x[it][3][e], -ex));
+    }
   }
 }
 
@@ -407,6 +381,9 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   // LDS: K slots 0, 1 then V slots 0, 1; the rotation's signs.
   __shared__ __attribute__((aligned(16))) char lds[2 * KTILE + 2 * VTILE];
   __shared__ __attribute__((aligned(16))) float sgn[D];
+  // (K, V) scale pair of the 128-key chunk of the tile in each K slot,
+  // loaded with the tile (one 4-byte element per lane, lanes 0 and 1).
+  __shared__ __attribute__((aligned(16))) float scl[2][64];
   char* const k_lds = lds;
   char* const v_lds = lds + 2 * KTILE;
 
@@ -448,7 +425,9 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   const int q_start = qt * kF8BM;
   if (q_start >= L) return;  // whole workgroup: a segment shorter than the grid's longest
 
-  const float sk = scales[unit], sv = scales[BH * sg.nseq + unit];
+  // Scale pairs (K, V) of this unit's 128-key chunks.
+  const int nchunks = ((VARLEN ? sg.max_len : N) + kFp8AmaxRows - 1) / kFp8AmaxRows;
+  const float* scl_g = scales + (size_t)unit * nchunks * 2;
 
   const size_t head = ((size_t)bh * N + row0) * D;
   const uint8_t* Kh = k8 + head;
@@ -457,7 +436,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   const int q0 = q_start + wave * 32;
   const int qi = q0 + c;
   // Q' operands (two e4m3 terms) and the exp2-domain score factor of this
-  // lane's query row, formed in the prologue below.
+  // lane's query row without the K scale, formed in the prologue below.
   i32x8 qreg[KD], qlo[KD];
   float c_log2;
 
@@ -489,9 +468,12 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     const int r = (wave * VLOADS + i) * 16 + lane / 4;
     ldv[i] = r * Npad + swz_chunk_rb<64>(r, lane % 4) * 16;
   }
-  auto gload_k = [&](char* tile, int j) __device__ {
+  auto gload_k = [&](int slot, int j) __device__ {
     const int key0 = j * kF8BN;
-    buffer_to_lds<KLOADS>(Kh + (size_t)key0 * D, (L - key0) * D, tile, ldk, wave * KLOADS);
+    buffer_to_lds<KLOADS>(Kh + (size_t)key0 * D, (L - key0) * D, k_lds + slot * KTILE, ldk,
+                          wave * KLOADS);
+    if (wave == 0)
+      stats_to_lds(scl_g + (j / 2) * 2, (char*)scl[slot], lane, 2 * (int)sizeof(float));
   };
   auto gload_v = [&](char* tile, int j) __device__ {
     const int key0 = j * kF8BN;
@@ -535,13 +517,13 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
         if (key >= L || (CAUSAL && key > qi)) s[t][r] = -INFINITY;
       }
   };
-  auto tile_max = [&](const f32x16 (&s)[2]) {
+  auto tile_max = [&](const f32x16 (&s)[2], float c) {
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    return half_max(mx) * c_log2;
+    return half_max(mx) * c;
   };
 
   // Key tiles in processing order: all of [0, n_kv), or under a block mask
@@ -571,8 +553,8 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     return;
   }
 
-  gload_k(k_lds, c0);
-  if (c1 < n_kv) gload_k(k_lds + KTILE, c1);
+  gload_k(0, c0);
+  if (c1 < n_kv) gload_k(1, c1);
   gload_v(v_lds, c0);
   if (rotate && tid < D) sgn[tid] = rotation_sign(seed, tid);
   __syncthreads();
@@ -640,7 +622,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     am = half_max(am);
     const Ratio448 rq(am);
     // Scores in the exp2 domain: s·c with c = scale·log2(e)·s_q(row)·s_k.
-    c_log2 = scale_from_amax(am) * sk * scale_log2;
+    c_log2 = scale_from_amax(am) * scale_log2;
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
@@ -661,11 +643,13 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   }
   wait_vmem();
   __syncthreads();
+  // Score factor (with the K scale) and V scale of the tile being softmaxed.
+  float c_cur = c_log2 * scl[0][0], sv_cur = scl[0][1];
   f32x16 s[2];
   scores(k_lds, s);
   if (c0 >= first_masked) mask(s, c0 * kF8BN);
   // The exponent offset starts at tile 0's row max; P̃ ≤ 2^τ afterwards.
-  float m_c = tile_max(s);
+  float m_c = tile_max(s, c_cur);
   // The first iteration refills K slot 0: every wave must have read K(0).
   __syncthreads();
 
@@ -676,7 +660,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     (void)j;
     if constexpr (HAS_NEXT) {
-      if (jn2 < n_kv) gload_k(k_lds + PAR * KTILE, jn2);
+      if (jn2 < n_kv) gload_k(PAR, jn2);
       gload_v(v_lds + (PAR ^ 1) * VTILE, jn);
     }
     // P̃·2^(8−τ) in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
@@ -690,14 +674,19 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // SPLIT: element e = 3 of every group of four on the polynomial.
-          const float x = fmaf(s[t][4 * wd + e], c_log2, off);
+          const float x = fmaf(s[t][4 * wd + e], c_cur, off);
           pv4[e] = (EXPM == EXP_POLY || (EXPM == EXP_SPLIT && e == 3)) ? exp2_poly(x) : exp2_hw(x);
           if constexpr (WANT_LSE) l_part += pv4[e];
         }
         p8[4 * t + wd] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
       }
     f32x16 ns[2];
+    float c_next = 0.0f, sv_next = 0.0f;
     if constexpr (HAS_NEXT) {
+      // Tile jn's scales sit with its K tile in slot PAR ^ 1 until the next
+      // iteration refills that slot.
+      c_next = c_log2 * scl[PAR ^ 1][0];
+      sv_next = scl[PAR ^ 1][1];
       scores(k_lds + (PAR ^ 1) * KTILE, ns);
       // Keep the softmax of tile j beside these MFMAs.
       asm volatile("" ::"v"(p8));
@@ -708,11 +697,12 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     for (int dt = 0; dt < DT; ++dt) {
       const i32x4 a0 = *(const i32x4*)(vt + dt * 32 * 64 + voff[0]);
       const i32x4 a1 = *(const i32x4*)(vt + dt * 32 * 64 + voff[1]);
-      oacc[dt] = mfma32_fp8(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8, oacc[dt]);
+      oacc[dt] = mfma32_fp8_ascale(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8,
+                                   oacc[dt], e8m0_of(sv_cur));
     }
     lacc = mfma32_fp8(ones, p8, lacc);
     if constexpr (HAS_NEXT) {
-      const float mx = tile_max(ns);
+      const float mx = tile_max(ns, c_next);
       if (__ballot(mx > m_c + kF8Tau)) {
         const bool resc = mx > m_c + kF8Tau;
         const float m_new = resc ? mx : m_c;
@@ -727,6 +717,8 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
       }
       s[0] = ns[0];
       s[1] = ns[1];
+      c_cur = c_next;
+      sv_cur = sv_next;
       wait_vmem();
       __syncthreads();
     }
@@ -769,7 +761,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     }
   }
 
-  const float inv = sv / lacc[0];
+  const float inv = 1.0f / lacc[0];
   if (qi < L) {
     bf16* Orow = O + head + (size_t)qi * D;
 #pragma unroll
@@ -856,28 +848,20 @@ static hipError_t launch_attend(const Fp8Attend& a, int d, bool causal, int exp_
 
 template <int D>
 static void launch_prep(const void* k, const void* v, uint8_t* k8, uint8_t* v8t, float* scales,
-                        float* partial, int BH, int N, bool rotate, uint64_t seed,
-                        const Fp8Segs& sg, hipStream_t stream) {
+                        int BH, int N, bool rotate, uint64_t seed, const Fp8Segs& sg,
+                        hipStream_t stream) {
   const int Npad = fp8_vcols(N, sg);
   const unsigned nchunks = (unsigned)((sg.max_len + kFp8AmaxRows - 1) / kFp8AmaxRows);
-  const unsigned nvblocks = (unsigned)((sg.max_len + 63) / 64);
-  const unsigned nseq = (unsigned)sg.nseq;
-  hipLaunchKernelGGL((fp8_amax_kernel<D>), dim3(nseq * nchunks, BH, 2), dim3(256), 0, stream,
-                     (const bf16*)k, (const bf16*)v, partial, N, BH, (int)rotate, seed, sg,
-                     (int)nchunks);
-  hipLaunchKernelGGL((fp8_quant_k_kernel<D>), dim3(nseq * nchunks, BH), dim3(256), 0, stream,
-                     (const bf16*)k, k8, (const float*)partial, scales, N, (int)rotate, seed, sg,
-                     (int)nchunks);
-  hipLaunchKernelGGL((fp8_quant_v_kernel<D>), dim3(nseq * nvblocks, BH), dim3(256), 0, stream,
-                     (const bf16*)v, v8t, (const float*)partial, scales, N, Npad, BH,
-                     (int)nchunks, sg, (int)nvblocks);
+  hipLaunchKernelGGL((fp8_prep_kernel<D>), dim3((unsigned)sg.nseq * nchunks, BH, 2), dim3(256),
+                     0, stream, (const bf16*)k, (const bf16*)v, k8, v8t, scales, N, Npad,
+                     (int)rotate, seed, sg, (int)nchunks);
 }
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
-                          uint8_t* k8, uint8_t* v8t, float* scales, float* partial, int B, int H,
-                          int N, int d, bool causal, float scale, int exp_mode, bool rotate,
-                          uint64_t seed, const uint8_t* block_mask, bool per_head,
-                          const int* cu_seqlens, int nseq, int max_seqlen, hipStream_t stream) {
+                          uint8_t* k8, uint8_t* v8t, float* scales, int B, int H, int N, int d,
+                          bool causal, float scale, int exp_mode, bool rotate, uint64_t seed,
+                          const uint8_t* block_mask, bool per_head, const int* cu_seqlens,
+                          int nseq, int max_seqlen, hipStream_t stream) {
   const int BH = B * H;
   Fp8Segs sg;
   sg.max_len = N;
@@ -886,8 +870,8 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
     sg.nseq = nseq;
     sg.max_len = max_seqlen;
   }
-  if (d == 64) launch_prep<64>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, sg, stream);
-  else launch_prep<128>(k, v, k8, v8t, scales, partial, BH, N, rotate, seed, sg, stream);
+  if (d == 64) launch_prep<64>(k, v, k8, v8t, scales, BH, N, rotate, seed, sg, stream);
+  else launch_prep<128>(k, v, k8, v8t, scales, BH, N, rotate, seed, sg, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   Fp8Attend a{(const bf16*)q, k8, v8t, scales, (bf16*)o, lse, BH, N, scale, (int)rotate, seed};
