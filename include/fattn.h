@@ -227,10 +227,13 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  * Q' ≈ scale_q·(Q8 + Q8lo/16); the scores use both terms (two fp8 MFMAs).
  * Q' is rotated and quantised inside the attention kernel (each workgroup
  * its own rows) and never stored.
- * The softmax keeps its exponent offset within a factor 2 of the running row
- * max (rescaling the partial output when the max grows by more), so every
- * unnormalised probability P̃ is at most 2; P is quantised to e4m3 as
- * P̃·2^7 ≤ 256. O is normalised by the sum of the quantised P̃ of its row.
+ * The softmax stores each unnormalised probability P̃ = 2^(s − m) in e4m3
+ * as P̃·2^(7−k) ≤ 256, with m the row's first tile max and k ≥ 0 the least
+ * integer that keeps every stored value of the row so far within that
+ * bound; the matrix core multiplies 2^k back (the P operand's block scale),
+ * so the partial output is rescaled only when k would pass 32 (m then moves
+ * to the row max). O is normalised by the sum of the quantised P̃ of its
+ * row.
  * Additionally requires B·H ≤ 65535 (ENOTSUP otherwise).
  * Validated range (GPU parity tests against float64 attention): d ∈ {64,
  * 128}, N from 1 to 32768, causal and not. Error against exact attention,

@@ -250,3 +250,41 @@ def test_fp8_output_does_not_depend_on_the_lse_request(shape, causal):
     torch.cuda.synchronize()
     assert l2 is None
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("d,causal", [(128, False), (128, True), (64, False)])
+def test_fp8_row_max_growing_past_the_exponent_cap(d, causal):
+    # Every 128 keys the row max rises by 3.8 to 6.4 log2 units (key rows
+    # t·e₀ with t growing chunk by chunk, query rows with 3 ≤ q₀ ≤ 5), 57 to
+    # 96 units over the row: the P operand's block-scale exponent grows and
+    # passes its cap of 32 once or twice per row, at different tiles for
+    # different rows of a wave, which moves the offset and rescales O. The
+    # keys of a 128-key chunk are identical (their e4m3 codes exact: every
+    # rotated element has the chunk's amax), so the fp8 softmax weights are
+    # nearly exact: O against exact attention within the fp8 bound, the LSE
+    # within the dense tests' tolerance of the model.
+    import tiled_attention_fattn_amd as fa
+    from tiled_attention_fattn_amd.inputs import bf16_round
+    N = 2000
+    rng = np.random.default_rng(95 + d)
+    q = rng.standard_normal((1, 2, N, d))
+    q[..., 0] = 3.0 + 0.5 * rng.integers(0, 5, size=(1, 2, N))
+    k = np.zeros((1, 2, N, d))
+    step = 10.0 if d == 128 else 7.0
+    k[..., 0] = step * (np.arange(N) // 128)
+    v = rng.standard_normal((1, 2, N, d))
+    (qf, qb), (kf, kb), (vf, vb) = bf16_round(q), bf16_round(k), bf16_round(v)
+    scale = d ** -0.5
+    print(f"[fp8] growing row max d={d} causal={causal}", flush=True)
+    o, lse = fa.fwd_fp8(to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(vb),
+                        causal=causal, scale=scale, rotate=True, seed=2)
+    torch.cuda.synchronize()
+    ref_o, _ = attention_forward(qf, kf, vf, causal, scale)
+    got = to_np(o)
+    assert np.all(np.isfinite(got))
+    rr = rel_rms(got, ref_o)
+    print(f"[fp8] growing row max rel-RMS {rr:.3e}", flush=True)
+    assert rr <= FP8_REL_RMS
+    model = fp8_attention_model(qf, kf, vf, causal, scale, rotate=True, seed=2)
+    lse_err = np.abs(to_np(lse) - model["lse"])
+    assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()

@@ -27,15 +27,19 @@
 //                   Q8lo = e4m3(16·(t − decode(Q8))). Loop: Sᵀ =
 //                   K8·(Q8 + Q8lo/16)ᵀ (two MFMAs, the second with the
 //                   block scale 2^-4) and Oᵀ += V8ᵀ·P8ᵀ on the
-//                   32x32x64 f8f6f4 MFMA; P̃ = 2^(s·c − m + 8) quantised to
-//                   e4m3 as P̃·2^(8−τ) with τ = 1: the exponent offset moves
-//                   only when a tile max exceeds it by more than τ
-//                   (FlashAttention-4 gist, technical summary 2.B), so
-//                   P̃ ≤ 2^τ and P̃·2^(8−τ) ≤ 256 < 448; a tile's K scale
-//                   joins the score factor, its V scale the PV MFMA's A
-//                   block scale; O = Oᵀ/l with l the sum of the quantised P̃
-//                   (formed by one more MFMA); the optional LSE uses the
-//                   fp32 sum before quantisation.
+//                   32x32x64 f8f6f4 MFMA; P̃ = 2^(s·c − m) quantised to
+//                   e4m3 as P̃·2^(8−τ−k) with τ = 1 and k ≥ 0 a per-row
+//                   integer that rises when a tile max exceeds m + k + τ,
+//                   so every stored value is at most 256 < 448; the PV and
+//                   row-sum MFMAs take 2^k back as the P operand's block
+//                   scale, so the offset m of O and l stays put and O needs
+//                   no rescale (FlashAttention-4 gist, technical summary
+//                   2.B: rescale only past a threshold; here the threshold
+//                   is k = 32, past which m moves to the row max and O is
+//                   rescaled); a tile's K scale joins the score factor, its
+//                   V scale the PV MFMA's A block scale; O = Oᵀ/l with l the
+//                   sum of the quantised P̃ (formed by one more MFMA); the
+//                   optional LSE uses the fp32 sum before quantisation.
 //
 // Variants of the same launches: a block mask over 128×128 blocks (the
 // attention kernel walks only the visible key tiles; the quantisation is
@@ -51,11 +55,14 @@
 namespace fattn {
 
 constexpr float kE4m3Max = 448.0f;
-// Conditional-rescale threshold of the fp8 softmax (log2 units) and the
-// matching exponent of the fixed P scale: P̃ ≤ 2^τ, stored as P̃·2^(8−τ).
+// Threshold of the fp8 softmax (log2 units) and the matching exponent of the
+// fixed P scale: P̃·2^−k ≤ 2^τ, stored as P̃·2^(8−τ−k).
 constexpr float kF8Tau = 1.0f;
 constexpr float kF8PExp = 8.0f - kF8Tau;
-constexpr int kRowSets = 2;  // rows per thread processed together in the row-wise kernels
+// Largest per-row exponent k of the P operand's block scale before the
+// accumulators are rescaled instead: O and l then hold at most 2^(8+k)·N
+// times the largest |V| (V below 2^72 stays finite up to N = 2^15).
+constexpr float kF8KMax = 32.0f;
 
 // SplitMix64: state advanced by the golden-ratio increment, then mixed.
 __device__ __forceinline__ float rotation_sign(uint64_t seed, int i) {
@@ -166,10 +173,11 @@ __device__ __forceinline__ float scale_from_amax(float a) { return a > 0.0f ? a 
 // E8M0 code of a positive normal power of two: its biased exponent.
 __device__ __forceinline__ int e8m0_of(float pow2) { return (int)(__float_as_uint(pow2) >> 23); }
 
-// The fp8 product with the A operand scaled by 2^(e8 − 127) (E8M0 block
-// scale, the same for the lane's 32 k values).
-__device__ __forceinline__ f32x16 mfma32_fp8_ascale(i32x8 a, i32x8 b, f32x16 c, int e8) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, e8, 0, 127);
+// The fp8 product with the A operand scaled by 2^(ea − 127) and the B operand
+// by 2^(eb − 127) (E8M0 block scales; each lane's scale covers the 32 k
+// values it holds).
+__device__ __forceinline__ f32x16 mfma32_fp8_scaled(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 
 // Four e4m3 codes (round to nearest even), a in the lowest byte.
@@ -483,7 +491,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
-  // Row sums: the normalisation of O uses the sum of the quantised P̃·2^(8−τ)
+  // Row sums: the normalisation of O uses the sum of the quantised P̃·2^(8−τ−k)
   // that enter the PV product, formed by the MFMA itself with an A operand of
   // e4m3 ones (every accumulator register of lane c then holds the sum for
   // query c), so numerator and denominator see the same probabilities. The
@@ -648,8 +656,17 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   f32x16 s[2];
   scores(k_lds, s);
   if (c0 >= first_masked) mask(s, c0 * kF8BN);
-  // The exponent offset starts at tile 0's row max; P̃ ≤ 2^τ afterwards.
+  // The exponent offset m_c of O and l starts at tile 0's row max and stays
+  // there: when a later tile's row max exceeds m_c + τ, the row's P̃ are
+  // stored as P̃·2^−k instead (k the least integer that keeps them ≤ 2^τ)
+  // and the PV and row-sum MFMAs take 2^k back as the P operand's block
+  // scale, so O and l need no rescale. Only when k would pass kF8KMax does
+  // the wave move m_c to the row max and rescale O and l.
   float m_c = tile_max(s, c_cur);
+  float kr = 0.0f;          // the row's k
+  float off = kF8PExp - m_c;
+  int e8p = 127;            // E8M0 code of 2^k
+  float pkr = 1.0f;         // 2^k, for the fp32 sum of the LSE
   // The first iteration refills K slot 0: every wave must have read K(0).
   __syncthreads();
 
@@ -663,9 +680,9 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
       if (jn2 < n_kv) gload_k(PAR, jn2);
       gload_v(v_lds + (PAR ^ 1) * VTILE, jn);
     }
-    // P̃·2^(8−τ) in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
-    const float off = kF8PExp - m_c;
+    // P̃·2^(8−τ−k) in e4m3; byte s of the operand: tile s/16, accumulator row s%16.
     i32x8 p8;
+    float t_sum = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -676,7 +693,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
           // SPLIT: element e = 3 of every group of four on the polynomial.
           const float x = fmaf(s[t][4 * wd + e], c_cur, off);
           pv4[e] = (EXPM == EXP_POLY || (EXPM == EXP_SPLIT && e == 3)) ? exp2_poly(x) : exp2_hw(x);
-          if constexpr (WANT_LSE) l_part += pv4[e];
+          if constexpr (WANT_LSE) t_sum += pv4[e];
         }
         p8[4 * t + wd] = cvt_fp8x4(pv4[0], pv4[1], pv4[2], pv4[3]);
       }
@@ -697,14 +714,17 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     for (int dt = 0; dt < DT; ++dt) {
       const i32x4 a0 = *(const i32x4*)(vt + dt * 32 * 64 + voff[0]);
       const i32x4 a1 = *(const i32x4*)(vt + dt * 32 * 64 + voff[1]);
-      oacc[dt] = mfma32_fp8_ascale(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8,
-                                   oacc[dt], e8m0_of(sv_cur));
+      oacc[dt] = mfma32_fp8_scaled(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), p8,
+                                   oacc[dt], e8m0_of(sv_cur), e8p);
     }
-    lacc = mfma32_fp8(ones, p8, lacc);
+    lacc = mfma32_fp8_scaled(ones, p8, lacc, 127, e8p);
+    if constexpr (WANT_LSE) l_part = fmaf(t_sum, pkr, l_part);
     if constexpr (HAS_NEXT) {
       const float mx = tile_max(ns, c_next);
-      if (__ballot(mx > m_c + kF8Tau)) {
-        const bool resc = mx > m_c + kF8Tau;
+      // NaN (a row with no key yet and none in this tile) leaves k as is.
+      float k_new = fmaxf(kr, __builtin_ceilf(mx - m_c - kF8Tau));
+      if (__ballot(k_new > kF8KMax)) {
+        const bool resc = k_new > kF8KMax;
         const float m_new = resc ? mx : m_c;
         const float alpha = resc ? exp2_hw(m_c - m_new) : 1.0f;
 #pragma unroll
@@ -714,7 +734,12 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
         lacc[0] *= alpha;  // only register 0 of the row-sum accumulator is read
         l_part *= alpha;
         m_c = m_new;
+        k_new = resc ? 0.0f : k_new;
       }
+      kr = k_new;
+      off = kF8PExp - m_c - kr;
+      pkr = __builtin_amdgcn_ldexpf(1.0f, (int)kr);
+      e8p = e8m0_of(pkr);
       s[0] = ns[0];
       s[1] = ns[1];
       c_cur = c_next;
