@@ -139,11 +139,18 @@ def quantize_per_block(x, cu_seqlens=None, blk=SCALE_BLOCK):
     return codes, scales
 
 
+# Smallest exponent of a power-of-two scale: 2^-126, the least normal fp32
+# value (the scale is applied as an E8M0 block scale of the fp8 product, and
+# its code is read from the scale's fp32 exponent field).
+POW2_MIN_EXP = -126
+
+
 def pow2_scale(amax):
-    """2^e for the least integer e with amax ≤ 448·2^e (1 where amax = 0)."""
+    """2^e for the least integer e ≥ POW2_MIN_EXP with amax ≤ 448·2^e (1
+    where amax = 0)."""
     amax = np.asarray(amax, dtype=np.float64)
     m, ex = np.frexp(np.where(amax > 0, amax / E4M3_MAX, 1.0))
-    e = np.where(m == 0.5, ex - 1, ex)
+    e = np.maximum(np.where(m == 0.5, ex - 1, ex), POW2_MIN_EXP)
     return np.where(amax > 0, np.ldexp(1.0, e), 1.0)
 
 

@@ -294,6 +294,23 @@ def test_pow2_scale_is_the_least_power_of_two_that_fits():
     assert np.all(amax[:-1] / s <= 448.0) and np.all(amax[:-1] / s > 224.0)
 
 
+def test_pow2_scale_floor_is_the_least_normal_fp32_power():
+    # Blocks whose amax is below 448·2^-126 keep the scale 2^-126 (the codes
+    # are then smaller than 448, down to e4m3 subnormals or zero); at
+    # 448·2^-126 exactly the least fitting power is that floor itself.
+    amax = np.array([448 * 2.0 ** -126, 448 * 2.0 ** -127, 2.0 ** -140, 448 * 2.0 ** -125])
+    np.testing.assert_array_equal(pow2_scale(amax),
+                                  [2.0 ** -126, 2.0 ** -126, 2.0 ** -126, 2.0 ** -125])
+    x = np.zeros((1, 1, 4, 2))
+    x[0, 0, 0, 0] = 448 * 2.0 ** -128
+    x[0, 0, 1, 1] = -2.0 ** -130
+    codes, sc = quantize_per_block_pow2(x)
+    assert np.all(sc == 2.0 ** -126)
+    assert codes[0, 0, 0, 0] == 0x6E       # 112 = 1.75·2^6: biased exponent 13, mantissa 6/8
+    assert codes[0, 0, 1, 1] == 0x98       # −2^-4: sign, biased exponent 3, mantissa 0
+    np.testing.assert_array_equal(dequantize_rows(codes, sc), x)
+
+
 def test_pow2_block_quantisation():
     # V: code = E4M3FN(v / 2^e) with the block's least fitting power of two;
     # the block maximum lands in (224, 448]; 448·2^k maps to code 0x7E
