@@ -219,9 +219,9 @@ fattn_status fattn_bwd_blocksparse(const void* q, const void* k, const void* v,
  * rounded to nearest even, with scale amax/448 (1 where amax = 0): K' with
  * one amax per (b, h) and chunk of 128 keys, Q' with one amax per row (each
  * query row meets the keys only through its own scores). V takes one power
- * of two per (b, h) and chunk, 2^e with e the least integer such that
- * amax ≤ 448·2^e (1 where amax = 0), and code = e4m3(v·2^−e), an exact
- * scaling; the PV product applies 2^e as the fp8 MFMA's block scale.
+ * of two per (b, h) and chunk, 2^e with e the least integer ≥ −126 such
+ * that amax ≤ 448·2^e (1 where amax = 0), and code = e4m3(v·2^−e), an
+ * exact scaling; the PV product applies 2^e as the fp8 MFMA's block scale.
  * Q' keeps a second e4m3 term for its quantisation residual,
  * Q8lo = e4m3(16·(x·448/amax − decode(Q8))), so that
  * Q' ≈ scale_q·(Q8 + Q8lo/16); the scores use both terms (two fp8 MFMAs).

@@ -288,3 +288,43 @@ def test_fp8_row_max_growing_past_the_exponent_cap(d, causal):
     model = fp8_attention_model(qf, kf, vf, causal, scale, rotate=True, seed=2)
     lse_err = np.abs(to_np(lse) - model["lse"])
     assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()
+
+
+def test_fp8_tiny_value_chunks():
+    # Chunks of 128 keys whose V (and K) values lie far below the usual range
+    # (|v| ≤ 2^-120, so 448·2^e would need e < −126): V keeps the scale
+    # 2^-126 and its codes (many of them bf16 subnormals), K its exact
+    # ratio; every code and scale as the model's, nothing overflows, and O
+    # stays within the fp8 bound of exact attention (the tiny K chunk's keys
+    # score about 0 and take a visible share of every row's weight).
+    import tiled_attention_fattn_amd as fa
+    from tiled_attention_fattn_amd.inputs import bf16_round
+    B, H, N, d = 1, 2, 512, 128
+    rng = np.random.default_rng(97)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    v[:, :, 128:256] *= 2.0 ** -122           # a whole chunk of tiny V
+    k[:, :, 256:384] *= 2.0 ** -122           # a whole chunk of tiny K
+    (qf, qb), (kf, kb), (vf, vb) = bf16_round(q), bf16_round(k), bf16_round(v)
+    scale = d ** -0.5
+    ws = torch.zeros(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    print("[fp8] tiny-value chunks", flush=True)
+    o, lse = fa.fwd_fp8(to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(vb),
+                        scale=scale, rotate=True, seed=7, workspace=ws)
+    torch.cuda.synchronize()
+    model = fp8_attention_model(qf, kf, vf, False, scale, rotate=True, seed=7)
+    k8, v8t, sc = (t.cpu().numpy() for t in fa.fp8_workspace_views(ws, B, H, N, d))
+    assert np.all(sc[:, :, 1, 1] == 2.0 ** -126)
+    np.testing.assert_array_equal(sc[..., 1], model["sv"][..., ::128])
+    np.testing.assert_allclose(sc[..., 0], model["sk"][..., ::128], rtol=1e-5)
+    v8 = _unpermute_v8t(v8t, N)
+    assert np.array_equal(e4m3_decode(v8), e4m3_decode(model["v8"]))
+    steps = _code_steps(k8, model["k8"])
+    assert steps.max() <= 1 and np.mean(steps == 0) >= 0.999
+    ref_o, _ = attention_forward(qf, kf, vf, False, scale)
+    got = to_np(o)
+    assert np.all(np.isfinite(got))
+    assert rel_rms(got, ref_o) <= FP8_REL_RMS
+    lse_err = np.abs(to_np(lse) - model["lse"])
+    assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()

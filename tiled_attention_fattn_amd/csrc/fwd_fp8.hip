@@ -327,12 +327,14 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(const bf16* __restrict__ 
     }
     const float am = block_max(m);
     // Least e with am ≤ 448·2^e: am/448 = f·2^k, f ∈ [0.5, 1); e = k − 1 when
-    // f = 0.5 exactly (the quotient is exact there, a power of two).
+    // f = 0.5 exactly (the quotient is exact there, a power of two). e stays
+    // at least −126 so that 2^e is a normal float, whose exponent field is
+    // the E8M0 code the attention kernel passes to the MFMA.
     int ex = 0;
     if (am > 0.0f) {
       int k;
       const float f = frexpf(am / kE4m3Max, &k);
-      ex = f == 0.5f ? k - 1 : k;
+      ex = max(f == 0.5f ? k - 1 : k, -126);
     }
     if (threadIdx.x == 0) sc[1] = ldexpf(1.0f, ex);
     uint8_t* dst = v8t + (size_t)bh * D * Npad + seg_vcol(sg, seg, row0) + c0;
