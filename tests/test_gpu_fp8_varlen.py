@@ -14,6 +14,8 @@ the float32 rotation, within a looser bound). Packings mix segment
 lengths of 0, 1, a few rows, tile multiples and ragged tails, both head
 dimensions, causal and not, hardware and split exp2; a larger packing
 (H=8, N=16384, lengths between 1 and 4096) is checked on sampled rows.
+Segments longer than max_seqlen are cut as documented, for the bf16 and the
+fp8 varlen forward.
 """
 import numpy as np
 import pytest
@@ -160,3 +162,42 @@ def test_fp8_varlen_large_packing_sampled():
         seg = np.searchsorted(cu, rows, side="right") - 1
         many = rows - cu[seg] >= 127
         assert np.max(np.abs(to_np(lse[0, h][idx])[many] - ref_l[many])) <= 2e-2
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_segments_longer_than_max_seqlen_are_cut(causal):
+    # max_seqlen below some segment lengths. The bf16 forward computes only
+    # a segment's first max_seqlen rows, each attending to all of the
+    # segment's keys: they equal those rows of a plain call on the whole
+    # segment. The fp8 forward cuts the segment, keys included (no key past
+    # the cut is quantised): its kept rows equal a plain fp8 call on those
+    # rows alone. O and LSE bit for bit; rows past the cut keep what the
+    # output held before (NaN here).
+    import tiled_attention_fattn_amd as fa
+    lengths = [300, 50, 200, 1, 129]
+    maxl = 128
+    H, d = 2, 128
+    inp, t, cu, cu_t, N = _setup(320, H, d, lengths)
+    print(f"[varlen cut] lengths={lengths} max_seqlen={maxl} causal={causal}", flush=True)
+    o16 = torch.full((1, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    l16 = torch.full((1, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fwd_varlen(t["q"], t["k"], t["v"], cu_t, maxl, causal=causal, out=o16, lse=l16)
+    o8 = torch.full((1, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o8, l8 = fa.fwd_fp8_varlen(t["q"], t["k"], t["v"], cu_t, maxl, causal=causal, rotate=True,
+                               seed=3, out=o8)
+    torch.cuda.synchronize()
+    for a, L in zip(cu[:-1], lengths):
+        a, keep = int(a), min(L, maxl)
+        whole = [t[n][:, :, a:a + L].clone() for n in ("q", "k", "v")]
+        cut = [x[:, :, :keep].clone() for x in whole]
+        p16, pl16 = fa.fwd(*whole, causal=causal)
+        p8, pl8 = fa.fwd_fp8(*cut, causal=causal, rotate=True, seed=3)
+        torch.cuda.synchronize()
+        sl = slice(a, a + keep)
+        assert torch.equal(o16[:, :, sl], p16[:, :, :keep])
+        assert torch.equal(l16[:, :, sl], pl16[:, :, :keep])
+        assert torch.equal(o8[:, :, sl], p8) and torch.equal(l8[:, :, sl], pl8)
+        if L > keep:
+            rest = slice(a + keep, a + L)
+            assert torch.isnan(o16[:, :, rest]).all() and torch.isnan(l16[:, :, rest]).all()
+            assert torch.isnan(o8[:, :, rest]).all()
