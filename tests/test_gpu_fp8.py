@@ -328,3 +328,29 @@ def test_fp8_tiny_value_chunks():
     assert rel_rms(got, ref_o) <= FP8_REL_RMS
     lse_err = np.abs(to_np(lse) - model["lse"])
     assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_bitwise_reproducible(causal):
+    # No atomics and a fixed reduction order: two calls on the same inputs
+    # give the same O, LSE and workspace bit for bit (dense, and packed
+    # segments with a length mix).
+    import tiled_attention_fattn_amd as fa
+    shape = (2, 4, 1100, 128)
+    inp = _inputs(40, shape)
+    q, k, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    B, H, N, d = shape
+    print(f"[fp8] reproducibility causal={causal}", flush=True)
+    ws1 = torch.zeros(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    ws2 = torch.ones_like(ws1)
+    o1, l1 = fa.fwd_fp8(q, k, v, causal=causal, rotate=True, seed=9, workspace=ws1)
+    o2, l2 = fa.fwd_fp8(q, k, v, causal=causal, rotate=True, seed=9, workspace=ws2)
+    cu = torch.tensor([0, 1, 300, 301, 777, 1100], dtype=torch.int32, device="cuda")
+    v1, m1 = fa.fwd_fp8_varlen(q, k, v, cu, 476, causal=causal, rotate=True, seed=9)
+    v2, m2 = fa.fwd_fp8_varlen(q, k, v, cu, 476, causal=causal, rotate=True, seed=9)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    k8a, v8a, sa = fa.fp8_workspace_views(ws1, B, H, N, d)
+    k8b, v8b, sb = fa.fp8_workspace_views(ws2, B, H, N, d)
+    assert torch.equal(k8a, k8b) and torch.equal(v8a, v8b) and torch.equal(sa, sb)
+    assert torch.equal(v1, v2) and torch.equal(m1, m2)
