@@ -121,6 +121,11 @@ __device__ __forceinline__ int lds_addr(const char* p) { return (int)(uint32_t)(
 // (it cannot tell which LDS bytes they write). The caller orders them with
 // wait_vmem() and a workgroup barrier before the data is read, and before
 // the LDS range is written again.
+// Each load sets m0 (the LDS destination) itself. The compiler treats m0 as
+// a reserved register and does not honour it as a clobber; this is sound
+// because none of the kernels' compiled code reads or writes m0 outside
+// these asm statements (checked on the gfx950 assembly of every kernel), so
+// no compiler value lives in m0 across them.
 template <int LOADS>
 __device__ __forceinline__ void buffer_to_lds(const void* base, int bytes, char* dst,
                                               const int (&off)[LOADS], int first) {
