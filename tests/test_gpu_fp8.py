@@ -354,3 +354,41 @@ def test_fp8_bitwise_reproducible(causal):
     k8b, v8b, sb = fa.fp8_workspace_views(ws2, B, H, N, d)
     assert torch.equal(k8a, k8b) and torch.equal(v8a, v8b) and torch.equal(sa, sb)
     assert torch.equal(v1, v2) and torch.equal(m1, m2)
+
+
+def test_fp8_subnormal_blocks():
+    # A K chunk and some Q rows whose rotated values all lie below 2^-128
+    # (bf16 subnormals), where 1/amax overflows in fp32: the quantiser
+    # rescales such blocks exactly, so the K codes and scales are the
+    # model's, every output is finite and within the fp8 bound of exact
+    # attention, and the LSE matches the model's.
+    import tiled_attention_fattn_amd as fa
+    from tiled_attention_fattn_amd.inputs import bf16_round
+    B, H, N, d = 1, 2, 384, 128
+    rng = np.random.default_rng(98)
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    k[:, :, 128:256] *= 2.0 ** -131
+    q[:, :, 5:40] *= 2.0 ** -131
+    (qf, qb), (kf, kb), (vf, vb) = bf16_round(q), bf16_round(k), bf16_round(v)
+    assert np.abs(kf[:, :, 128:256]).max() < 2.0 ** -128
+    scale = d ** -0.5
+    ws = torch.zeros(fa.fp8_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    print("[fp8] subnormal blocks", flush=True)
+    o, lse = fa.fwd_fp8(to_device_bf16(qb), to_device_bf16(kb), to_device_bf16(vb),
+                        scale=scale, rotate=True, seed=7, workspace=ws)
+    torch.cuda.synchronize()
+    model = fp8_attention_model(qf, kf, vf, False, scale, rotate=True, seed=7)
+    k8, _, sc = (t.cpu().numpy() for t in fa.fp8_workspace_views(ws, B, H, N, d))
+    # the tiny chunk's scale (about 3e-42) is an fp32 subnormal: two steps of
+    # 2^-149 on top of the relative tolerance
+    np.testing.assert_allclose(sc[..., 0], model["sk"][..., ::128], rtol=1e-5, atol=2.0 ** -148)
+    steps = _code_steps(k8, model["k8"])
+    assert steps.max() <= 1 and np.mean(steps == 0) >= 0.999
+    got = to_np(o)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(to_np(lse)))
+    ref_o, _ = attention_forward(qf, kf, vf, False, scale)
+    assert rel_rms(got, ref_o) <= FP8_REL_RMS
+    lse_err = np.abs(to_np(lse) - model["lse"])
+    assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()

@@ -143,7 +143,10 @@ __device__ __forceinline__ void fwht_row(float (&x)[kEpl], int lane_in_row) {
   }
 }
 
-// Loads the 32 values of (row, part), rotated when `rot`; false if row >= N.
+// Loads the 32 values of (row, part), rotated when `rot` (signs and the
+// Walsh–Hadamard butterflies, without the 1/√d: the quantisation below is
+// scale-invariant, so the factor joins the row's or chunk's scale instead);
+// false if row >= N.
 // Every lane of a row must call it (the rotation exchanges values).
 template <int D>
 __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, int part, bool rot,
@@ -161,9 +164,6 @@ __device__ __forceinline__ bool load_row_part(const bf16* src, int row, int N, i
 #pragma unroll
     for (int e = 0; e < kEpl; ++e) x[e] *= sgn[part * kEpl + e];
     fwht_row<LPR>(x, part);
-    const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
-#pragma unroll
-    for (int e = 0; e < kEpl; ++e) x[e] *= inv_sqrt_d;
   }
   return ok;
 }
@@ -188,7 +188,9 @@ __device__ __forceinline__ int cvt_fp8x4(float a, float b, float c, float d) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
-__device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -kE4m3Max), kE4m3Max); }
+// 1/√d of the rotation R = diag(s)·H_d/√d, applied to the scales.
+template <int D>
+constexpr float kInvSqrtD = D == 128 ? 0.08838834764831845f : 0.125f;
 
 // Decode the four e4m3 codes of a packed word (lowest byte first).
 __device__ __forceinline__ void dec_fp8x4(int w, float* out) {
@@ -198,19 +200,28 @@ __device__ __forceinline__ void dec_fp8x4(int w, float* out) {
   out[3] = __builtin_amdgcn_cvt_f32_fp8(w, 3);
 }
 
-// x·448/amax with one correctly rounded division (x·448 is exact for bf16 x),
-// so exact e4m3 midpoints stay exact.
+// x·448/amax with one correctly rounded division (x·448 is exact for x of at
+// most 21 significant bits, bf16 values among them), so exact e4m3
+// midpoints stay exact.
 //
 // The quotient is formed by multiplying with the correctly rounded reciprocal
 // of amax and one FMA correction from the exact remainder (Markstein's
 // division step), which yields the correctly rounded fp32 quotient for
-// normal operands at a quarter of the cost of a general division.
+// normal operands at a quarter of the cost of a general division. An amax
+// below 2^-100 (whose reciprocal could overflow) is scaled by 2^64 first,
+// with x·448 alike, which is exact. Since |x| ≤ amax, the quotient never
+// exceeds 448, so no e4m3 code saturates; amax = 0 (all x zero) gives 0.
 struct Ratio448 {
-  float am, inv;
-  __device__ explicit Ratio448(float a) : am(a), inv(a > 0.0f ? __frcp_rn(a) : 0.0f) {}
+  float am, inv, mul;
+  __device__ explicit Ratio448(float a) {
+    const bool tiny = a < 0x1p-100f;
+    am = tiny ? a * 0x1p64f : a;
+    mul = tiny ? kE4m3Max * 0x1p64f : kE4m3Max;
+    inv = am > 0.0f ? __frcp_rn(am) : 0.0f;
+  }
 };
 __device__ __forceinline__ float ratio448(float x, const Ratio448& r) {
-  const float a = x * kE4m3Max;          // exact: 8 significant bits times 7·2^6
+  const float a = x * r.mul;
   const float q0 = a * r.inv;
   const float e = fmaf(-q0, r.am, a);    // exact remainder a − q0·amax
   return fmaf(e, r.inv, q0);
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(const bf16* __restrict__ 
     }
     const float am = block_max(m);
     const Ratio448 rk(am);
-    if (threadIdx.x == 0) sc[0] = scale_from_amax(am);
+    if (threadIdx.x == 0) sc[0] = scale_from_amax(rotate ? am * kInvSqrtD<D> : am);
 #pragma unroll
     for (int u = 0; u < KPASS; ++u) {
       if (!ok[u]) continue;
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(const bf16* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float x = xs[u][16 * c + e];
-          tt[e] = am > 0.0f ? clamp448(ratio448(x, rk)) : x;
+          tt[e] = ratio448(x, rk);
         }
         i32x4 w;
 #pragma unroll
@@ -574,9 +585,9 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
   // score MFMA. Rotation: signs, then the unnormalised Walsh–Hadamard
   // butterflies over d bits 0–4 (in lane), bit 5 (the two lane halves, by a
   // half swap) and bit 6 (in lane, kk), in the same order and form as the
-  // row-wise prep kernels (lower index a + b, upper a − b), then 1/√d. The
-  // row's amax over both halves sets its scale; codes and the residual
-  // term as in the K quantisation.
+  // K preparation (lower index a + b, upper a − b); the 1/√d joins the
+  // row's scale. The row's amax over both halves sets that scale; codes and
+  // the residual term as in the K quantisation.
   {
     float x[KD][32];
     const bf16* Qrow = Q + head + (size_t)qi * D + 32 * h;
@@ -618,11 +629,6 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
           x[1][e] = a - b;
         }
       }
-      const float inv_sqrt_d = D == 128 ? 0.08838834764831845f : 0.125f;
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
-#pragma unroll
-        for (int e = 0; e < 32; ++e) x[kk][e] *= inv_sqrt_d;
     }
     float am = 0.0f;
 #pragma unroll
@@ -632,7 +638,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
     am = half_max(am);
     const Ratio448 rq(am);
     // Scores in the exp2 domain: s·c with c = scale·log2(e)·s_q(row)·s_k.
-    c_log2 = scale_from_amax(am) * scale_log2;
+    c_log2 = scale_from_amax(rotate ? am * kInvSqrtD<D> : am) * scale_log2;
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
@@ -641,7 +647,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v = x[kk][4 * g + e];
-          tt[e] = am > 0.0f ? clamp448(ratio448(v, rq)) : v;
+          tt[e] = ratio448(v, rq);
         }
         const int w = cvt_fp8x4(tt[0], tt[1], tt[2], tt[3]);
         dec_fp8x4(w, dec);
