@@ -392,3 +392,39 @@ def test_fp8_subnormal_blocks():
     assert rel_rms(got, ref_o) <= FP8_REL_RMS
     lse_err = np.abs(to_np(lse) - model["lse"])
     assert np.all(lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])), lse_err.max()
+
+
+def test_fp8_causal_issue_groups_ragged():
+    # Causal d = 128 with 4 to 8 query tiles per head runs in issue groups of
+    # whole heads (as many as fill the resident workgroups once); 100 heads
+    # of 640 rows (5 tiles) make groups of 96 and 4 heads. Every output
+    # element must be written (NaN-poisoned), O within the fp8 bound of exact
+    # attention and the LSE within the model's tolerance on every head.
+    import tiled_attention_fattn_amd as fa
+    shape = (4, 25, 640, 128)
+    inp = _inputs(640, shape)
+    q, k, v = (to_device_bf16(inp[n][1]) for n in ("q", "k", "v"))
+    scale = shape[-1] ** -0.5
+    o = torch.full(shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    print(f"[fp8] causal issue groups shape={shape}", flush=True)
+    o, lse = fa.fwd_fp8(q, k, v, causal=True, scale=scale, rotate=True, seed=6, out=o)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item(), "elements left unwritten"
+    ref_o, _ = attention_forward(inp["q"][0], inp["k"][0], inp["v"][0], True, scale)
+    rr = rel_rms(to_np(o), ref_o)
+    print(f"[fp8] causal issue groups rel-RMS {rr:.4e}", flush=True)
+    assert rr <= FP8_REL_RMS
+    model = fp8_attention_model(inp["q"][0], inp["k"][0], inp["v"][0], True, scale,
+                                rotate=True, seed=6)
+    # As in the packed-sequence tests: a row dominated by few scores (an
+    # early causal row, or one with an outlier-sized score) moves its LSE by
+    # the change of one score when one K' code is a step off the model's
+    # (float32 against float64 rotation, opposite sides of a tie); across
+    # 100 heads such rows occur (seen: one of 64000, 0.048). The strict bound
+    # on 99% of the rows, a loose one on all.
+    lse_err = np.abs(to_np(lse) - model["lse"])
+    strict = lse_err <= 2e-3 + 1e-3 * np.abs(model["lse"])
+    assert np.mean(strict) >= 0.99, (np.mean(strict), lse_err.max())
+    assert np.all(lse_err <= 5e-2 + 1e-2 * np.abs(model["lse"])), lse_err.max()
+    print(f"[fp8] causal issue groups: {np.sum(~strict)} rows outside the strict LSE bound, "
+          f"rows {np.unique(np.nonzero(~strict)[2])[:10]}", flush=True)
