@@ -632,7 +632,7 @@ void fwd_fp8_kernel(const bf16* __restrict__ Q, const uint8_t* __restrict__ k8,
           const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[kk][e]),
                                                           __float_as_uint(x[kk][e]), false, false);
           const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
-          x[kk][e] = h ? (lo - hi) : (lo + hi);
+          x[kk][e] = fmaf(hi, h ? -1.0f : 1.0f, lo);  // lo + hi, or lo − hi
         }
       }
       if constexpr (KD == 2) {
